@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed, block-quantized MoE layer on one MI355X.
+
+A step is one pass of the whole layer (router, top-k + softmax, permutation/union, expert FFNs,
+combine + shared expert) over one batch of seeded synthetic input, as ``moe_layer`` calls:
+
+  decode1 (default): 1 token, H 2048, 256 experts top-8 + shared (I 512), 4-bit experts. The layer
+      is replicated 48 times at distinct HBM addresses (all 256 experts of each copy resident) and
+      one step is 48 sequential ``moe_layer`` calls, one per copy, so every call streams its
+      experts from HBM rather than from the 256 MB Infinity Cache.
+  verify4: the same with 4 tokens and 8-bit experts.
+  stack48: 48 distinct layers of 512 experts top-10, 2-bit experts, 1 token (36 GB resident).
+  prefill8k: one 8192-token chunk through one layer (256 experts, 4-bit, shared expert).
+
+value = MoE-layer tokens/s = (layer calls x tokens per call) / time, inputs resident in HBM.
+The JSON line also carries the roofline of the dominant kernel stage (expert weight bytes per
+launch over its HIP-event-timed duration for decode; expert FLOPs for prefill) and the fp64 CPU
+oracle timed on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import quantized_expert_ffn_moe_amd as moe  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFS = 2516.6     # MI355X dense fp16/bf16 MFMA, TFLOP/s (256 CU x 4096 flop/clk x 2.4 GHz)
+REPLICAS = 48
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def expert_weight_bytes(spec, n_routed: int) -> int:
+    """Packed codes + fp16 scales of n_routed routed experts plus the shared expert."""
+    b = n_routed * spec.expert_bytes()
+    if spec.Is:
+        b += spec.expert_bytes(spec.Is)
+    return b
+
+
+def upload(spec, d):
+    return moe.DeviceLayer.from_host(moe.LayerDesc.from_spec(spec), d)
+
+
+def clone_layer(L: moe.DeviceLayer) -> moe.DeviceLayer:
+    def c(p):
+        return None if p is None else (p[0].clone(), p[1].clone())
+    m = L.mats
+    return moe.DeviceLayer(L.desc, L.w_router.clone(), None if L.router_bias is None else L.router_bias.clone(),
+                           c(m["gate"]), c(m["up"]), c(m["down"]), c(m["sh_gate"]), c(m["sh_up"]), c(m["sh_down"]))
+
+
+def dev_x(x):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+
+
+def time_calls(fn_list, warmup: int, reps: int):
+    """Per-call HIP-event durations (ms) of a list of zero-arg launches, on torch's current stream."""
+    for _ in range(warmup):
+        for f in fn_list:
+            f()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        for f in fn_list:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def decode_workload(name: str, steps: int, warmup: int):
+    spec = synth.CONFIGS[name]
+    layers = []
+    xs = []
+    t0 = time.time()
+    if name == "stack48":
+        for l in range(spec.layers):
+            d = synth.make_layer(spec, layer=l)
+            layers.append(upload(spec, d))
+            xs.append(dev_x(d["x"]))
+            log("generated layer %d/%d (%.0f s)" % (l + 1, spec.layers, time.time() - t0))
+    else:
+        d = synth.make_layer(spec)
+        base = upload(spec, d)
+        layers = [base] + [clone_layer(base) for _ in range(REPLICAS - 1)]
+        xs = [dev_x(d["x"])] * REPLICAS
+    torch.cuda.synchronize()
+    log("%s: %d resident layer copies ready in %.1f s" % (name, len(layers), time.time() - t0))
+    T = spec.T
+    ws = moe.Workspace()
+    out = torch.empty((T, spec.H), dtype=torch.float32, device="cuda")
+    ids = [torch.empty((T, spec.k), dtype=torch.int32, device="cuda") for _ in layers]
+    calls = [lambda L=L, x=x, i=i: moe.moe_layer(L, x, out=out, ids=i, ws=ws) for L, x, i in zip(layers, xs, ids)]
+
+    def step():
+        for c in calls:
+            c()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    ms_per_step = ms / steps
+    value = len(layers) * T * steps / (ms / 1e3)
+
+    # dominant stage: the decode expert FFNs (moe_experts_decode), timed per launch with HIP events
+    nU = [len(set(i.cpu().numpy().ravel().tolist())) for i in ids]
+    ysh = torch.empty((T, spec.H), dtype=torch.float32, device="cuda")
+    ypairs = torch.empty((T * spec.k, spec.H), dtype=torch.float32, device="cuda")
+    ews = moe.Workspace()
+    ecalls = [lambda L=L, x=x, i=i: moe.moe_experts_decode(L, x, i, y_pairs=ypairs, y_shared=ysh, ws=ews)
+              for L, x, i in zip(layers, xs, ids)]
+    durs = time_calls(ecalls, 2, max(3, steps))
+    avg_ms = float(np.mean(durs))
+    bytes_per_launch = float(np.mean([expert_weight_bytes(spec, u) for u in nU]))
+    achieved = bytes_per_launch / (avg_ms / 1e3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "moe_experts_decode (k_decode_gateup + k_decode_down)",
+            "bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(avg_ms * 1e3, 2),
+            "distinct_experts_per_call": float(np.mean(nU))}
+    cfg = {"workload": name, "tokens_per_call": T, "hidden": spec.H, "experts": spec.E, "top_k": spec.k,
+           "inter": spec.I, "shared_inter": spec.Is, "format": synth.FMT_NAMES[spec.fmt],
+           "layer_calls_per_step": len(layers), "resident_layers": len(layers)}
+    return value, ms_per_step, roof, cfg
+
+
+def prefill_workload(steps: int, warmup: int):
+    spec = synth.CONFIGS["prefill8k"]
+    t0 = time.time()
+    d = synth.make_layer(spec)
+    L = upload(spec, d)
+    x = dev_x(d["x"])
+    log("prefill8k ready in %.1f s" % (time.time() - t0))
+    T = spec.T
+    ws = moe.Workspace()
+    out = torch.empty((T, spec.H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, spec.k), dtype=torch.int32, device="cuda")
+    for _ in range(warmup):
+        moe.moe_layer(L, x, out=out, ids=ids, ws=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        moe.moe_layer(L, x, out=out, ids=ids, ws=ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms_per_step = a.elapsed_time(b) / steps
+    value = T / (ms_per_step / 1e3)
+    # expert stage on its own
+    offsets, perm, inv = moe.moe_permute(L, ids)
+    y_sorted = torch.empty((T * spec.k, spec.H), dtype=torch.float32, device="cuda")
+    y_sh = torch.empty((T, spec.H), dtype=torch.float32, device="cuda")
+    pws = moe.Workspace()
+    durs = time_calls([lambda: moe.moe_experts_prefill(L, x, offsets, perm, y_sorted=y_sorted, y_shared=y_sh,
+                                                       ws=pws)], 2, max(3, steps))
+    avg_ms = float(np.mean(durs))
+    flops = 6.0 * spec.H * spec.I * (T * spec.k) + 6.0 * spec.H * spec.Is * T
+    achieved = flops / (avg_ms / 1e3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_F16_PEAK_TFS, 4), "traffic": None,
+            "kernel": "moe_experts_prefill (tiles + x->fp16 + k_prefill_gateup + k_prefill_down)",
+            "flops_per_launch": flops, "avg_launch_us": round(avg_ms * 1e3, 1)}
+    return {"metric": "MoE-layer tokens/s (8192-token prefill chunk)", "value": round(value, 1),
+            "unit": "tokens/s", "dtype": "f16", "ms_per_step": round(ms_per_step, 4), "roofline": roof,
+            "config": {"workload": "prefill8k", "tokens_per_call": T, "hidden": spec.H, "experts": spec.E,
+                       "top_k": spec.k, "inter": spec.I, "shared_inter": spec.Is,
+                       "format": synth.FMT_NAMES[spec.fmt]}}
+
+
+def cpu_baseline(name: str, budget_s: float = 12.0):
+    """The fp64 oracle (single thread) on a bounded sample of the workload's tokens."""
+    import oracle
+    spec = synth.CONFIGS[name]
+    d = synth.make_layer(spec, layer=0)
+    O = oracle.Layer.from_synth(spec, d)
+    xs = synth.make_x(spec, layer=0, seed=1, T=64)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        O.token(xs[n % 64])
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(n / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d tokens through one full %s layer (router, top-k, experts, combine), fp64, 1 thread, %.1f s"
+                      % (n, name, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode1", choices=["decode1", "verify4", "stack48", "prefill8k"])
+    ap.add_argument("--no-prefill", action="store_true", help="skip the secondary 8K prefill measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (expert parallelism is a design "
+              "note); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()
+
+    if args.workload == "prefill8k":
+        r = prefill_workload(args.steps, args.warmup)
+        value, ms, roof, cfg, metric = r["value"], r["ms_per_step"], r["roofline"], r["config"], r["metric"]
+        secondary = None
+    else:
+        value, ms, roof, cfg = decode_workload(args.workload, args.steps, args.warmup)
+        metric = "MoE-layer tokens/s (decode, %% HBM peak on expert-weight bytes)"
+        secondary = None if args.no_prefill else prefill_workload(max(3, args.steps // 4), 2)
+    line = {"metric": metric.replace("%%", "%"), "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16" if args.workload == "prefill8k" else "f32",
+            "data": "synthetic (seeded N(0,0.02) weights quantised to block-32 codes, bf16 N(0,1) activations, "
+                    "Zipf-biased router)",
+            "config": cfg, "roofline": roof}
+    if secondary is not None:
+        line["prefill"] = secondary
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.workload if args.workload != "stack48" else "stack48", 12.0)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

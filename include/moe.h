@@ -1,0 +1,195 @@
+/*
+ * moe.h -- C ABI of the routed, block-quantized MoE expert layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer: a router scores every expert for each token, the k best experts are chosen and
+ * weighted by a softmax over the chosen k, the (token, expert) pairs are grouped by expert, each
+ * chosen expert runs a SwiGLU FFN whose weights are integer codes with one fp16 scale per 32
+ * values, and the expert outputs are summed with their weights plus an always-used shared expert.
+ *
+ * Passages this follows (the pages describe the layer, not its arithmetic):
+ *   - only a few experts run per token: 8 of 256 (648news 10-cyber-on-strata-moe-local-inference,
+ *     section "tiered VRAM/RAM inference"), about ten of 24,576 over 48 layers (bagrov.by
+ *     ierarhicheskaya-pamyat-moe-modelej-strata-maya, section "MoE architecture and hierarchical
+ *     caching");
+ *   - the router and a shared expert stay resident on the GPU (648news
+ *     07-nano-cuda-moe-qwen38-release, section "asynchronous CPU/GPU compute");
+ *   - integer values with one scale per 32 (same page, section "memory hierarchy spanning VRAM and
+ *     RAM"); 2-, 3- and 4-bit class expert formats (same page, format table in section "speed
+ *     comparison and accuracy check");
+ *   - prompts are processed in 8K-token chunks with GEMMs and grouped expert kernels (same page,
+ *     same section); decode runs the selected experts on the GPU (same page, section
+ *     "asynchronous CPU/GPU compute").
+ * Here every expert stays resident in HBM; there is no host offload and no expert cache.
+ *
+ * ----------------------------------------------------------------------------------------------
+ * Conventions for every entry point
+ *   - Every pointer is a DEVICE pointer unless stated otherwise; descriptors (moe_layer_desc,
+ *     moe_layer_weights) are HOST structs read during the call and not kept.
+ *   - The caller owns every buffer. The library allocates nothing and keeps no pointer after it
+ *     returns. Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *     call returns without waiting; buffers must stay valid until the stream has passed the work.
+ *   - Arguments are checked on the host before anything is enqueued. A failed check returns a
+ *     status other than MOE_OK and enqueues nothing. A failed launch returns MOE_ERR_HIP.
+ *   - The library has no global mutable state and is reentrant. Two calls that share a workspace
+ *     must be ordered on one stream.
+ *   - Preconditions that are not checked: router logits are finite (no NaN); ids passed in are in
+ *     [0, E) and distinct within a token; buffers hold the documented number of elements.
+ *
+ * Data layout (row-major, innermost index contiguous)
+ *   x            bf16 bits  [T][H]
+ *   w_router     fp32       [E][H]        router_bias fp32 [E] or NULL (= 0)
+ *   gate, up     codes      [E][I][H*bits/8], scales fp16 bits [E][I][H/32]
+ *   down         codes      [E][H][I*bits/8], scales fp16 bits [E][H][I/32]
+ *   sh_gate/up   codes      [Is][H*bits/8],   scales [Is][H/32]     (shared expert, if Is > 0)
+ *   sh_down      codes      [H][Is*bits/8],   scales [H][Is/32]
+ *   Code packing along a row (K = the row length):
+ *     MOE_Q8_B32  one int8 per element, value = code * scale
+ *     MOE_Q4_B32  element 2i in the low nibble of byte i, 2i+1 in the high nibble; two's
+ *                 complement (-8..7); value = code * scale
+ *     MOE_Q2_B32  element 4i+m in bits 2m..2m+1 of byte i; unsigned c (0..3);
+ *                 value = (c - 1.5) * scale
+ *   The scale of element kappa of row n is scales[n][kappa / 32].
+ *   logits fp32 [T][E]; ids int32 [T][k]; p fp32 [T][k]; pair q = t*k + j.
+ *   offsets int32 [E+1]; perm int32 [T*k] (sorted position -> pair); inv int32 [T*k] (pair ->
+ *   sorted position).
+ *   Outputs Y, y_pairs, y_sorted, y_shared are fp32 with rows of H.
+ *
+ * Shape limits (MOE_ERR_INVALID_ARG otherwise): T >= 1; 1 <= k <= min(E, 16); E <= 1024;
+ * H, I multiples of 32 and Is = 0 or a multiple of 32; H <= 16384; I, Is <= 4096;
+ * pointers to codes, scales, x, outputs and workspace 16-byte aligned. The prefill path
+ * (moe_experts_prefill, and moe_layer with T > 4) also needs H, I and Is to be multiples of 64
+ * (MOE_ERR_UNSUPPORTED otherwise).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef int32_t moe_status;
+enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,  /* null pointer, bad shape, misalignment */
+    MOE_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (e.g. T > 4 to decode) */
+    MOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than moe_workspace_size() */
+    MOE_ERR_HIP = 4           /* a HIP launch failed */
+};
+
+typedef int32_t moe_qformat;
+enum { MOE_Q8_B32 = 0, MOE_Q4_B32 = 1, MOE_Q2_B32 = 2 };
+
+/* Entry-point selector for moe_workspace_size(). */
+typedef int32_t moe_call;
+enum {
+    MOE_CALL_ROUTE = 0,
+    MOE_CALL_PERMUTE = 1,
+    MOE_CALL_EXPERTS_DECODE = 2,
+    MOE_CALL_EXPERTS_PREFILL = 3,
+    MOE_CALL_COMBINE = 4,
+    MOE_CALL_LAYER = 5
+};
+
+/* One stack of quantized matrices (device pointers). */
+typedef struct {
+    const void* codes;
+    const uint16_t* scales;
+} moe_qmat;
+
+typedef struct {
+    int32_t hidden;        /* H */
+    int32_t inter;         /* I, SwiGLU intermediate of a routed expert */
+    int32_t num_experts;   /* E */
+    int32_t top_k;         /* k */
+    int32_t shared_inter;  /* Is, 0 = no shared expert */
+    moe_qformat fmt;       /* code format of every expert matrix */
+} moe_layer_desc;
+
+typedef struct {
+    const float* w_router;     /* [E][H] */
+    const float* router_bias;  /* [E] or NULL */
+    moe_qmat gate, up, down;   /* routed experts, stacked expert-major */
+    moe_qmat sh_gate, sh_up, sh_down;  /* shared expert; ignored when shared_inter == 0 */
+} moe_layer_weights;
+
+/*
+ * Router and top-k selection.
+ *   logits[t][e] = sum_h x[t][h] * w_router[e][h] + bias[e]   (fp32 accumulation)
+ *   ids[t][j]    = the j-th expert in the order (logit descending, expert index ascending),
+ *                  -0.0 and +0.0 being equal
+ *   p[t][j]      = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0) over the chosen k (fp32)
+ * logits may be NULL (then they live in the workspace). T >= 1. Workspace: MOE_CALL_ROUTE.
+ */
+moe_status moe_route(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x, int32_t T,
+                     float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stable counting sort of the pairs q = t*k + j by expert ids[q] (integer, deterministic):
+ *   offsets[e] = number of pairs with expert < e (offsets[E] = T*k);
+ *   pos(q) = offsets[ids[q]] + number of earlier pairs q' < q with the same expert;
+ *   perm[pos(q)] = q, inv[q] = pos(q).
+ * Workspace: MOE_CALL_PERMUTE.
+ */
+moe_status moe_permute(const moe_layer_desc* desc, const int32_t* ids, int32_t T, int32_t* offsets, int32_t* perm,
+                       int32_t* inv, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Expert FFNs for a decode step of 1 <= T <= 4 tokens (T > 4 returns MOE_ERR_UNSUPPORTED).
+ * Each distinct chosen expert's weights are read once for all tokens that chose it.
+ *   y_pairs[q]  = D_e (silu(G_e x_t) * (U_e x_t)), e = ids[q], for every pair q = t*k + j
+ *   y_shared[t] = the shared expert on x_t (required iff Is > 0, else ignored)
+ * Math in fp32; dequantised weights are exact. Workspace: MOE_CALL_EXPERTS_DECODE.
+ */
+moe_status moe_experts_decode(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x,
+                              int32_t T, const int32_t* ids, float* y_pairs, float* y_shared, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
+ * Expert FFNs for a prefill chunk (any T >= 1): a grouped GEMM over expert-sorted row tiles
+ * (rows in perm order, groups from offsets, as moe_permute returns them), with the shared
+ * expert as one more group of all T tokens.
+ *   y_sorted[i] = expert FFN of pair perm[i] (sorted order), y_shared[t] as above.
+ * Operands are fp16 on the matrix cores (x converted from bf16, weights dequantised once to fp16,
+ * the SwiGLU activation h kept in fp16) with fp32 accumulation and fp32 outputs.
+ * Workspace: MOE_CALL_EXPERTS_PREFILL.
+ */
+moe_status moe_experts_prefill(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x,
+                               int32_t T, const int32_t* offsets, const int32_t* perm, float* y_sorted,
+                               float* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weighted combine, atomic-free and deterministic:
+ *   out[t] = sum_{j=0}^{k-1} p[t][j] * y_rows[r(t,j)] + y_shared[t]     (slot order, then shared)
+ * with r(t,j) = row_of_pair[t*k+j] (e.g. inv from moe_permute) or t*k+j when row_of_pair is NULL.
+ * y_shared may be NULL (no shared term). No workspace.
+ */
+moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const float* p, const float* y_rows,
+                       const int32_t* row_of_pair, const float* y_shared, float* out, void* stream);
+
+/*
+ * The whole layer: route, permute, experts, combine. T <= 4 takes the decode path, larger T the
+ * prefill path. out [T][H] fp32. logits/ids/p are optional outputs (NULL = kept in the workspace).
+ * Workspace: MOE_CALL_LAYER.
+ */
+moe_status moe_layer(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x, int32_t T,
+                     float* out, float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Bytes of workspace an entry point needs for this shape (host only; no GPU work). */
+moe_status moe_workspace_size(const moe_layer_desc* desc, int32_t T, moe_call call, size_t* bytes);
+
+/* Static string for a status code (host only). */
+const char* moe_status_string(moe_status status);
+
+/* MOE_ABI_VERSION of the built library (host only). */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -68,6 +68,7 @@ def load(path: str):
     L.orc_token.argtypes = [ctypes.POINTER(_Layer), vp, vp, vp, vp, vp, vp, vp, vp]
     L.orc_layer_forward.restype = ctypes.c_int
     L.orc_layer_forward.argtypes = [ctypes.POINTER(_Layer), vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.orc_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
     L.orc_dense_masked.restype = ctypes.c_int
     L.orc_dense_masked.argtypes = [ctypes.POINTER(_Layer), vp, i32, vp]
     return L
@@ -204,6 +205,19 @@ def permute(ids: np.ndarray, E: int):
     inv = np.empty(T * k, np.int32)
     lib().orc_permute(_p(i), T, k, E, _p(offsets), _p(perm), _p(inv))
     return offsets, perm, inv
+
+
+def combine(p: np.ndarray, y_rows: np.ndarray, row_of_pair=None, y_shared=None) -> np.ndarray:
+    """Weighted combine of given expert outputs (fp64): p [T][k], y_rows [rows][H]."""
+    pp = np.ascontiguousarray(p, np.float64)
+    T, k = pp.shape
+    yr = np.ascontiguousarray(y_rows, np.float64)
+    H = yr.shape[-1]
+    rp = None if row_of_pair is None else np.ascontiguousarray(row_of_pair, np.int32)
+    ys = None if y_shared is None else np.ascontiguousarray(y_shared, np.float64)
+    out = np.empty((T, H))
+    lib().orc_combine(T, k, H, _p(pp), _p(yr), _p(rp), _p(ys), _p(out))
+    return out
 
 
 def expert_ffn(fmt, H, I, gate, up, down, x):

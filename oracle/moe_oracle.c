@@ -257,6 +257,25 @@ int orc_layer_forward(const orc_layer* L, const uint16_t* x, int32_t T, const do
     return 0;
 }
 
+/*
+ * Combine alone, on given expert outputs: out[t] = sum_j p[t][j] * y_rows[r(t,j)] (slot order) +
+ * y_shared[t], with r(t,j) = row_of_pair[t*k+j], or t*k+j when row_of_pair is NULL; y_shared may be
+ * NULL. The same sum orc_token forms from its own expert outputs.
+ */
+void orc_combine(int32_t T, int32_t k, int32_t H, const double* p, const double* y_rows, const int32_t* row_of_pair,
+                 const double* y_shared, double* out) {
+    for (int32_t t = 0; t < T; ++t)
+        for (int32_t m = 0; m < H; ++m) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                int64_t q = (int64_t)t * k + j;
+                int64_t r = row_of_pair ? row_of_pair[q] : q;
+                acc += p[q] * y_rows[r * H + m];
+            }
+            out[(int64_t)t * H + m] = acc + (y_shared ? y_shared[(int64_t)t * H + m] : 0.0);
+        }
+}
+
 /* ------------------------------------------------------------------ brute force */
 
 int orc_dense_masked(const orc_layer* L, const uint16_t* x, int32_t T, double* Y) {

@@ -70,6 +70,9 @@ int orc_token(const orc_layer* L, const uint16_t* x_row, const double* logits_in
 int orc_layer_forward(const orc_layer* L, const uint16_t* x, int32_t T, const double* logits_in,
                       double* logits, int32_t* ids, double* p, double* y_pairs, double* y_shared,
                       double* Y);
+/* out[t] = sum_j p[t][j] * y_rows[row_of_pair ? row_of_pair[t*k+j] : t*k+j] + y_shared[t] (NULL = 0) */
+void orc_combine(int32_t T, int32_t k, int32_t H, const double* p, const double* y_rows, const int32_t* row_of_pair,
+                 const double* y_shared, double* out);
 /*
  * Brute force: every expert on every token, weighted by a mask that is the full softmax restricted
  * to the k best experts (by rank counting) and renormalised, summed in expert order, plus shared.

@@ -1,0 +1,272 @@
+"""Python binding of ``libmoe.so`` (include/moe.h): the routed, block-quantized MoE expert layer on
+AMD Instinct MI355X (gfx950).
+
+This module only marshals arguments: torch tensors supply device memory and the current HIP
+stream, ctypes passes plain pointers to the C ABI, and every step of the layer runs in the HIP
+kernels of ``csrc/``. There is no fallback: if the library is missing or fails to load, importing
+the binding works but every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MoeError", "LayerDesc", "DeviceLayer", "Workspace", "lib", "library_path",
+    "moe_route", "moe_permute", "moe_experts_decode", "moe_experts_prefill", "moe_combine", "moe_layer",
+    "moe_workspace_size", "moe_status_string", "moe_abi_version",
+    "MOE_Q8_B32", "MOE_Q4_B32", "MOE_Q2_B32",
+    "MOE_CALL_ROUTE", "MOE_CALL_PERMUTE", "MOE_CALL_EXPERTS_DECODE", "MOE_CALL_EXPERTS_PREFILL",
+    "MOE_CALL_COMBINE", "MOE_CALL_LAYER",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_Q8_B32, MOE_Q4_B32, MOE_Q2_B32 = 0, 1, 2
+(MOE_CALL_ROUTE, MOE_CALL_PERMUTE, MOE_CALL_EXPERTS_DECODE, MOE_CALL_EXPERTS_PREFILL, MOE_CALL_COMBINE,
+ MOE_CALL_LAYER) = range(6)
+_BITS = {MOE_Q8_B32: 8, MOE_Q4_B32: 4, MOE_Q2_B32: 2}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s (status %d)" % (what, moe_status_string(status), status))
+        self.status = status
+
+
+class _QMat(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("shared_inter", ctypes.c_int32), ("fmt", ctypes.c_int32)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("w_router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("gate", _QMat), ("up", _QMat), ("down", _QMat),
+                ("sh_gate", _QMat), ("sh_up", _QMat), ("sh_down", _QMat)]
+
+
+_lib = None
+_lib_error = None
+
+
+def lib():
+    """The loaded C library (raises if it is not built or does not load)."""
+    global _lib, _lib_error
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError("libmoe.so is not built (run quantized_expert_ffn_moe_amd/build.py); "
+                               "there is no fallback path")
+        L = ctypes.CDLL(library_path)
+        vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32
+        D, W = ctypes.POINTER(_Desc), ctypes.POINTER(_Weights)
+        sz = ctypes.c_size_t
+        L.moe_route.restype = st
+        L.moe_route.argtypes = [D, W, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_permute.restype = st
+        L.moe_permute.argtypes = [D, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_experts_decode.restype = st
+        L.moe_experts_decode.argtypes = [D, W, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_experts_prefill.restype = st
+        L.moe_experts_prefill.argtypes = [D, W, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_combine.restype = st
+        L.moe_combine.argtypes = [D, i32, vp, vp, vp, vp, vp, vp]
+        L.moe_layer.restype = st
+        L.moe_layer.argtypes = [D, W, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_workspace_size.restype = st
+        L.moe_workspace_size.argtypes = [D, i32, i32, ctypes.POINTER(sz)]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [st]
+        L.moe_abi_version.restype = i32
+        L.moe_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def moe_abi_version() -> int:
+    return int(lib().moe_abi_version())
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoeError(status, what)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError("expected a device tensor, got %s" % t.device)
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+class LayerDesc:
+    def __init__(self, hidden: int, inter: int, num_experts: int, top_k: int, shared_inter: int, fmt: int):
+        self.hidden, self.inter, self.num_experts = hidden, inter, num_experts
+        self.top_k, self.shared_inter, self.fmt = top_k, shared_inter, fmt
+        self.c = _Desc(hidden, inter, num_experts, top_k, shared_inter, fmt)
+
+    @classmethod
+    def from_spec(cls, spec) -> "LayerDesc":
+        return cls(spec.H, spec.I, spec.E, spec.k, spec.Is, spec.fmt)
+
+
+class DeviceLayer:
+    """Device-resident weights of one layer in the canonical layout, plus the C descriptor."""
+
+    def __init__(self, desc: LayerDesc, w_router, router_bias, gate, up, down, sh_gate=None, sh_up=None, sh_down=None):
+        self.desc = desc
+        self.w_router, self.router_bias = w_router, router_bias
+        self.mats = dict(gate=gate, up=up, down=down, sh_gate=sh_gate, sh_up=sh_up, sh_down=sh_down)
+
+        def qm(pair):
+            return _QMat(None, None) if pair is None else _QMat(_ptr(pair[0]), _ptr(pair[1]))
+
+        self.c = _Weights(_ptr(w_router), _ptr(router_bias), qm(gate), qm(up), qm(down), qm(sh_gate), qm(sh_up),
+                          qm(sh_down))
+
+    @classmethod
+    def from_host(cls, desc: LayerDesc, d: dict, device="cuda") -> "DeviceLayer":
+        """Upload a dict of numpy arrays (w_router, router_bias, gate/up/down/sh_* as (codes, scales))."""
+        def up(a, dt):
+            if a is None:
+                return None
+            return torch.from_numpy(a).to(device=device, dtype=dt).contiguous()
+
+        def pair(p):
+            if p is None:
+                return None
+            return (torch.from_numpy(p[0]).to(device), torch.from_numpy(p[1].view("int16")).to(device))
+
+        return cls(desc, up(d["w_router"], torch.float32), up(d.get("router_bias"), torch.float32), pair(d["gate"]),
+                   pair(d["up"]), pair(d["down"]), pair(d.get("sh_gate")), pair(d.get("sh_up")), pair(d.get("sh_down")))
+
+
+class Workspace:
+    """A growable device byte buffer handed to the library (the library itself allocates nothing)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def moe_workspace_size(desc: LayerDesc, T: int, call: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_workspace_size(ctypes.byref(desc.c), T, call, ctypes.byref(n)), "moe_workspace_size")
+    return int(n.value)
+
+
+def _ws(layer_desc, T, call, ws):
+    need = moe_workspace_size(layer_desc, T, call)
+    if ws is None:
+        ws = Workspace()
+    buf = ws.get(need) if isinstance(ws, Workspace) else ws
+    return buf, (0 if buf is None else buf.numel())
+
+
+def _x_bits(x):
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16)
+    if x.dtype in (torch.int16, torch.uint16):
+        return x
+    raise TypeError("x must be bf16 (or its 16-bit pattern)")
+
+
+def moe_route(layer: DeviceLayer, x, logits=None, ids=None, p=None, ws=None, stream=None):
+    d = layer.desc
+    T = x.shape[0]
+    dev = x.device
+    ids = torch.empty((T, d.top_k), dtype=torch.int32, device=dev) if ids is None else ids
+    p = torch.empty((T, d.top_k), dtype=torch.float32, device=dev) if p is None else p
+    buf, nb = _ws(d, T, MOE_CALL_ROUTE, ws) if logits is None else (None, 0)
+    _check(lib().moe_route(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(logits), _ptr(ids),
+                           _ptr(p), _ptr(buf), nb, _stream(stream)), "moe_route")
+    return logits, ids, p
+
+
+def moe_permute(layer: DeviceLayer, ids, offsets=None, perm=None, inv=None, ws=None, stream=None):
+    d = layer.desc
+    T = ids.shape[0]
+    dev = ids.device
+    offsets = torch.empty(d.num_experts + 1, dtype=torch.int32, device=dev) if offsets is None else offsets
+    perm = torch.empty(T * d.top_k, dtype=torch.int32, device=dev) if perm is None else perm
+    inv = torch.empty(T * d.top_k, dtype=torch.int32, device=dev) if inv is None else inv
+    buf, nb = _ws(d, T, MOE_CALL_PERMUTE, ws)
+    _check(lib().moe_permute(ctypes.byref(d.c), _ptr(ids), T, _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(buf), nb,
+                             _stream(stream)), "moe_permute")
+    return offsets, perm, inv
+
+
+def moe_experts_decode(layer: DeviceLayer, x, ids, y_pairs=None, y_shared=None, ws=None, stream=None):
+    d = layer.desc
+    T = x.shape[0]
+    dev = x.device
+    y_pairs = torch.empty((T * d.top_k, d.hidden), dtype=torch.float32, device=dev) if y_pairs is None else y_pairs
+    if y_shared is None and d.shared_inter > 0:
+        y_shared = torch.empty((T, d.hidden), dtype=torch.float32, device=dev)
+    buf, nb = _ws(d, T, MOE_CALL_EXPERTS_DECODE, ws)
+    _check(lib().moe_experts_decode(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(ids),
+                                    _ptr(y_pairs), _ptr(y_shared), _ptr(buf), nb, _stream(stream)),
+           "moe_experts_decode")
+    return y_pairs, y_shared
+
+
+def moe_experts_prefill(layer: DeviceLayer, x, offsets, perm, y_sorted=None, y_shared=None, ws=None, stream=None):
+    d = layer.desc
+    T = x.shape[0]
+    dev = x.device
+    y_sorted = torch.empty((T * d.top_k, d.hidden), dtype=torch.float32, device=dev) if y_sorted is None else y_sorted
+    if y_shared is None and d.shared_inter > 0:
+        y_shared = torch.empty((T, d.hidden), dtype=torch.float32, device=dev)
+    buf, nb = _ws(d, T, MOE_CALL_EXPERTS_PREFILL, ws)
+    _check(lib().moe_experts_prefill(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(offsets),
+                                     _ptr(perm), _ptr(y_sorted), _ptr(y_shared), _ptr(buf), nb, _stream(stream)),
+           "moe_experts_prefill")
+    return y_sorted, y_shared
+
+
+def moe_combine(layer_or_desc, p, y_rows, row_of_pair=None, y_shared=None, out=None, stream=None):
+    d = layer_or_desc.desc if isinstance(layer_or_desc, DeviceLayer) else layer_or_desc
+    T = p.shape[0]
+    out = torch.empty((T, d.hidden), dtype=torch.float32, device=p.device) if out is None else out
+    _check(lib().moe_combine(ctypes.byref(d.c), T, _ptr(p), _ptr(y_rows), _ptr(row_of_pair), _ptr(y_shared),
+                             _ptr(out), _stream(stream)), "moe_combine")
+    return out
+
+
+def moe_layer(layer: DeviceLayer, x, out=None, logits=None, ids=None, p=None, ws=None, stream=None):
+    d = layer.desc
+    T = x.shape[0]
+    out = torch.empty((T, d.hidden), dtype=torch.float32, device=x.device) if out is None else out
+    buf, nb = _ws(d, T, MOE_CALL_LAYER, ws)
+    _check(lib().moe_layer(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(out), _ptr(logits),
+                           _ptr(ids), _ptr(p), _ptr(buf), nb, _stream(stream)), "moe_layer")
+    return out

@@ -1,0 +1,294 @@
+// The C ABI of include/moe.h: host-side argument checks, workspace carving and stream-ordered
+// launches. Nothing here allocates device memory or synchronises the stream.
+#include <string.h>
+
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxE = 1024, kMaxK = 16, kMaxH = 16384, kMaxI = 4096, kMaxT = 1 << 20;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status check_desc(const moe_layer_desc* d) {
+    if (!d) return MOE_ERR_INVALID_ARG;
+    if (d->fmt != MOE_Q8_B32 && d->fmt != MOE_Q4_B32 && d->fmt != MOE_Q2_B32) return MOE_ERR_INVALID_ARG;
+    if (d->hidden < 32 || d->hidden > kMaxH || d->hidden % 32) return MOE_ERR_INVALID_ARG;
+    if (d->inter < 32 || d->inter > kMaxI || d->inter % 32) return MOE_ERR_INVALID_ARG;
+    if (d->shared_inter < 0 || d->shared_inter > kMaxI || d->shared_inter % 32) return MOE_ERR_INVALID_ARG;
+    if (d->num_experts < 1 || d->num_experts > kMaxE) return MOE_ERR_INVALID_ARG;
+    if (d->top_k < 1 || d->top_k > kMaxK || d->top_k > d->num_experts) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status check_T(int32_t T) { return (T >= 1 && T <= kMaxT) ? MOE_OK : MOE_ERR_INVALID_ARG; }
+
+bool prefill_shape_ok(const moe_layer_desc* d) {
+    return d->hidden % 64 == 0 && d->inter % 64 == 0 && d->shared_inter % 64 == 0;
+}
+
+bool qmat_ok(const moe_qmat& q) { return q.codes && q.scales && aligned16(q.codes) && ((uintptr_t)q.scales & 1u) == 0; }
+
+moe_status check_expert_weights(const moe_layer_desc* d, const moe_layer_weights* w) {
+    if (!w) return MOE_ERR_INVALID_ARG;
+    if (!qmat_ok(w->gate) || !qmat_ok(w->up) || !qmat_ok(w->down)) return MOE_ERR_INVALID_ARG;
+    if (d->shared_inter > 0 && (!qmat_ok(w->sh_gate) || !qmat_ok(w->sh_up) || !qmat_ok(w->sh_down)))
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status check_router_weights(const moe_layer_weights* w) {
+    if (!w || !w->w_router || !aligned16(w->w_router)) return MOE_ERR_INVALID_ARG;
+    if (w->router_bias && ((uintptr_t)w->router_bias & 3u)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+LayerView view(const moe_layer_desc* d, const moe_layer_weights* w) {
+    LayerView L;
+    L.H = d->hidden; L.I = d->inter; L.E = d->num_experts; L.k = d->top_k; L.Is = d->shared_inter; L.fmt = d->fmt;
+    L.w_router = w->w_router; L.bias = w->router_bias;
+    L.g_codes = (const uint8_t*)w->gate.codes; L.g_scales = w->gate.scales;
+    L.u_codes = (const uint8_t*)w->up.codes; L.u_scales = w->up.scales;
+    L.d_codes = (const uint8_t*)w->down.codes; L.d_scales = w->down.scales;
+    const bool sh = d->shared_inter > 0;
+    L.sg_codes = sh ? (const uint8_t*)w->sh_gate.codes : nullptr; L.sg_scales = sh ? w->sh_gate.scales : nullptr;
+    L.su_codes = sh ? (const uint8_t*)w->sh_up.codes : nullptr; L.su_scales = sh ? w->sh_up.scales : nullptr;
+    L.sd_codes = sh ? (const uint8_t*)w->sh_down.codes : nullptr; L.sd_scales = sh ? w->sh_down.scales : nullptr;
+    return L;
+}
+
+LayerView shape_view(const moe_layer_desc* d) {
+    LayerView L{};
+    L.H = d->hidden; L.I = d->inter; L.E = d->num_experts; L.k = d->top_k; L.Is = d->shared_inter; L.fmt = d->fmt;
+    return L;
+}
+
+// ------------------------------------------------------------------ workspace layouts
+
+struct RouteWs { float* logits; };
+RouteWs carve_route(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
+    Carve c(base);
+    RouteWs r;
+    r.logits = c.take<float>((size_t)T * d->num_experts);
+    if (bytes) *bytes = c.bytes();
+    return r;
+}
+
+struct PermWs { int32_t* chunks; };
+PermWs carve_perm(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
+    Carve c(base);
+    PermWs r;
+    r.chunks = c.take<int32_t>((size_t)perm_chunks(T) * d->num_experts);
+    if (bytes) *bytes = c.bytes();
+    return r;
+}
+
+struct DecodeWs { float* h; };
+DecodeWs carve_decode(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
+    Carve c(base);
+    DecodeWs r;
+    r.h = c.take<float>(decode_scratch_floats(shape_view(d), T));
+    if (bytes) *bytes = c.bytes();
+    return r;
+}
+
+struct PrefillWs { void* scratch; };
+PrefillWs carve_prefill_ws(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
+    Carve c(base);
+    PrefillWs r;
+    r.scratch = c.take<char>(prefill_scratch_bytes(shape_view(d), T));
+    if (bytes) *bytes = c.bytes();
+    return r;
+}
+
+struct LayerWs {
+    float* logits;
+    int32_t* ids;
+    float* p;
+    float* y_rows;     // y_pairs (decode) or y_sorted (prefill), [T*k][H]
+    float* y_shared;   // [T][H]
+    int32_t *offsets, *perm, *inv, *chunks;  // prefill only
+    float* h;          // decode only
+    void* prefill;     // prefill only
+};
+LayerWs carve_layer(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
+    Carve c(base);
+    LayerWs r{};
+    const size_t P = (size_t)T * d->top_k;
+    r.logits = c.take<float>((size_t)T * d->num_experts);
+    r.ids = c.take<int32_t>(P);
+    r.p = c.take<float>(P);
+    r.y_rows = c.take<float>(P * d->hidden);
+    r.y_shared = c.take<float>((size_t)T * d->hidden);
+    if (T <= 4) {
+        r.h = c.take<float>(decode_scratch_floats(shape_view(d), T));
+    } else {
+        r.offsets = c.take<int32_t>((size_t)d->num_experts + 1);
+        r.perm = c.take<int32_t>(P);
+        r.inv = c.take<int32_t>(P);
+        r.chunks = c.take<int32_t>((size_t)perm_chunks(T) * d->num_experts);
+        r.prefill = c.take<char>(prefill_scratch_bytes(shape_view(d), T));
+    }
+    if (bytes) *bytes = c.bytes();
+    return r;
+}
+
+moe_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return MOE_OK;
+    if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+    return ws_bytes >= need ? MOE_OK : MOE_ERR_WORKSPACE;
+}
+
+#define MOE_TRY(expr)                   \
+    do {                                \
+        moe_status _st = (expr);        \
+        if (_st != MOE_OK) return _st;  \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+moe_status moe_workspace_size(const moe_layer_desc* d, int32_t T, moe_call call, size_t* bytes) {
+    MOE_TRY(check_desc(d));
+    MOE_TRY(check_T(T));
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    size_t b = 0;
+    switch (call) {
+        case MOE_CALL_ROUTE: carve_route(d, T, nullptr, &b); break;
+        case MOE_CALL_PERMUTE: carve_perm(d, T, nullptr, &b); break;
+        case MOE_CALL_EXPERTS_DECODE:
+            if (T > 4) return MOE_ERR_UNSUPPORTED;
+            carve_decode(d, T, nullptr, &b);
+            break;
+        case MOE_CALL_EXPERTS_PREFILL:
+            if (!prefill_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
+            carve_prefill_ws(d, T, nullptr, &b);
+            break;
+        case MOE_CALL_COMBINE: b = 0; break;
+        case MOE_CALL_LAYER:
+            if (T > 4 && !prefill_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
+            carve_layer(d, T, nullptr, &b);
+            break;
+        default: return MOE_ERR_INVALID_ARG;
+    }
+    *bytes = b;
+    return MOE_OK;
+}
+
+moe_status moe_route(const moe_layer_desc* d, const moe_layer_weights* w, const uint16_t* x, int32_t T,
+                     float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_desc(d));
+    MOE_TRY(check_T(T));
+    MOE_TRY(check_router_weights(w));
+    if (!x || !aligned16(x) || !ids || !p) return MOE_ERR_INVALID_ARG;
+    if (logits && ((uintptr_t)logits & 3u)) return MOE_ERR_INVALID_ARG;
+    size_t need = 0;
+    carve_route(d, T, nullptr, &need);
+    if (!logits) MOE_TRY(check_ws(ws, ws_bytes, need));
+    float* lg = logits ? logits : carve_route(d, T, ws, nullptr).logits;
+    hipStream_t s = (hipStream_t)stream;
+    MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, lg, s));
+    return launch_topk(lg, T, d->num_experts, d->top_k, ids, p, s);
+}
+
+moe_status moe_permute(const moe_layer_desc* d, const int32_t* ids, int32_t T, int32_t* offsets, int32_t* perm,
+                       int32_t* inv, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_desc(d));
+    MOE_TRY(check_T(T));
+    if (!ids || !offsets || !perm || !inv) return MOE_ERR_INVALID_ARG;
+    size_t need = 0;
+    carve_perm(d, T, nullptr, &need);
+    MOE_TRY(check_ws(ws, ws_bytes, need));
+    return launch_permute(ids, T, d->top_k, d->num_experts, offsets, perm, inv, carve_perm(d, T, ws, nullptr).chunks,
+                          (hipStream_t)stream);
+}
+
+moe_status moe_experts_decode(const moe_layer_desc* d, const moe_layer_weights* w, const uint16_t* x, int32_t T,
+                              const int32_t* ids, float* y_pairs, float* y_shared, void* ws, size_t ws_bytes,
+                              void* stream) {
+    MOE_TRY(check_desc(d));
+    MOE_TRY(check_T(T));
+    if (T > 4) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(check_expert_weights(d, w));
+    if (!x || !aligned16(x) || !ids || !y_pairs || !aligned16(y_pairs)) return MOE_ERR_INVALID_ARG;
+    if (d->shared_inter > 0 && (!y_shared || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
+    size_t need = 0;
+    carve_decode(d, T, nullptr, &need);
+    MOE_TRY(check_ws(ws, ws_bytes, need));
+    return launch_decode_experts(view(d, w), x, T, ids, y_pairs, y_shared, carve_decode(d, T, ws, nullptr).h,
+                                 (hipStream_t)stream);
+}
+
+moe_status moe_experts_prefill(const moe_layer_desc* d, const moe_layer_weights* w, const uint16_t* x, int32_t T,
+                               const int32_t* offsets, const int32_t* perm, float* y_sorted, float* y_shared, void* ws,
+                               size_t ws_bytes, void* stream) {
+    MOE_TRY(check_desc(d));
+    MOE_TRY(check_T(T));
+    if (!prefill_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(check_expert_weights(d, w));
+    if (!x || !aligned16(x) || !offsets || !perm || !y_sorted) return MOE_ERR_INVALID_ARG;
+    if (d->shared_inter > 0 && !y_shared) return MOE_ERR_INVALID_ARG;
+    size_t need = 0;
+    carve_prefill_ws(d, T, nullptr, &need);
+    MOE_TRY(check_ws(ws, ws_bytes, need));
+    return launch_prefill_experts(view(d, w), x, T, offsets, perm, y_sorted, y_shared,
+                                  carve_prefill_ws(d, T, ws, nullptr).scratch, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const moe_layer_desc* d, int32_t T, const float* p, const float* y_rows,
+                       const int32_t* row_of_pair, const float* y_shared, float* out, void* stream) {
+    MOE_TRY(check_desc(d));
+    MOE_TRY(check_T(T));
+    if (!p || !y_rows || !out || !aligned16(y_rows) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+    if (y_shared && !aligned16(y_shared)) return MOE_ERR_INVALID_ARG;
+    return launch_combine(T, d->top_k, d->hidden, p, y_rows, row_of_pair, y_shared, out, (hipStream_t)stream);
+}
+
+moe_status moe_layer(const moe_layer_desc* d, const moe_layer_weights* w, const uint16_t* x, int32_t T, float* out,
+                     float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_desc(d));
+    MOE_TRY(check_T(T));
+    if (T > 4 && !prefill_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
+    MOE_TRY(check_router_weights(w));
+    MOE_TRY(check_expert_weights(d, w));
+    if (!x || !aligned16(x) || !out || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+    if ((logits && ((uintptr_t)logits & 3u)) || (ids && ((uintptr_t)ids & 3u)) || (p && ((uintptr_t)p & 3u)))
+        return MOE_ERR_INVALID_ARG;
+    size_t need = 0;
+    carve_layer(d, T, nullptr, &need);
+    MOE_TRY(check_ws(ws, ws_bytes, need));
+    const LayerWs lw = carve_layer(d, T, ws, nullptr);
+    float* lg = logits ? logits : lw.logits;
+    int32_t* id = ids ? ids : lw.ids;
+    float* pr = p ? p : lw.p;
+    const LayerView L = view(d, w);
+    hipStream_t s = (hipStream_t)stream;
+    const float* ysh = d->shared_inter > 0 ? lw.y_shared : nullptr;
+    MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, L.H, L.E, lg, s));
+    MOE_TRY(launch_topk(lg, T, L.E, L.k, id, pr, s));
+    if (T <= 4) {
+        MOE_TRY(launch_decode_experts(L, x, T, id, lw.y_rows, lw.y_shared, lw.h, s));
+        return launch_combine(T, L.k, L.H, pr, lw.y_rows, nullptr, ysh, out, s);
+    }
+    MOE_TRY(launch_permute(id, T, L.k, L.E, lw.offsets, lw.perm, lw.inv, lw.chunks, s));
+    MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, lw.prefill, s));
+    return launch_combine(T, L.k, L.H, pr, lw.y_rows, lw.inv, ysh, out, s);
+}
+
+}  // extern "C"

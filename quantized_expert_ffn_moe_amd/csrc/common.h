@@ -1,0 +1,120 @@
+// Internal helpers shared by the gfx950 kernels of the MoE layer library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------------------------- numbers
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Order-preserving map of a float to uint32 with -0 folded onto +0 (NaN excluded by contract).
+__device__ __forceinline__ uint32_t ordered_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// ------------------------------------------------------------------------------------- reductions
+
+template <int kWidth>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = kWidth / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// ------------------------------------------------------------------------------------- formats
+
+// Bits per code and the byte size of one 32-element block.
+__host__ __device__ constexpr int fmt_bits(int fmt) { return fmt == MOE_Q8_B32 ? 8 : fmt == MOE_Q4_B32 ? 4 : 2; }
+__host__ __device__ constexpr int block_bytes(int fmt) { return 32 * fmt_bits(fmt) / 8; }
+__host__ __device__ inline int64_t row_bytes(int fmt, int64_t K) { return K * fmt_bits(fmt) / 8; }
+
+// Raw bytes of one 32-element block (8 dwords; Q4 uses 4, Q2 uses 2).
+struct Block32 {
+    uint32_t w[8];
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_block(const uint8_t* p, Block32& b) {
+    if constexpr (FMT == MOE_Q8_B32) {
+        const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+        const uint4 c = reinterpret_cast<const uint4*>(p)[1];
+        b.w[0] = a.x; b.w[1] = a.y; b.w[2] = a.z; b.w[3] = a.w;
+        b.w[4] = c.x; b.w[5] = c.y; b.w[6] = c.z; b.w[7] = c.w;
+    } else if constexpr (FMT == MOE_Q4_B32) {
+        const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+        b.w[0] = a.x; b.w[1] = a.y; b.w[2] = a.z; b.w[3] = a.w;
+    } else {
+        const uint2 a = reinterpret_cast<const uint2*>(p)[0];
+        b.w[0] = a.x; b.w[1] = a.y;
+    }
+}
+
+// Level of element i (0..31) of a block, as an exact float (before the scale).
+template <int FMT>
+__device__ __forceinline__ float block_level(const Block32& b, int i) {
+    if constexpr (FMT == MOE_Q8_B32) {
+        return (float)(int32_t)(int8_t)(b.w[i >> 2] >> (8 * (i & 3)));
+    } else if constexpr (FMT == MOE_Q4_B32) {
+        // element i sits in nibble i of the little-endian block
+        int32_t v = (int32_t)(b.w[i >> 3] << (28 - 4 * (i & 7))) >> 28;
+        return (float)v;
+    } else {
+        uint32_t c = (b.w[i >> 4] >> (2 * (i & 15))) & 3u;
+        return (float)c - 1.5f;
+    }
+}
+
+// ------------------------------------------------------------------------------------- launch checks
+
+#define MOE_LAUNCH_CHECK()                                  \
+    do {                                                    \
+        if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Sequential carve-out of a caller workspace with 256-byte alignment.
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T>
+    T* take(size_t n) {
+        off = align_up(off, 256);
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += n * sizeof(T);
+        return p;
+    }
+    size_t bytes() const { return align_up(off, 256); }
+};
+
+}  // namespace moe

@@ -1,0 +1,43 @@
+// Internal launchers of the gfx950 kernels (host side). Each returns MOE_OK or MOE_ERR_HIP.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// Shapes and weight pointers as the kernels see them (validated by the API layer).
+struct LayerView {
+    int H, I, E, k, Is, fmt;
+    const float* w_router;
+    const float* bias;
+    const uint8_t *g_codes, *u_codes, *d_codes;
+    const uint16_t *g_scales, *u_scales, *d_scales;
+    const uint8_t *sg_codes, *su_codes, *sd_codes;
+    const uint16_t *sg_scales, *su_scales, *sd_scales;
+    __host__ __device__ int Imax() const { return I > Is ? I : Is; }
+};
+
+moe_status launch_router(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
+                         float* logits, hipStream_t s);
+moe_status launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* p, hipStream_t s);
+
+// permutation: counts/bases scratch of chunks(T) * E ints
+int perm_chunks(int T);
+moe_status launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* perm, int32_t* inv,
+                          int32_t* chunk_scratch, hipStream_t s);
+
+// decode experts: h scratch of (T*k + 1) * T * Imax floats
+size_t decode_scratch_floats(const LayerView& L, int T);
+moe_status launch_decode_experts(const LayerView& L, const uint16_t* x, int T, const int32_t* ids, float* y_pairs,
+                                 float* y_shared, float* h_scratch, hipStream_t s);
+
+// prefill experts
+size_t prefill_scratch_bytes(const LayerView& L, int T);
+moe_status launch_prefill_experts(const LayerView& L, const uint16_t* x, int T, const int32_t* offsets,
+                                  const int32_t* perm, float* y_sorted, float* y_shared, void* scratch,
+                                  hipStream_t s);
+
+moe_status launch_combine(int T, int k, int H, const float* p, const float* y_rows, const int32_t* row_of_pair,
+                          const float* y_shared, float* out, hipStream_t s);
+
+}  // namespace moe

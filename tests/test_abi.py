@@ -1,0 +1,114 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point include/moe.h declares, sizes
+workspaces, and rejects bad arguments on the host before any GPU work (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_expert_ffn_moe_amd as moe
+from quantized_expert_ffn_moe_amd import build as moe_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(moe.library_path):
+        moe_build.build()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"moe_route", "moe_permute", "moe_experts_decode", "moe_experts_prefill", "moe_combine", "moe_layer",
+            "moe_workspace_size", "moe_status_string", "moe_abi_version"} <= set(names)
+    L = ctypes.CDLL(moe.library_path)
+    for n in names:
+        assert hasattr(L, n), n
+    assert moe.moe_abi_version() == 1
+    assert moe.moe_status_string(moe.MOE_ERR_WORKSPACE) == "workspace too small"
+
+
+def D(H=2048, I=512, E=256, k=8, Is=512, fmt=moe.MOE_Q4_B32):
+    return moe.LayerDesc(H, I, E, k, Is, fmt)
+
+
+def test_workspace_sizes():
+    d = D()
+    for call in range(6):
+        n = moe.moe_workspace_size(d, 1, call)
+        assert n >= 0
+    assert moe.moe_workspace_size(d, 8192, moe.MOE_CALL_LAYER) > 8192 * 8 * 2048 * 4   # holds y_sorted
+    assert moe.moe_workspace_size(d, 4, moe.MOE_CALL_COMBINE) == 0
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_workspace_size(d, 5, moe.MOE_CALL_EXPERTS_DECODE)
+    assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_workspace_size(D(H=96), 8, moe.MOE_CALL_EXPERTS_PREFILL)      # 96 % 64 != 0
+    assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("bad", [dict(k=0), dict(k=17, E=32), dict(k=9, E=8), dict(E=1025), dict(H=100),
+                                 dict(I=0), dict(Is=48 + 1), dict(fmt=3), dict(H=32768)])
+def test_bad_descriptors(bad):
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_workspace_size(D(**bad), 1, moe.MOE_CALL_LAYER)
+    assert e.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def _raw(fn, *args):
+    return getattr(moe.lib(), fn)(*args)
+
+
+def test_host_validation_rejects_before_launch():
+    """Invalid calls return a status without touching the GPU (fake but aligned device addresses)."""
+    d = D()
+    fake = 0x10000
+    w = moe._Weights(fake, None, moe._QMat(fake, fake), moe._QMat(fake, fake), moe._QMat(fake, fake),
+                     moe._QMat(fake, fake), moe._QMat(fake, fake), moe._QMat(fake, fake))
+    ref = ctypes.byref
+    # T = 0
+    assert _raw("moe_layer", ref(d.c), ref(w), fake, 0, fake, None, None, None, fake, 1 << 40, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    # misaligned x
+    assert _raw("moe_layer", ref(d.c), ref(w), fake + 2, 1, fake, None, None, None, fake, 1 << 40, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    # workspace too small
+    assert _raw("moe_layer", ref(d.c), ref(w), fake, 1, fake, None, None, None, fake, 64, None) == \
+        moe.MOE_ERR_WORKSPACE
+    # missing workspace
+    assert _raw("moe_layer", ref(d.c), ref(w), fake, 1, fake, None, None, None, None, 0, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    # decode entry with T > 4
+    assert _raw("moe_experts_decode", ref(d.c), ref(w), fake, 5, fake, fake, fake, fake, 1 << 40, None) == \
+        moe.MOE_ERR_UNSUPPORTED
+    # null router weights for route
+    w2 = moe._Weights(None, None, w.gate, w.up, w.down, w.sh_gate, w.sh_up, w.sh_down)
+    assert _raw("moe_route", ref(d.c), ref(w2), fake, 1, fake, fake, fake, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    # shared expert declared but missing
+    w3 = moe._Weights(fake, None, w.gate, w.up, w.down, moe._QMat(None, None), w.sh_up, w.sh_down)
+    assert _raw("moe_experts_decode", ref(d.c), ref(w3), fake, 1, fake, fake, fake, fake, 1 << 40, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    # permute without outputs
+    assert _raw("moe_permute", ref(d.c), fake, 4, None, fake, fake, fake, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    # combine with misaligned rows
+    assert _raw("moe_combine", ref(d.c), 1, fake, fake + 4, None, None, fake, None) == moe.MOE_ERR_INVALID_ARG
+    # prefill with a shape the MFMA path does not tile
+    d96 = D(H=96, I=64, Is=0)
+    assert _raw("moe_experts_prefill", ref(d96.c), ref(w), fake, 8, fake, fake, fake, None, fake, 1 << 40, None) == \
+        moe.MOE_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    d = D(H=64, I=64, E=4, k=2, Is=0)
+    with pytest.raises(ValueError):
+        moe.DeviceLayer(d, torch.zeros(4, 64), None, (torch.zeros(1, dtype=torch.uint8), torch.zeros(1)),
+                        (torch.zeros(1), torch.zeros(1)), (torch.zeros(1), torch.zeros(1)))

@@ -30,6 +30,7 @@ MUTANTS = {
     "combine_ignores_p": ("acc[m] += pr[j] * y[m];", "acc[m] += y[m];"),
     "shared_dropped": ("for (int32_t m = 0; m < H; ++m) acc[m] += y[m];", ";"),
     "permutation_unstable": ("int32_t pos = offsets[e] + seen[e];", "int32_t pos = offsets[e + 1] - 1 - seen[e];"),
+    "combine_alone_row_map": ("int64_t r = row_of_pair ? row_of_pair[q] : q;", "int64_t r = q;"),
     "up_uses_gate": ("u += weight(fmt, u_codes, u_scales, H, n, kappa) * x[kappa];",
                      "u += weight(fmt, g_codes, g_scales, H, n, kappa) * x[kappa];"),
 }

@@ -106,6 +106,7 @@ def golden_layer(g):
             c, s = pack_spec(fmt, g["shared"][name], N, K)
             sh["sh_" + name] = (c[None], s[None])
     L = oracle.Layer(H, I, E, k, fmt, wr, None, mats["gate"], mats["up"], mats["down"], Is, **sh)
+    L.host = dict(w_router=wr, router_bias=None, gate=mats["gate"], up=mats["up"], down=mats["down"], **sh)
     return L, xb
 
 
@@ -316,6 +317,22 @@ def pin_logits_override():
     np.testing.assert_allclose(out["p"], 0.5, rtol=1e-15)
 
 
+def pin_combine_alone():
+    """The stand-alone combine reproduces the layer's Y from its own parts, in pair order and through a
+    row map (rows stored in a shuffled order)."""
+    spec, d, L = tiny_layer(synth.Q4, H=64, I=32, E=6, k=3, Is=32, T=4)
+    out = L.forward(d["x"])
+    yp = out["y_pairs"].reshape(-1, spec.H)
+    np.testing.assert_allclose(oracle.combine(out["p"], yp, None, out["y_shared"]), out["Y"], rtol=1e-14, atol=1e-15)
+    order = np.random.default_rng(4).permutation(yp.shape[0]).astype(np.int32)   # row r holds pair order[r]
+    rows = np.empty_like(order)
+    rows[order] = np.arange(len(order), dtype=np.int32)
+    got = oracle.combine(out["p"], yp[order], rows, out["y_shared"])
+    np.testing.assert_allclose(got, out["Y"], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(oracle.combine(out["p"], yp, None, None), out["Y"] - out["y_shared"], rtol=1e-12,
+                               atol=1e-14)
+
+
 ALL_PINS = (
     [("golden:" + os.path.basename(f), (lambda f=f: pin_golden(f))) for f in GOLDEN_FILES]
     + [("f16_reader", pin_f16_reader), ("bf16_reader", pin_bf16_reader), ("levels", pin_levels_exhaustive)]
@@ -325,7 +342,7 @@ ALL_PINS = (
     + [("expert_numpy:" + synth.FMT_NAMES[f], (lambda f=f: pin_expert_numpy(f))) for f in (synth.Q8, synth.Q4, synth.Q2)]
     + [("dense_masked:" + synth.FMT_NAMES[f], (lambda f=f: pin_dense_masked(f))) for f in (synth.Q8, synth.Q4, synth.Q2)]
     + [("full_mixture", pin_full_mixture), ("k1_single_ffn", pin_k1_single_ffn), ("relabel", pin_relabel),
-       ("scale_down", pin_scale_down), ("logits_override", pin_logits_override)]
+       ("scale_down", pin_scale_down), ("logits_override", pin_logits_override), ("combine_alone", pin_combine_alone)]
 )
 
 
