@@ -67,22 +67,21 @@ def dev_x(x):
     return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
 
 
-def time_calls(fn_list, warmup: int, reps: int):
-    """Per-call HIP-event durations (ms) of a list of zero-arg launches, on torch's current stream."""
+def time_calls(fn_list, warmup: int, reps: int) -> float:
+    """Average duration (ms) of one launch from a list of zero-arg launches, played back to back
+    reps times between two HIP events on torch's current stream (the stream the library uses)."""
     for _ in range(warmup):
         for f in fn_list:
             f()
     torch.cuda.synchronize()
-    evs = []
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
     for _ in range(reps):
         for f in fn_list:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
             f()
-            b.record()
-            evs.append((a, b))
+    b.record()
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
+    return a.elapsed_time(b) / (reps * len(fn_list))
 
 
 def decode_workload(name: str, steps: int, warmup: int):
@@ -133,13 +132,12 @@ def decode_workload(name: str, steps: int, warmup: int):
     ews = moe.Workspace()
     ecalls = [lambda L=L, x=x, i=i: moe.moe_experts_decode(L, x, i, y_pairs=ypairs, y_shared=ysh, ws=ews)
               for L, x, i in zip(layers, xs, ids)]
-    durs = time_calls(ecalls, 2, max(3, steps))
-    avg_ms = float(np.mean(durs))
+    avg_ms = time_calls(ecalls, 2, max(3, steps))
     bytes_per_launch = float(np.mean([expert_weight_bytes(spec, u) for u in nU]))
     achieved = bytes_per_launch / (avg_ms / 1e3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "moe_experts_decode (k_decode_gateup + k_decode_down)",
+            "kernel": "moe_experts_decode (k_dec_gateup + k_dec_down), back-to-back over the resident copies",
             "bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(avg_ms * 1e3, 2),
             "distinct_experts_per_call": float(np.mean(nU))}
     cfg = {"workload": name, "tokens_per_call": T, "hidden": spec.H, "experts": spec.E, "top_k": spec.k,
@@ -175,9 +173,8 @@ def prefill_workload(steps: int, warmup: int):
     y_sorted = torch.empty((T * spec.k, spec.H), dtype=torch.float32, device="cuda")
     y_sh = torch.empty((T, spec.H), dtype=torch.float32, device="cuda")
     pws = moe.Workspace()
-    durs = time_calls([lambda: moe.moe_experts_prefill(L, x, offsets, perm, y_sorted=y_sorted, y_shared=y_sh,
-                                                       ws=pws)], 2, max(3, steps))
-    avg_ms = float(np.mean(durs))
+    avg_ms = time_calls([lambda: moe.moe_experts_prefill(L, x, offsets, perm, y_sorted=y_sorted, y_shared=y_sh,
+                                                         ws=pws)], 2, max(3, steps))
     flops = 6.0 * spec.H * spec.I * (T * spec.k) + 6.0 * spec.H * spec.Is * T
     achieved = flops / (avg_ms / 1e3) / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",

@@ -32,6 +32,10 @@
  *     status other than MOE_OK and enqueues nothing. A failed launch returns MOE_ERR_HIP.
  *   - The library has no global mutable state and is reentrant. Two calls that share a workspace
  *     must be ordered on one stream.
+ *   - Workspaces: size them with moe_workspace_size(), 16-byte aligned, any contents. No kernel
+ *     waits on another block of its own grid; every cross-block dependency is a kernel boundary,
+ *     so calls may be captured in a HIP graph. Expert ids read from memory are range-checked
+ *     before they address weights.
  *   - Preconditions that are not checked: router logits are finite (no NaN); ids passed in are in
  *     [0, E) and distinct within a token; buffers hold the documented number of elements.
  *
@@ -172,9 +176,10 @@ moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const float* p, co
                        const int32_t* row_of_pair, const float* y_shared, float* out, void* stream);
 
 /*
- * The whole layer: route, permute, experts, combine. T <= 4 takes the decode path, larger T the
- * prefill path. out [T][H] fp32. logits/ids/p are optional outputs (NULL = kept in the workspace).
- * Workspace: MOE_CALL_LAYER.
+ * The whole layer: route, permute, experts, combine. T <= 4 takes the decode path (three launches:
+ * router GEMV; top-k + gate/up; down with the combine fused), larger T the prefill path (router GEMM,
+ * top-k, permutation, grouped GEMMs, combine). out [T][H] fp32. logits/ids/p are optional outputs
+ * (NULL = kept in the workspace). Workspace: MOE_CALL_LAYER.
  */
 moe_status moe_layer(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x, int32_t T,
                      float* out, float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes,

@@ -206,7 +206,7 @@ def moe_route(layer: DeviceLayer, x, logits=None, ids=None, p=None, ws=None, str
     dev = x.device
     ids = torch.empty((T, d.top_k), dtype=torch.int32, device=dev) if ids is None else ids
     p = torch.empty((T, d.top_k), dtype=torch.float32, device=dev) if p is None else p
-    buf, nb = _ws(d, T, MOE_CALL_ROUTE, ws) if logits is None else (None, 0)
+    buf, nb = _ws(d, T, MOE_CALL_ROUTE, ws)
     _check(lib().moe_route(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(logits), _ptr(ids),
                            _ptr(p), _ptr(buf), nb, _stream(stream)), "moe_route")
     return logits, ids, p

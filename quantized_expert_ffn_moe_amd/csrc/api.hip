@@ -120,11 +120,11 @@ LayerWs carve_layer(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
     r.logits = c.take<float>((size_t)T * d->num_experts);
     r.ids = c.take<int32_t>(P);
     r.p = c.take<float>(P);
-    r.y_rows = c.take<float>(P * d->hidden);
-    r.y_shared = c.take<float>((size_t)T * d->hidden);
     if (T <= 4) {
         r.h = c.take<float>(decode_scratch_floats(shape_view(d), T));
     } else {
+        r.y_rows = c.take<float>(P * d->hidden);
+        r.y_shared = c.take<float>((size_t)T * d->hidden);
         r.offsets = c.take<int32_t>((size_t)d->num_experts + 1);
         r.perm = c.take<int32_t>(P);
         r.inv = c.take<int32_t>(P);
@@ -203,7 +203,10 @@ moe_status moe_route(const moe_layer_desc* d, const moe_layer_weights* w, const 
     if (!logits) MOE_TRY(check_ws(ws, ws_bytes, need));
     float* lg = logits ? logits : carve_route(d, T, ws, nullptr).logits;
     hipStream_t s = (hipStream_t)stream;
-    MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, lg, s));
+    if (T <= 4)
+        MOE_TRY(launch_route_gemv(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, lg, s));
+    else
+        MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, lg, s));
     return launch_topk(lg, T, d->num_experts, d->top_k, ids, p, s);
 }
 
@@ -231,8 +234,9 @@ moe_status moe_experts_decode(const moe_layer_desc* d, const moe_layer_weights* 
     size_t need = 0;
     carve_decode(d, T, nullptr, &need);
     MOE_TRY(check_ws(ws, ws_bytes, need));
-    return launch_decode_experts(view(d, w), x, T, ids, y_pairs, y_shared, carve_decode(d, T, ws, nullptr).h,
-                                 (hipStream_t)stream);
+    const DecodeWs dw = carve_decode(d, T, ws, nullptr);
+    return launch_decode_experts(view(d, w), x, T, nullptr, const_cast<int32_t*>(ids), nullptr, dw.h, nullptr, y_pairs,
+                                 y_shared, (hipStream_t)stream);
 }
 
 moe_status moe_experts_prefill(const moe_layer_desc* d, const moe_layer_weights* w, const uint16_t* x, int32_t T,
@@ -279,13 +283,13 @@ moe_status moe_layer(const moe_layer_desc* d, const moe_layer_weights* w, const 
     float* pr = p ? p : lw.p;
     const LayerView L = view(d, w);
     hipStream_t s = (hipStream_t)stream;
+    if (T <= 4) {
+        MOE_TRY(launch_route_gemv(w->w_router, w->router_bias, x, T, L.H, L.E, lg, s));
+        return launch_decode_experts(L, x, T, lg, id, pr, lw.h, out, nullptr, nullptr, s);
+    }
     const float* ysh = d->shared_inter > 0 ? lw.y_shared : nullptr;
     MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, L.H, L.E, lg, s));
     MOE_TRY(launch_topk(lg, T, L.E, L.k, id, pr, s));
-    if (T <= 4) {
-        MOE_TRY(launch_decode_experts(L, x, T, id, lw.y_rows, lw.y_shared, lw.h, s));
-        return launch_combine(T, L.k, L.H, pr, lw.y_rows, nullptr, ysh, out, s);
-    }
     MOE_TRY(launch_permute(id, T, L.k, L.E, lw.offsets, lw.perm, lw.inv, lw.chunks, s));
     MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, lw.prefill, s));
     return launch_combine(T, L.k, L.H, pr, lw.y_rows, lw.inv, ysh, out, s);

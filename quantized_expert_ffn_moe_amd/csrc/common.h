@@ -100,7 +100,7 @@ __device__ __forceinline__ float block_level(const Block32& b, int i) {
         if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP; \
     } while (0)
 
-inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+__host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Sequential carve-out of a caller workspace with 256-byte alignment.
 struct Carve {
@@ -116,5 +116,82 @@ struct Carve {
     }
     size_t bytes() const { return align_up(off, 256); }
 };
+
+}  // namespace moe
+
+// ------------------------------------------------------------------------------------- DPP wave ops
+// DPP row/bank controls of GFX9: quad_perm, row_half_mirror, row_mirror, row_bcast:15, row_bcast:31.
+namespace moe {
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Sum over the 64 lanes; the result is returned to every lane (via lane 63).
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __uint_as_float(dpp_u32<0xb1>(__float_as_uint(v)));    // quad_perm [1,0,3,2]
+    v += __uint_as_float(dpp_u32<0x4e>(__float_as_uint(v)));    // quad_perm [2,3,0,1]
+    v += __uint_as_float(dpp_u32<0x141>(__float_as_uint(v)));   // row_half_mirror
+    v += __uint_as_float(dpp_u32<0x140>(__float_as_uint(v)));   // row_mirror
+    v += __uint_as_float(dpp_u32<0x142, 0xa>(__float_as_uint(v)));  // row_bcast:15
+    v += __uint_as_float(dpp_u32<0x143, 0xc>(__float_as_uint(v)));  // row_bcast:31
+    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
+}
+
+// Max over the 64 lanes of an unsigned value, returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xb1>(v));
+    v = max(v, dpp_u32<0x4e>(v));
+    v = max(v, dpp_u32<0x141>(v));
+    v = max(v, dpp_u32<0x140>(v));
+    v = max(v, dpp_u32<0x142, 0xa>(v));
+    v = max(v, dpp_u32<0x143, 0xc>(v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Inverse of ordered_key (the -0 that ordered_key folds onto +0 comes back as +0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Top-k of one token by one wave: KPL keys per lane (expert e = lane + 64 i) held in registers,
+// k rounds of a DPP wave max of the order-preserving key, ties resolved to the lowest index with
+// ballots; lane j < k ends with the j-th expert and its softmax weight over the chosen k (the
+// first chosen, i.e. largest, logit is subtracted before exp).
+template <int KPL>
+__device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, int k, int& my_id, float& my_p) {
+    const int lane = threadIdx.x % kWave;
+    uint32_t key[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const int e = lane + kWave * i;
+        key[i] = e < E ? ordered_key(l[e]) : 0u;
+    }
+    int mine = 0;
+    uint32_t mykey = 0u;
+    for (int j = 0; j < k; ++j) {
+        uint32_t lb = key[0];
+#pragma unroll
+        for (int i = 1; i < KPL; ++i) lb = max(lb, key[i]);
+        const uint32_t vmax = wave_max_u32(lb);
+        int sel = 0;
+#pragma unroll
+        for (int i = KPL - 1; i >= 0; --i) {   // the lowest i holding the maximum wins
+            const uint64_t b = __ballot(key[i] == vmax);
+            if (b) sel = kWave * i + __ffsll((unsigned long long)b) - 1;
+        }
+#pragma unroll
+        for (int i = 0; i < KPL; ++i)
+            if (lane + kWave * i == sel) key[i] = 0u;
+        if (lane == j) { mine = sel; mykey = vmax; }
+    }
+    const float v = lane < k ? key_value(mykey) : 0.f;
+    const float vmax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v)));
+    const float ex = lane < k ? expf(v - vmax) : 0.f;
+    const float s = wave_sum(ex);
+    my_id = mine;
+    my_p = ex / s;
+}
 
 }  // namespace moe

@@ -1,226 +1,714 @@
-// Decode-regime experts (1 <= T <= 4 tokens): fused dequantise + GEMV, HBM-bound.
+// Decode regime (1 <= T <= 4 tokens): router + top-k, then the chosen experts' FFNs streamed from HBM.
 //
 // Decode on the pages runs the selected experts' weights on the GPU and prices each token by the
 // expert bytes it reads (648news 07-nano-cuda-moe-qwen38-release, section "asynchronous CPU/GPU
 // compute"; 648news 10-cyber-on-strata-moe-local-inference, section "bitwise validation and speed
-// bottleneck", about 117 MB of weights per token). Here every expert is resident in HBM, so the
-// kernels stream exactly the packed bytes of the distinct chosen experts plus the shared expert.
+// bottleneck", about 117 MB of weights per token). Every expert is resident in HBM here, so the
+// kernels move exactly the packed bytes of the distinct chosen experts plus the shared expert.
 //
-// Phase 1 (gate/up): one wave per (expert slot, row n); lane l owns 32-element blocks l, l+64, ...
-//   g_t = sum G[n][:] x_t, u_t = sum U[n][:] x_t, h[slot][t][n] = silu(g_t) * u_t.
-// Phase 2 (down): a 16-lane group per (expert slot, output row m), y = D[m][:] h[slot][t][:].
-// Tokens that share an expert share one read of its weights (the union of the T*k choices).
+// Three launches per layer. Each kernel costs about 2 us of fixed overhead on this GPU and a
+// device-scope fence (L2 write-back + invalidate) costs several us, so no kernel synchronises with
+// other blocks: every cross-block dependency is a kernel boundary, and work that all blocks need
+// (top-k, the union of chosen experts) is recomputed per block from data already in HBM.
+//   k_route_gemv     router logits, one wave per expert row, all loads issued before use.
+//   k_dec_gateup     per block: top-k of every token from the logits (one wave per token, in
+//                    registers), the union of the chosen experts in LDS, x staged as fp16 pairs
+//                    laid out to match the packed codes; then gate/up rows streamed with every
+//                    load of a wave issued up front: codes become fp16 by OR-ing them into the
+//                    mantissa of 1024.0 and multiply into x with v_dot2_f32_f16 (fp32
+//                    accumulation); the constant 1024 (and the code offset) is removed once per
+//                    block with a precomputed sum over x. Block 0 publishes ids and p.
+//   k_dec_down       output rows m: every chosen expert's down row m times its h (LDS as fp16
+//                    hi/lo pairs, laid out so that lanes reading consecutive 32-blocks hit
+//                    consecutive banks), weighted by the routing probability and summed with the
+//                    shared expert (combine fused), or written per pair for moe_experts_decode.
 #include "kernels.h"
 
 namespace moe {
 
-// Union of the chosen experts of T tokens, built by wave 0 of every block from ids (T*k <= 64).
-struct DecodeRouting {
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// ----------------------------------------------------------------------------------- routing plan
+
+// Union of the chosen experts of T <= 4 tokens (T*k <= 64 pairs), built in LDS by a whole block.
+struct DecodePlan {
     int nU;                  // distinct routed experts
-    int expert[64];          // slot -> expert id (slots in order of first appearance)
-    uint32_t tokmask[64];    // slot -> bitmask of tokens that chose it
-    int pair_of[64][4];      // slot, token -> pair index q (or -1)
+    int expert[64];          // slot -> expert id, slots in order of first appearance
+    uint32_t tokmask[64];    // slot -> bitmask of the tokens that chose it
+    int pair_of[64][4];      // slot, token -> pair q = t*k + j, or -1
+    float pw[64][4];         // slot, token -> routing probability of that pair (0 if none)
 };
 
-__device__ void build_routing(const int32_t* __restrict__ ids, int T, int k, DecodeRouting& r) {
-    const int lane = threadIdx.x;  // wave 0 only
-    const int P = T * k;
-    const int q = lane;
-    const int e = q < P ? ids[q] : -1;
-    int first_q = q;
-    for (int q2 = 0; q2 < 64; ++q2) {
-        const int e2 = __shfl(e, q2, kWave);
-        if (q2 < q && e2 == e && first_q == q) first_q = q2;
+// first: LDS scratch of E ints. ids outside [0, E) are ignored (no memory access with them).
+__device__ void build_plan(const int32_t* __restrict__ ids, const float* __restrict__ p, int T, int k, int E,
+                           DecodePlan& P, int* first) {
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += blockDim.x) first[e] = 64;
+    for (int i = tid; i < 64; i += blockDim.x) {
+        P.tokmask[i] = 0u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) { P.pair_of[i][t] = -1; P.pw[i][t] = 0.f; }
     }
-    const uint64_t firsts = __ballot(q < P && first_q == q);
-    const int slot = __popcll(firsts & ((1ull << first_q) - 1ull));
-    r.tokmask[lane] = 0u;
-    for (int t = 0; t < 4; ++t) r.pair_of[lane][t] = -1;
-    __builtin_amdgcn_wave_barrier();
-    if (q < P) {
-        if (first_q == q) r.expert[slot] = e;
-        atomicOr(&r.tokmask[slot], 1u << (q / k));
-        r.pair_of[slot][q / k] = q;
-    }
-    if (lane == 0) r.nU = __popcll(firsts);
-}
-
-template <int FMT, int T>
-__global__ __launch_bounds__(256) void k_decode_gateup(LayerView L, const uint16_t* __restrict__ x,
-                                                       const int32_t* __restrict__ ids, float* __restrict__ h) {
-    __shared__ DecodeRouting R;
-    if (threadIdx.x < kWave) build_routing(ids, T, L.k, R);
     __syncthreads();
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int P = T * L.k;
-    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-    int slot, n, e;
-    uint32_t mask;
-    const uint8_t *gc, *uc;
-    const uint16_t *gs, *us;
-    const int64_t rb = row_bytes(FMT, L.H);
-    const int nb = L.H / 32;
-    if (r < (int64_t)P * L.I) {
-        slot = (int)(r / L.I);
-        n = (int)(r % L.I);
-        if (slot >= R.nU) return;
-        e = R.expert[slot];
-        mask = R.tokmask[slot];
-        const int64_t row = (int64_t)e * L.I + n;
-        gc = L.g_codes + row * rb; uc = L.u_codes + row * rb;
-        gs = L.g_scales + row * nb; us = L.u_scales + row * nb;
-    } else {
-        n = (int)(r - (int64_t)P * L.I);
-        if (L.Is == 0 || n >= L.Is) return;
-        slot = P;
-        mask = (1u << T) - 1u;
-        gc = L.sg_codes + (int64_t)n * rb; uc = L.su_codes + (int64_t)n * rb;
-        gs = L.sg_scales + (int64_t)n * nb; us = L.su_scales + (int64_t)n * nb;
+    const int npairs = T * k;
+    const int q = tid;
+    int e = -1;
+    bool valid = false;
+    if (tid < 64) {
+        e = q < npairs ? ids[q] : -1;
+        valid = q < npairs && e >= 0 && e < E;
+        if (valid) atomicMin(&first[e], q);
     }
-    float g[T], u[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) g[t] = u[t] = 0.f;
-    for (int b = lane; b < nb; b += kWave) {
-        Block32 bg, bu;
-        load_block<FMT>(gc + (int64_t)b * block_bytes(FMT), bg);
-        load_block<FMT>(uc + (int64_t)b * block_bytes(FMT), bu);
-        const float sg = f16_to_f32(gs[b]), su = f16_to_f32(us[b]);
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)t * L.H + (size_t)b * 32);
-            float dg = 0.f, du = 0.f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint4 xv = xp[c];
-                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int el = c * 8 + 2 * i;
-                    const float x0 = bf16_lo(xw[i]), x1 = bf16_hi(xw[i]);
-                    dg += block_level<FMT>(bg, el) * x0 + block_level<FMT>(bg, el + 1) * x1;
-                    du += block_level<FMT>(bu, el) * x0 + block_level<FMT>(bu, el + 1) * x1;
-                }
-            }
-            g[t] += sg * dg;
-            u[t] += su * du;
+    __syncthreads();
+    if (tid < 64) {
+        const int fq = valid ? first[e] : 63;
+        const uint64_t firsts = __ballot(valid && fq == q);
+        const int slot = __popcll(firsts & ((1ull << fq) - 1ull));
+        if (valid) {
+            if (fq == q) P.expert[slot] = e;
+            atomicOr(&P.tokmask[slot], 1u << (q / k));
+            P.pair_of[slot][q / k] = q;
+            P.pw[slot][q / k] = p ? p[q] : 0.f;
         }
+        if (tid == 0) P.nU = __popcll(firsts);
     }
-    const int Imax = L.Imax();
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const float gs_ = group_sum<kWave>(g[t]);
-        const float us_ = group_sum<kWave>(u[t]);
-        if (lane == 0 && (mask >> t) & 1u) h[((size_t)slot * T + t) * Imax + n] = silu_mul(gs_, us_);
-    }
+    __syncthreads();
 }
 
-template <int FMT, int T>
-__global__ __launch_bounds__(256) void k_decode_down(LayerView L, const int32_t* __restrict__ ids,
-                                                     const float* __restrict__ h, float* __restrict__ y_pairs,
-                                                     float* __restrict__ y_shared) {
-    __shared__ DecodeRouting R;
-    if (threadIdx.x < kWave) build_routing(ids, T, L.k, R);
-    __syncthreads();
-    const int sub = threadIdx.x % 16;
-    const int64_t grp = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
-    const int P = T * L.k;
-    const int64_t slot64 = grp / L.H;
-    const int m = (int)(grp % L.H);
-    const int slot = (int)slot64;
-    const int Imax = L.Imax();
-    int Kin;
-    uint32_t mask;
-    const uint8_t* dc;
-    const uint16_t* ds;
-    bool active = true;
-    if (slot < P) {
-        active = slot < R.nU;
-        const int e = active ? R.expert[slot] : 0;
-        mask = active ? R.tokmask[slot] : 0u;
-        Kin = L.I;
-        const int64_t row = (int64_t)e * L.H + m;
-        dc = L.d_codes + row * row_bytes(FMT, L.I);
-        ds = L.d_scales + row * (L.I / 32);
-    } else {
-        active = slot == P && L.Is > 0;
-        mask = (1u << T) - 1u;
-        Kin = L.Is;
-        dc = L.sd_codes + (int64_t)m * row_bytes(FMT, L.Is);
-        ds = L.sd_scales + (int64_t)m * (L.Is / 32);
-    }
-    // every lane of a 16-lane group takes the same branch; whole groups may idle
+// ----------------------------------------------------------------------------------- K1 router
+
+template <int T>
+__global__ __launch_bounds__(256) void k_route_gemv(const float* __restrict__ w_r, const float* __restrict__ bias,
+                                                    const uint16_t* __restrict__ x, int H, int E,
+                                                    float* __restrict__ logits) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int e = blockIdx.x * 4 + wave;
+    if (e >= E) return;
+    // all of a lane's W_r and x chunks are loaded before any is used (8 in flight per group)
+    const float4* wr = reinterpret_cast<const float4*>(w_r + (size_t)e * H);
     float acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = 0.f;
-    if (active) {
-        const int nb = Kin / 32;
-        for (int b = sub; b < nb; b += 16) {
-            Block32 bd;
-            load_block<FMT>(dc + (int64_t)b * block_bytes(FMT), bd);
-            const float sd = f16_to_f32(ds[b]);
+    const int nch = H / 4;
+    for (int c0 = 0; c0 < nch; c0 += 8 * kWave) {
+        float4 wv[8];
+        uint2 xv[T][8];
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                if (!((mask >> t) & 1u)) continue;
-                const float4* hp = reinterpret_cast<const float4*>(h + ((size_t)slot * T + t) * Imax + (size_t)b * 32);
-                float d = 0.f;
+        for (int i = 0; i < 8; ++i) {
+            const int c = c0 + i * kWave + lane;
+            wv[i] = c < nch ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const float4 hv = hp[c];
-                    d += block_level<FMT>(bd, 4 * c) * hv.x + block_level<FMT>(bd, 4 * c + 1) * hv.y +
-                         block_level<FMT>(bd, 4 * c + 2) * hv.z + block_level<FMT>(bd, 4 * c + 3) * hv.w;
+            for (int t = 0; t < T; ++t)
+                xv[t][i] = c < nch ? reinterpret_cast<const uint2*>(x + (size_t)t * H)[c] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                acc[t] += wv[i].x * bf16_lo(xv[t][i].x) + wv[i].y * bf16_hi(xv[t][i].x) +
+                          wv[i].z * bf16_lo(xv[t][i].y) + wv[i].w * bf16_hi(xv[t][i].y);
+    }
+    const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const float s = wave_sum(acc[t]);
+        if (lane == 0) logits[(size_t)t * E + e] = s + b;
+    }
+}
+
+// ----------------------------------------------------------------------------------- code pairs
+
+// Per format: pairs of codes per dword (NP), dwords per 32-block (ND), and for pair j of a dword the
+// two element indices (e0, e1), the factor f (the code sits f times its level above 1024.0 in each
+// fp16 half) and the matching activation scale xs = 1 / f.
+template <int FMT> struct Fmt;
+template <> struct Fmt<MOE_Q4_B32> {
+    static constexpr int NP = 4, ND = 4;
+    __device__ static int e0(int d, int j) { return 8 * d + j; }
+    __device__ static int e1(int d, int j) { return 8 * d + j + 4; }
+    __device__ static float xs(int j) { return (j & 1) ? 0.0625f : 1.f; }
+};
+template <> struct Fmt<MOE_Q8_B32> {
+    static constexpr int NP = 2, ND = 8;
+    __device__ static int e0(int d, int j) { return 4 * d + j; }
+    __device__ static int e1(int d, int j) { return 4 * d + j + 2; }
+    __device__ static float xs(int) { return 1.f; }
+};
+template <> struct Fmt<MOE_Q2_B32> {
+    static constexpr int NP = 8, ND = 2;
+    __device__ static int e0(int d, int j) { return 16 * d + j; }
+    __device__ static int e1(int d, int j) { return 16 * d + j + 8; }
+    // f = 2, 4, 16, 64, 256 for j = 0..4 and 2, 8, 32 for j = 5..7
+    __device__ static float xs(int j) {
+        return j == 0 ? 0.5f : j == 1 ? 0.25f : j == 2 ? 0.0625f : j == 3 ? 0.015625f : j == 4 ? 0.00390625f
+             : j == 5 ? 0.5f : j == 6 ? 0.125f : 0.03125f;
+    }
+};
+
+constexpr uint32_t kMagic = 0x64006400u;  // (1024.0, 1024.0) as fp16 pair
+
+// Subtract the same constant K from both fp16 halves; exact when K and the results are integers
+// below 2048 (all values here are).
+template <int K>
+__device__ __forceinline__ uint32_t sub_k(uint32_t pr) {
+    half2_t v = __builtin_bit_cast(half2_t, pr);
+    v -= half2_t{(_Float16)(float)K, (_Float16)(float)K};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// The 16 fp16 pairs of one 32-element block, each half = f * level exactly: the stored code (offset
+// to be unsigned) is OR-ed into the mantissa of 1024.0 at f times its unit, then 1024 + f * offset
+// is subtracted (Q4: offset 8, Q8: offset 128, Q2: offset 1.5, the level being c - 1.5).
+template <int FMT>
+__device__ __forceinline__ void code_pairs(const uint32_t* w, uint32_t (&pr)[16]) {
+    if constexpr (FMT == MOE_Q4_B32) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t u = w[d] ^ 0x88888888u;
+            const uint32_t v = u >> 8;
+            pr[4 * d + 0] = sub_k<1032>((u & 0x000F000Fu) | kMagic);
+            pr[4 * d + 1] = sub_k<1152>((u & 0x00F000F0u) | kMagic);
+            pr[4 * d + 2] = sub_k<1032>((v & 0x000F000Fu) | kMagic);
+            pr[4 * d + 3] = sub_k<1152>((v & 0x00F000F0u) | kMagic);
+        }
+    } else if constexpr (FMT == MOE_Q8_B32) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+            const uint32_t u = w[d] ^ 0x80808080u;
+            pr[2 * d + 0] = sub_k<1152>((u & 0x00FF00FFu) | kMagic);
+            pr[2 * d + 1] = sub_k<1152>(((u >> 8) & 0x00FF00FFu) | kMagic);
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const uint32_t u = w[d];
+            const uint32_t v = u >> 9;   // elements 5..7 (and 13..15) at bits 1, 3, 5 (17, 19, 21)
+            pr[8 * d + 0] = sub_k<1027>(((u << 1) & 0x00060006u) | kMagic);
+            pr[8 * d + 1] = sub_k<1030>((u & 0x000C000Cu) | kMagic);
+            pr[8 * d + 2] = sub_k<1048>((u & 0x00300030u) | kMagic);
+            pr[8 * d + 3] = sub_k<1120>((u & 0x00C000C0u) | kMagic);
+            pr[8 * d + 4] = sub_k<1408>((u & 0x03000300u) | kMagic);
+            pr[8 * d + 5] = sub_k<1027>((v & 0x00060006u) | kMagic);
+            pr[8 * d + 6] = sub_k<1036>((v & 0x00180018u) | kMagic);
+            pr[8 * d + 7] = sub_k<1072>((v & 0x00600060u) | kMagic);
+        }
+    }
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_codes(const uint8_t* p, uint32_t (&w)[8]) {
+    if constexpr (FMT == MOE_Q8_B32) {
+        const uint4 a = reinterpret_cast<const uint4*>(p)[0], b = reinterpret_cast<const uint4*>(p)[1];
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    } else if constexpr (FMT == MOE_Q4_B32) {
+        const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    } else {
+        const uint2 a = reinterpret_cast<const uint2*>(p)[0];
+        w[0] = a.x; w[1] = a.y;
+    }
+}
+
+// ----------------------------------------------------------------------------------- staging
+
+// 32 activations (fp32, natural order) -> fp16 pairs in code-pair order, scaled by the pair's xs:
+// NH = 1 keeps one fp16 per value, NH = 2 also a second fp16 with the rounding residual (value =
+// hi + lo to about 22 bits). Stored as NH * 4 uint4 at dst[c * stride].
+template <int FMT, int NH>
+__device__ __forceinline__ void stage_pairs(const float (&v)[32], uint4* dst, size_t stride) {
+    using F = Fmt<FMT>;
+    uint32_t hi[16], lo[16];
+#pragma unroll
+    for (int d = 0; d < F::ND; ++d)
+#pragma unroll
+        for (int j = 0; j < F::NP; ++j) {
+            const float sc = F::xs(j);
+            const float a = v[F::e0(d, j)] * sc, b = v[F::e1(d, j)] * sc;
+            const _Float16 ah = (_Float16)a, bh = (_Float16)b;
+            half2_t ph = {ah, bh};
+            hi[d * F::NP + j] = __builtin_bit_cast(uint32_t, ph);
+            if constexpr (NH == 2) {
+                half2_t pl = {(_Float16)(a - (float)ah), (_Float16)(b - (float)bh)};
+                lo[d * F::NP + j] = __builtin_bit_cast(uint32_t, pl);
+            }
+        }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dst[c * stride] = make_uint4(hi[4 * c], hi[4 * c + 1], hi[4 * c + 2], hi[4 * c + 3]);
+    if constexpr (NH == 2) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            dst[(4 + c) * stride] = make_uint4(lo[4 * c], lo[4 * c + 1], lo[4 * c + 2], lo[4 * c + 3]);
+    }
+}
+
+__device__ __forceinline__ void bf16x32_to_f32(const uint4 (&raw)[4], float (&v)[32]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t wv[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { v[8 * c + 2 * i] = bf16_lo(wv[i]); v[8 * c + 2 * i + 1] = bf16_hi(wv[i]); }
+    }
+}
+
+// ----------------------------------------------------------------------------------- K2 gate/up
+
+constexpr int kGateUpRows = 2;    // gate/up rows per K2 wave
+constexpr int kDownRows = 2;      // output rows per K3 wave
+constexpr int kDownJ = 4;         // down items per row whose loads a K3 lane issues together
+
+// LDS of k_dec_gateup: plan | first[E] | ids_s[64] | p_s[64] | xq[T][4][nb] uint4
+__host__ __device__ inline size_t lds_head(int E) {
+    return align_up(sizeof(DecodePlan), 16) + align_up((size_t)E * 4, 16) + 2 * 64 * 4;
+}
+static size_t gateup_smem_bytes(int T, int H, int E) { return lds_head(E) + (size_t)T * (H / 32) * 64; }
+
+// Per block: top-k of every token (given logits) or the given ids, the union of the chosen experts,
+// x as fp16 pairs; per wave: R consecutive rows of one expert's gate and up, all loads issued before
+// use, h = silu(g) * u written for each token that chose the expert.
+template <int FMT, int T, bool ROUTE, int KPL>
+__global__ __launch_bounds__(256) void k_dec_gateup(LayerView L, const uint16_t* __restrict__ x,
+                                                    const float* __restrict__ logits, int32_t* __restrict__ ids,
+                                                    float* __restrict__ p, float* __restrict__ h) {
+    constexpr int R = kGateUpRows;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    DecodePlan& P = *reinterpret_cast<DecodePlan*>(smem);
+    int* first = reinterpret_cast<int*>(smem + align_up(sizeof(DecodePlan), 16));
+    int* ids_s = reinterpret_cast<int*>(smem + align_up(sizeof(DecodePlan), 16) + align_up((size_t)L.E * 4, 16));
+    float* p_s = reinterpret_cast<float*>(ids_s + 64);
+    uint4* xq = reinterpret_cast<uint4*>(smem + lds_head(L.E));
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int H = L.H, nb = H / 32;
+    const int Imax = L.Imax();
+    const int npairs = T * L.k;
+
+    // x chunks are loaded first (they do not depend on the routing)
+    constexpr int kMaxStage = 1;   // T * H / 32 <= 256 is staged from registers; the rest in a loop
+    uint4 xraw[kMaxStage][4];
+#pragma unroll
+    for (int s = 0; s < kMaxStage; ++s) {
+        const int tb = threadIdx.x + s * blockDim.x;
+        if (tb < T * nb) {
+            const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(tb / nb) * H + (size_t)(tb % nb) * 32);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xraw[s][c] = xr[c];
+        }
+    }
+    const int32_t* ids_src = ids;
+    if constexpr (ROUTE) {
+        // top-k of token `wave` from the router logits, recomputed by every block
+        if (wave < T) {
+            int id;
+            float pr;
+            topk_wave<KPL>(logits + (size_t)wave * L.E, L.E, L.k, id, pr);
+            if (lane < L.k) {
+                ids_s[wave * L.k + lane] = id;
+                p_s[wave * L.k + lane] = pr;
+                if (blockIdx.x == 0) {
+                    ids[wave * L.k + lane] = id;
+                    p[wave * L.k + lane] = pr;
                 }
-                acc[t] += sd * d;
+            }
+        }
+        __syncthreads();
+        ids_src = ids_s;
+    }
+    build_plan(ids_src, nullptr, T, L.k, L.E, P, first);
+
+#pragma unroll
+    for (int s = 0; s < kMaxStage; ++s) {
+        const int tb = threadIdx.x + s * blockDim.x;
+        if (tb < T * nb) {
+            float v[32];
+            bf16x32_to_f32(xraw[s], v);
+            stage_pairs<FMT, 1>(v, xq + (size_t)(tb / nb) * 4 * nb + tb % nb, nb);
+        }
+    }
+    for (int tb = threadIdx.x + kMaxStage * blockDim.x; tb < T * nb; tb += blockDim.x) {
+        uint4 raw[4];
+        const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(tb / nb) * H + (size_t)(tb % nb) * 32);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) raw[c] = xr[c];
+        float v[32];
+        bf16x32_to_f32(raw, v);
+        stage_pairs<FMT, 1>(v, xq + (size_t)(tb / nb) * 4 * nb + tb % nb, nb);
+    }
+    __syncthreads();
+
+    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t r0 = gw * R;
+    int slot = -1, n0 = 0;
+    const uint8_t *gc = nullptr, *uc = nullptr;
+    const uint16_t *gs = nullptr, *us = nullptr;
+    const int64_t rb = row_bytes(FMT, H);
+    if (r0 < (int64_t)npairs * L.I) {
+        const int sl = (int)(r0 / L.I);
+        n0 = (int)(r0 % L.I);
+        if (sl < P.nU) {
+            slot = sl;
+            const int64_t row = (int64_t)P.expert[slot] * L.I + n0;
+            gc = L.g_codes + row * rb; uc = L.u_codes + row * rb;
+            gs = L.g_scales + row * nb; us = L.u_scales + row * nb;
+        }
+    } else {
+        n0 = (int)(r0 - (int64_t)npairs * L.I);
+        if (L.Is > 0 && n0 < L.Is) {
+            slot = 64;  // shared
+            gc = L.sg_codes + (int64_t)n0 * rb; uc = L.su_codes + (int64_t)n0 * rb;
+            gs = L.sg_scales + (int64_t)n0 * nb; us = L.su_scales + (int64_t)n0 * nb;
+        }
+    }
+    if (slot < 0) return;   // uniform per wave
+
+    const uint32_t mask = slot < 64 ? P.tokmask[slot] : (1u << T) - 1u;
+    float g[R][T], u[R][T];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int t = 0; t < T; ++t) g[i][t] = u[i][t] = 0.f;
+    for (int b = lane; b < nb; b += kWave) {
+        uint32_t wg[R][8], wu[R][8];
+        uint16_t sgb[R], sub[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            load_codes<FMT>(gc + i * rb + (int64_t)b * block_bytes(FMT), wg[i]);
+            load_codes<FMT>(uc + i * rb + (int64_t)b * block_bytes(FMT), wu[i]);
+            sgb[i] = gs[i * nb + b];
+            sub[i] = us[i * nb + b];
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            uint32_t xr[16];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint4 v = xq[((size_t)t * 4 + c) * nb + b];
+                xr[4 * c] = v.x; xr[4 * c + 1] = v.y; xr[4 * c + 2] = v.z; xr[4 * c + 3] = v.w;
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                uint32_t pg[16], pu[16];
+                code_pairs<FMT>(wg[i], pg);
+                code_pairs<FMT>(wu[i], pu);
+                float dg = 0.f, du = 0.f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) { dg = dot2(pg[j], xr[j], dg); du = dot2(pu[j], xr[j], du); }
+                g[i][t] += f16_to_f32(sgb[i]) * dg;
+                u[i][t] += f16_to_f32(sub[i]) * du;
             }
         }
     }
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const float v = group_sum<16>(acc[t]);
-        if (active && sub == 0 && ((mask >> t) & 1u)) {
-            if (slot < P) {
-                const int q = R.pair_of[slot][t];
-                y_pairs[(size_t)q * L.H + m] = v;
-            } else {
-                y_shared[(size_t)t * L.H + m] = v;
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const float gs_ = wave_sum(g[i][t]);
+            const float us_ = wave_sum(u[i][t]);
+            if (lane == 0 && ((mask >> t) & 1u)) {
+                const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
+                h[(size_t)row * Imax + n0 + i] = silu_mul(gs_, us_);
+            }
+        }
+}
+
+// ----------------------------------------------------------------------------------- K3 down
+
+// LDS of k_dec_down: plan | first[E] | ids/p [64] | hq[rows][8][nbm] uint4 (fp16 hi/lo pairs;
+// lanes reading consecutive 32-blocks hit consecutive banks) | partials [4][RPW][T][items]
+static size_t down_smem_bytes(int T, int k, int E, int Imax, int items_max, bool combine) {
+    size_t b = lds_head(E) + (size_t)(T * k + T) * (Imax / 32) * 128;
+    if (!combine) b += (size_t)4 * kDownRows * T * items_max * 4;
+    return b;
+}
+
+// Each wave owns RPW output rows m; lane items are (slot, 32-block) pairs of those rows; a lane
+// issues the loads of up to MAXJ items of every row before using any of them. h is fetched while
+// the plan is built and kept in LDS as fp16 hi + lo pairs (about 22 bits), so the dot products run
+// on v_dot2_f32_f16 with fp32 accumulation.
+template <int FMT, int T, bool COMBINE>
+__global__ __launch_bounds__(256) void k_dec_down(LayerView L, const int32_t* __restrict__ ids,
+                                                  const float* __restrict__ p, const float* __restrict__ h,
+                                                  float* __restrict__ out, float* __restrict__ y_pairs,
+                                                  float* __restrict__ y_shared, int items_max) {
+    constexpr int RPW = kDownRows, MAXJ = kDownJ;
+    constexpr int kPre = 1;   // (row, block) items of h per thread loaded before the plan is built
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    DecodePlan& P = *reinterpret_cast<DecodePlan*>(smem);
+    int* first = reinterpret_cast<int*>(smem + align_up(sizeof(DecodePlan), 16));
+    uint4* hq = reinterpret_cast<uint4*>(smem + lds_head(L.E));
+    const int Imax = L.Imax();
+    const int nbm = Imax / 32;
+    const int npairs = T * L.k;
+    const int nrows_h = npairs + (L.Is > 0 ? T : 0);
+    float* part = reinterpret_cast<float*>(hq + (size_t)(npairs + T) * 8 * nbm);
+
+    float4 hpre[kPre][8];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) {
+        const int rbk = threadIdx.x + i * blockDim.x;
+        if (rbk < nrows_h * nbm) {
+            const float4* hp = reinterpret_cast<const float4*>(h + (size_t)(rbk / nbm) * Imax + (size_t)(rbk % nbm) * 32);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) hpre[i][c] = hp[c];
+        }
+    }
+    build_plan(ids, COMBINE ? p : nullptr, T, L.k, L.E, P, first);
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int H = L.H;
+    const int nbI = L.I / 32, nbS = L.Is / 32;
+    const int nU = P.nU;
+    const int items = nU * nbI + nbS;
+    const int nit = (items + kWave - 1) / kWave;
+    const int64_t rbI = row_bytes(FMT, L.I), rbS = row_bytes(FMT, L.Is);
+    const int m0 = (blockIdx.x * 4 + wave) * RPW;
+    float* mypart = part + (size_t)wave * RPW * T * items_max;
+
+    float acc[RPW][T];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
+
+    for (int j0 = 0; j0 < nit; j0 += MAXJ) {
+        uint32_t w[RPW][MAXJ][8];
+        uint16_t sdb[RPW][MAXJ];
+        int slot_[MAXJ], b_[MAXJ];
+        bool ok[RPW][MAXJ];
+#pragma unroll
+        for (int jj = 0; jj < MAXJ; ++jj) {
+            const int it = lane + kWave * (j0 + jj);
+            const bool iv = it < items;
+            int slot = 64, b = 0;
+            if (iv) {
+                if (it < nU * nbI) { slot = it / nbI; b = it - slot * nbI; }
+                else b = it - nU * nbI;
+            }
+            slot_[jj] = slot;
+            b_[jj] = b;
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const int m = m0 + r;
+                ok[r][jj] = iv && m < H;
+                sdb[r][jj] = 0;
+                if (ok[r][jj]) {
+                    const uint8_t* dc;
+                    if (slot < 64) {
+                        const int64_t row = (int64_t)P.expert[slot] * H + m;
+                        dc = L.d_codes + row * rbI + (int64_t)b * block_bytes(FMT);
+                        sdb[r][jj] = L.d_scales[row * nbI + b];
+                    } else {
+                        dc = L.sd_codes + (int64_t)m * rbS + (int64_t)b * block_bytes(FMT);
+                        sdb[r][jj] = L.sd_scales[(int64_t)m * nbS + b];
+                    }
+                    load_codes<FMT>(dc, w[r][jj]);
+                }
+            }
+        }
+        if (j0 == 0) {
+            // h into LDS as fp16 hi/lo pairs in code-pair order
+#pragma unroll
+            for (int i = 0; i < kPre; ++i) {
+                const int rbk = threadIdx.x + i * blockDim.x;
+                if (rbk < nrows_h * nbm) {
+                    float v[32];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        v[4 * c] = hpre[i][c].x; v[4 * c + 1] = hpre[i][c].y;
+                        v[4 * c + 2] = hpre[i][c].z; v[4 * c + 3] = hpre[i][c].w;
+                    }
+                    stage_pairs<FMT, 2>(v, hq + (size_t)(rbk / nbm) * 8 * nbm + rbk % nbm, nbm);
+                }
+            }
+            for (int rbk = threadIdx.x + kPre * blockDim.x; rbk < nrows_h * nbm; rbk += blockDim.x) {
+                const float4* hp = reinterpret_cast<const float4*>(h + (size_t)(rbk / nbm) * Imax + (size_t)(rbk % nbm) * 32);
+                float v[32];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const float4 q = hp[c];
+                    v[4 * c] = q.x; v[4 * c + 1] = q.y; v[4 * c + 2] = q.z; v[4 * c + 3] = q.w;
+                }
+                stage_pairs<FMT, 2>(v, hq + (size_t)(rbk / nbm) * 8 * nbm + rbk % nbm, nbm);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int jj = 0; jj < MAXJ; ++jj) {
+            const int slot = slot_[jj], b = b_[jj];
+            const int it = lane + kWave * (j0 + jj);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                if (!ok[r][jj]) continue;
+                uint32_t pd[16];
+                code_pairs<FMT>(w[r][jj], pd);
+                const float sd = f16_to_f32(sdb[r][jj]);
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
+                    float d = 0.f;
+                    if (row >= 0) {
+                        const uint4* hp = hq + (size_t)row * 8 * nbm + b;
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) {
+                            const uint4 hv = hp[(size_t)c * nbm];
+                            const int j = 4 * (c & 3);
+                            d = dot2(pd[j], hv.x, d);
+                            d = dot2(pd[j + 1], hv.y, d);
+                            d = dot2(pd[j + 2], hv.z, d);
+                            d = dot2(pd[j + 3], hv.w, d);
+                        }
+                    }
+                    if constexpr (COMBINE) {
+                        const float wgt = slot < 64 ? P.pw[slot][t] : 1.f;
+                        acc[r][t] += wgt * sd * d;
+                    } else {
+                        mypart[((size_t)r * T + t) * items_max + it] = sd * d;
+                    }
+                }
+            }
+        }
+    }
+
+    if constexpr (COMBINE) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const float sm = wave_sum(acc[r][t]);
+                if (lane == 0 && m0 + r < H) out[(size_t)t * H + m0 + r] = sm;
+            }
+    } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane -> (row, slot, token): the slot's block partials summed in order
+        for (int st = lane; st < RPW * (nU + 1) * T; st += kWave) {
+            const int r = st / ((nU + 1) * T), rem = st % ((nU + 1) * T);
+            const int slot = rem / T, t = rem % T;
+            const int m = m0 + r;
+            if (m >= H) continue;
+            const float* pr = mypart + ((size_t)r * T + t) * items_max;
+            if (slot < nU) {
+                const int q = P.pair_of[slot][t];
+                if (q < 0) continue;
+                float sum = 0.f;
+                for (int b = 0; b < nbI; ++b) sum += pr[slot * nbI + b];
+                y_pairs[(size_t)q * H + m] = sum;
+            } else if (nbS > 0) {
+                float sum = 0.f;
+                for (int b = 0; b < nbS; ++b) sum += pr[nU * nbI + b];
+                y_shared[(size_t)t * H + m] = sum;
             }
         }
     }
 }
 
-size_t decode_scratch_floats(const LayerView& L, int T) { return (size_t)(T * L.k + 1) * T * L.Imax(); }
+// ----------------------------------------------------------------------------------- launchers
+
+static int kpl_for(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16; }
+
+moe_status launch_route_gemv(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
+                             float* logits, hipStream_t s) {
+    const dim3 grid((E + 3) / 4), block(256);
+    switch (T) {
+        case 1: hipLaunchKernelGGL(k_route_gemv<1>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 2: hipLaunchKernelGGL(k_route_gemv<2>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 3: hipLaunchKernelGGL(k_route_gemv<3>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 4: hipLaunchKernelGGL(k_route_gemv<4>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        default: return MOE_ERR_UNSUPPORTED;
+    }
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+// h rows: T*k pairs then T shared tokens, Imax floats each
+size_t decode_scratch_floats(const LayerView& L, int T) { return (size_t)(T * L.k + T) * L.Imax(); }
+
+static int down_items_max(const LayerView& L, int T) {
+    const int slots = min(T * L.k, L.E);
+    return slots * (L.I / 32) + L.Is / 32;
+}
+
+size_t decode_smem_bytes(const LayerView& L, int T, bool combine) {
+    const size_t a = gateup_smem_bytes(T, L.H, L.E);
+    const size_t b = down_smem_bytes(T, L.k, L.E, L.Imax(), down_items_max(L, T), combine);
+    return a > b ? a : b;
+}
+
+// Kernels asking for more than 64 KB of dynamic LDS must say so (gfx950 has 160 KB per CU).
+template <typename K>
+static bool allow_smem(K kernel, size_t bytes) {
+    if (bytes > 160 * 1024) return false;
+    if (bytes <= 65536) return true;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes) == hipSuccess;
+}
+
+template <int FMT, int T, bool ROUTE, int KPL>
+static moe_status launch_gateup(const LayerView& L, const uint16_t* x, const float* logits, int32_t* ids, float* p,
+                                float* h, hipStream_t s) {
+    const int64_t rows1 = (int64_t)T * L.k * L.I + L.Is;
+    const int64_t waves1 = (rows1 + kGateUpRows - 1) / kGateUpRows;
+    const size_t sm = gateup_smem_bytes(T, L.H, L.E);
+    auto kern = k_dec_gateup<FMT, T, ROUTE, KPL>;
+    if (!allow_smem(kern, sm)) return MOE_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((waves1 + 3) / 4)), dim3(256), sm, s, L, x, logits, ids, p, h);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
 
 template <int FMT, int T>
-static moe_status launch_decode_t(const LayerView& L, const uint16_t* x, const int32_t* ids, float* y_pairs,
-                                  float* y_shared, float* h, hipStream_t s) {
-    const int64_t P = (int64_t)T * L.k;
-    const int64_t rows1 = P * L.I + L.Is;
-    hipLaunchKernelGGL((k_decode_gateup<FMT, T>), dim3((unsigned)((rows1 + 3) / 4)), dim3(256), 0, s, L, x, ids, h);
-    MOE_LAUNCH_CHECK();
-    const int64_t rows2 = (P + (L.Is > 0 ? 1 : 0)) * L.H;
-    hipLaunchKernelGGL((k_decode_down<FMT, T>), dim3((unsigned)((rows2 + 15) / 16)), dim3(256), 0, s, L, ids, h,
-                       y_pairs, y_shared);
+static moe_status launch_experts_t(const LayerView& L, const uint16_t* x, const float* logits, int32_t* ids, float* p,
+                                   float* h, float* out, float* y_pairs, float* y_shared, hipStream_t s) {
+    moe_status st;
+    if (logits) {
+        switch (kpl_for(L.E)) {
+            case 1: st = launch_gateup<FMT, T, true, 1>(L, x, logits, ids, p, h, s); break;
+            case 2: st = launch_gateup<FMT, T, true, 2>(L, x, logits, ids, p, h, s); break;
+            case 4: st = launch_gateup<FMT, T, true, 4>(L, x, logits, ids, p, h, s); break;
+            case 8: st = launch_gateup<FMT, T, true, 8>(L, x, logits, ids, p, h, s); break;
+            default: st = launch_gateup<FMT, T, true, 16>(L, x, logits, ids, p, h, s); break;
+        }
+    } else {
+        st = launch_gateup<FMT, T, false, 1>(L, x, nullptr, ids, nullptr, h, s);
+    }
+    if (st != MOE_OK) return st;
+    const int items_max = down_items_max(L, T);
+    const int blocks = (L.H + 4 * kDownRows - 1) / (4 * kDownRows);
+    const bool combine = out != nullptr;
+    const size_t sm = down_smem_bytes(T, L.k, L.E, L.Imax(), items_max, combine);
+    if (combine) {
+        if (!allow_smem(k_dec_down<FMT, T, true>, sm)) return MOE_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL((k_dec_down<FMT, T, true>), dim3(blocks), dim3(256), sm, s, L, ids, p, h, out, nullptr,
+                           nullptr, items_max);
+    } else {
+        if (!allow_smem(k_dec_down<FMT, T, false>, sm)) return MOE_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL((k_dec_down<FMT, T, false>), dim3(blocks), dim3(256), sm, s, L, ids, nullptr, h, nullptr,
+                           y_pairs, y_shared, items_max);
+    }
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
 
 template <int FMT>
-static moe_status launch_decode_f(const LayerView& L, const uint16_t* x, int T, const int32_t* ids, float* y_pairs,
-                                  float* y_shared, float* h, hipStream_t s) {
+static moe_status launch_experts_f(const LayerView& L, const uint16_t* x, int T, const float* logits, int32_t* ids,
+                                   float* p, float* h, float* out, float* y_pairs, float* y_shared, hipStream_t s) {
     switch (T) {
-        case 1: return launch_decode_t<FMT, 1>(L, x, ids, y_pairs, y_shared, h, s);
-        case 2: return launch_decode_t<FMT, 2>(L, x, ids, y_pairs, y_shared, h, s);
-        case 3: return launch_decode_t<FMT, 3>(L, x, ids, y_pairs, y_shared, h, s);
-        case 4: return launch_decode_t<FMT, 4>(L, x, ids, y_pairs, y_shared, h, s);
+        case 1: return launch_experts_t<FMT, 1>(L, x, logits, ids, p, h, out, y_pairs, y_shared, s);
+        case 2: return launch_experts_t<FMT, 2>(L, x, logits, ids, p, h, out, y_pairs, y_shared, s);
+        case 3: return launch_experts_t<FMT, 3>(L, x, logits, ids, p, h, out, y_pairs, y_shared, s);
+        case 4: return launch_experts_t<FMT, 4>(L, x, logits, ids, p, h, out, y_pairs, y_shared, s);
         default: return MOE_ERR_UNSUPPORTED;
     }
 }
 
-moe_status launch_decode_experts(const LayerView& L, const uint16_t* x, int T, const int32_t* ids, float* y_pairs,
-                                 float* y_shared, float* h, hipStream_t s) {
+moe_status launch_decode_experts(const LayerView& L, const uint16_t* x, int T, const float* logits, int32_t* ids,
+                                 float* p, float* h, float* out, float* y_pairs, float* y_shared, hipStream_t s) {
     switch (L.fmt) {
-        case MOE_Q8_B32: return launch_decode_f<MOE_Q8_B32>(L, x, T, ids, y_pairs, y_shared, h, s);
-        case MOE_Q4_B32: return launch_decode_f<MOE_Q4_B32>(L, x, T, ids, y_pairs, y_shared, h, s);
-        case MOE_Q2_B32: return launch_decode_f<MOE_Q2_B32>(L, x, T, ids, y_pairs, y_shared, h, s);
+        case MOE_Q8_B32: return launch_experts_f<MOE_Q8_B32>(L, x, T, logits, ids, p, h, out, y_pairs, y_shared, s);
+        case MOE_Q4_B32: return launch_experts_f<MOE_Q4_B32>(L, x, T, logits, ids, p, h, out, y_pairs, y_shared, s);
+        case MOE_Q2_B32: return launch_experts_f<MOE_Q2_B32>(L, x, T, logits, ids, p, h, out, y_pairs, y_shared, s);
         default: return MOE_ERR_INVALID_ARG;
     }
 }

@@ -17,6 +17,7 @@ struct LayerView {
     __host__ __device__ int Imax() const { return I > Is ? I : Is; }
 };
 
+// router GEMM (any T) and the top-k + softmax kernel (one wave per token)
 moe_status launch_router(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
                          float* logits, hipStream_t s);
 moe_status launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* p, hipStream_t s);
@@ -26,10 +27,16 @@ int perm_chunks(int T);
 moe_status launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* perm, int32_t* inv,
                           int32_t* chunk_scratch, hipStream_t s);
 
-// decode experts: h scratch of (T*k + 1) * T * Imax floats
+// decode (T <= 4): router GEMV; gate/up (given logits, every block runs the top-k and block 0
+// publishes ids/p); down(+combine). h scratch: decode_scratch_floats() floats.
+moe_status launch_route_gemv(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
+                             float* logits, hipStream_t s);
 size_t decode_scratch_floats(const LayerView& L, int T);
-moe_status launch_decode_experts(const LayerView& L, const uint16_t* x, int T, const int32_t* ids, float* y_pairs,
-                                 float* y_shared, float* h_scratch, hipStream_t s);
+size_t decode_smem_bytes(const LayerView& L, int T, bool combine);
+// logits != NULL: route inside (ids/p written); else ids given. out != NULL: combined output [T][H]
+// (p required); else y_pairs [T*k][H] and y_shared [T][H].
+moe_status launch_decode_experts(const LayerView& L, const uint16_t* x, int T, const float* logits, int32_t* ids,
+                                 float* p, float* h, float* out, float* y_pairs, float* y_shared, hipStream_t s);
 
 // prefill experts
 size_t prefill_scratch_bytes(const LayerView& L, int T);

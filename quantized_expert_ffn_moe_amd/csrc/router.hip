@@ -7,34 +7,6 @@
 
 namespace moe {
 
-// ----------------------------------------------------------------------------- decode GEMV
-// One wave per expert row: W_r row streamed with 16-byte loads, x (T <= 4 tokens) re-read from
-// L1/L2, fp32 accumulation, wave reduction.
-template <int T>
-__global__ __launch_bounds__(64) void k_router_gemv(const float* __restrict__ w_r, const float* __restrict__ bias,
-                                                    const uint16_t* __restrict__ x, int H, int E,
-                                                    float* __restrict__ logits) {
-    const int e = blockIdx.x;
-    const int lane = threadIdx.x;
-    const float4* wr = reinterpret_cast<const float4*>(w_r + (size_t)e * H);
-    float acc[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = 0.f;
-    for (int c = lane; c < H / 4; c += kWave) {
-        const float4 wv = wr[c];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const uint2 xv = reinterpret_cast<const uint2*>(x + (size_t)t * H)[c];
-            acc[t] += wv.x * bf16_lo(xv.x) + wv.y * bf16_hi(xv.x) + wv.z * bf16_lo(xv.y) + wv.w * bf16_hi(xv.y);
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const float s = group_sum<kWave>(acc[t]);
-        if (lane == 0) logits[(size_t)t * E + e] = s + (bias ? bias[e] : 0.f);
-    }
-}
-
 // ----------------------------------------------------------------------------- prefill GEMM
 // logits[T][E] = x[T][H] * W_r[E][H]^T + b, fp32 FMA tiles of 64 tokens x 64 experts.
 constexpr int kRgTile = 64, kRgK = 32;
@@ -86,41 +58,19 @@ __global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ w
 }
 
 // ----------------------------------------------------------------------------- top-k + softmax
-// One wave per token. Each lane holds up to 16 logits as 64-bit keys (ordered value, ~index) so
-// that one unsigned max picks the larger value and, on equal values, the lower index. k rounds of
-// a wave-wide max, then the softmax over the chosen k in fp32 with the first (largest) logit
-// subtracted.
+// One wave per token (topk_wave): k rounds of a DPP wave max over order-preserving keys, ties to the
+// lower expert index, then the softmax over the chosen k.
+template <int KPL>
 __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ logits, int T, int E, int k,
                                                       int32_t* __restrict__ ids, float* __restrict__ p) {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int t = blockIdx.x * 4 + wave;
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
     if (t >= T) return;
-    const float* l = logits + (size_t)t * E;
-    uint64_t keys[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int e = lane + kWave * i;
-        keys[i] = e < E ? ((uint64_t)ordered_key(l[e]) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
-    }
-    int mine = 0;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) best = keys[i] > best ? keys[i] : best;
-        best = wave_max_u64(best);
-        const int e = (int)(~(uint32_t)best);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (keys[i] == best) keys[i] = 0ull;
-        if (lane == j) mine = e;
-    }
-    const float v = lane < k ? l[mine] : 0.f;
-    const float vmax = __shfl(v, 0, kWave);
-    const float ex = lane < k ? expf(v - vmax) : 0.f;
-    const float s = group_sum<kWave>(ex);
+    int id;
+    float pr;
+    topk_wave<KPL>(logits + (size_t)t * E, E, k, id, pr);
     if (lane < k) {
-        ids[(size_t)t * k + lane] = mine;
-        p[(size_t)t * k + lane] = ex / s;
+        ids[(size_t)t * k + lane] = id;
+        p[(size_t)t * k + lane] = pr;
     }
 }
 
@@ -128,23 +78,19 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
 
 moe_status launch_router(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
                          float* logits, hipStream_t s) {
-    if (T <= 4) {
-        switch (T) {
-            case 1: hipLaunchKernelGGL(k_router_gemv<1>, dim3(E), dim3(64), 0, s, w_r, bias, x, H, E, logits); break;
-            case 2: hipLaunchKernelGGL(k_router_gemv<2>, dim3(E), dim3(64), 0, s, w_r, bias, x, H, E, logits); break;
-            case 3: hipLaunchKernelGGL(k_router_gemv<3>, dim3(E), dim3(64), 0, s, w_r, bias, x, H, E, logits); break;
-            default: hipLaunchKernelGGL(k_router_gemv<4>, dim3(E), dim3(64), 0, s, w_r, bias, x, H, E, logits); break;
-        }
-    } else {
-        dim3 grid((T + kRgTile - 1) / kRgTile, (E + kRgTile - 1) / kRgTile);
-        hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, s, w_r, bias, x, T, H, E, logits);
-    }
+    dim3 grid((T + kRgTile - 1) / kRgTile, (E + kRgTile - 1) / kRgTile);
+    hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, s, w_r, bias, x, T, H, E, logits);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
 
 moe_status launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* p, hipStream_t s) {
-    hipLaunchKernelGGL(k_topk_softmax, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, p);
+    const dim3 grid((T + 3) / 4), block(256);
+    if (E <= 64) hipLaunchKernelGGL(k_topk_softmax<1>, grid, block, 0, s, logits, T, E, k, ids, p);
+    else if (E <= 128) hipLaunchKernelGGL(k_topk_softmax<2>, grid, block, 0, s, logits, T, E, k, ids, p);
+    else if (E <= 256) hipLaunchKernelGGL(k_topk_softmax<4>, grid, block, 0, s, logits, T, E, k, ids, p);
+    else if (E <= 512) hipLaunchKernelGGL(k_topk_softmax<8>, grid, block, 0, s, logits, T, E, k, ids, p);
+    else hipLaunchKernelGGL(k_topk_softmax<16>, grid, block, 0, s, logits, T, E, k, ids, p);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
