@@ -60,9 +60,7 @@
  *
  * Shape limits (MOE_ERR_INVALID_ARG otherwise): T >= 1; 1 <= k <= min(E, 16); E <= 1024;
  * H, I multiples of 32 and Is = 0 or a multiple of 32; H <= 16384; I, Is <= 4096;
- * pointers to codes, scales, x, outputs and workspace 16-byte aligned. The prefill path
- * (moe_experts_prefill, and moe_layer with T > 4) also needs H, I and Is to be multiples of 64
- * (MOE_ERR_UNSUPPORTED otherwise).
+ * pointers to codes, scales, x, outputs and workspace 16-byte aligned.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -137,7 +135,8 @@ moe_status moe_route(const moe_layer_desc* desc, const moe_layer_weights* w, con
  *   offsets[e] = number of pairs with expert < e (offsets[E] = T*k);
  *   pos(q) = offsets[ids[q]] + number of earlier pairs q' < q with the same expert;
  *   perm[pos(q)] = q, inv[q] = pos(q).
- * Workspace: MOE_CALL_PERMUTE.
+ * A pair whose id lies outside [0, E) is dropped (no slot, inv[q] = -1, offsets[E] counts the
+ * kept pairs; perm entries past offsets[E] are left unwritten). Workspace: MOE_CALL_PERMUTE.
  */
 moe_status moe_permute(const moe_layer_desc* desc, const int32_t* ids, int32_t T, int32_t* offsets, int32_t* perm,
                        int32_t* inv, void* ws, size_t ws_bytes, void* stream);
@@ -156,7 +155,8 @@ moe_status moe_experts_decode(const moe_layer_desc* desc, const moe_layer_weight
 /*
  * Expert FFNs for a prefill chunk (any T >= 1): a grouped GEMM over expert-sorted row tiles
  * (rows in perm order, groups from offsets, as moe_permute returns them), with the shared
- * expert as one more group of all T tokens.
+ * expert as one more group of all T tokens. Offsets are clamped to [0, T*k] and perm entries
+ * outside [0, T*k) read token 0, so inconsistent inputs give wrong rows but no stray access.
  *   y_sorted[i] = expert FFN of pair perm[i] (sorted order), y_shared[t] as above.
  * Operands are fp16 on the matrix cores (x converted from bf16, weights dequantised once to fp16,
  * the SwiGLU activation h kept in fp16) with fp32 accumulation and fp32 outputs.
@@ -169,8 +169,9 @@ moe_status moe_experts_prefill(const moe_layer_desc* desc, const moe_layer_weigh
 /*
  * Weighted combine, atomic-free and deterministic:
  *   out[t] = sum_{j=0}^{k-1} p[t][j] * y_rows[r(t,j)] + y_shared[t]     (slot order, then shared)
- * with r(t,j) = row_of_pair[t*k+j] (e.g. inv from moe_permute) or t*k+j when row_of_pair is NULL.
- * y_shared may be NULL (no shared term). No workspace.
+ * with r(t,j) = row_of_pair[t*k+j] (e.g. inv from moe_permute) or t*k+j when row_of_pair is NULL;
+ * a row outside [0, T*k) (a dropped pair) contributes nothing. y_shared may be NULL (no shared
+ * term). No workspace.
  */
 moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const float* p, const float* y_rows,
                        const int32_t* row_of_pair, const float* y_shared, float* out, void* stream);

@@ -25,10 +25,6 @@ moe_status check_desc(const moe_layer_desc* d) {
 
 moe_status check_T(int32_t T) { return (T >= 1 && T <= kMaxT) ? MOE_OK : MOE_ERR_INVALID_ARG; }
 
-bool prefill_shape_ok(const moe_layer_desc* d) {
-    return d->hidden % 64 == 0 && d->inter % 64 == 0 && d->shared_inter % 64 == 0;
-}
-
 bool qmat_ok(const moe_qmat& q) { return q.codes && q.scales && aligned16(q.codes) && ((uintptr_t)q.scales & 1u) == 0; }
 
 moe_status check_expert_weights(const moe_layer_desc* d, const moe_layer_weights* w) {
@@ -177,12 +173,10 @@ moe_status moe_workspace_size(const moe_layer_desc* d, int32_t T, moe_call call,
             carve_decode(d, T, nullptr, &b);
             break;
         case MOE_CALL_EXPERTS_PREFILL:
-            if (!prefill_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
             carve_prefill_ws(d, T, nullptr, &b);
             break;
         case MOE_CALL_COMBINE: b = 0; break;
         case MOE_CALL_LAYER:
-            if (T > 4 && !prefill_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
             carve_layer(d, T, nullptr, &b);
             break;
         default: return MOE_ERR_INVALID_ARG;
@@ -244,7 +238,6 @@ moe_status moe_experts_prefill(const moe_layer_desc* d, const moe_layer_weights*
                                size_t ws_bytes, void* stream) {
     MOE_TRY(check_desc(d));
     MOE_TRY(check_T(T));
-    if (!prefill_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
     MOE_TRY(check_expert_weights(d, w));
     if (!x || !aligned16(x) || !offsets || !perm || !y_sorted) return MOE_ERR_INVALID_ARG;
     if (d->shared_inter > 0 && !y_shared) return MOE_ERR_INVALID_ARG;
@@ -268,7 +261,6 @@ moe_status moe_layer(const moe_layer_desc* d, const moe_layer_weights* w, const 
                      float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes, void* stream) {
     MOE_TRY(check_desc(d));
     MOE_TRY(check_T(T));
-    if (T > 4 && !prefill_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
     MOE_TRY(check_router_weights(w));
     MOE_TRY(check_expert_weights(d, w));
     if (!x || !aligned16(x) || !out || !aligned16(out)) return MOE_ERR_INVALID_ARG;

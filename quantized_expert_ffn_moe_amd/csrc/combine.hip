@@ -23,6 +23,7 @@ __global__ __launch_bounds__(256) void k_combine(int T, int k, int H, const floa
     if (c >= H / 4) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
+        if ((unsigned)rows[j] >= (unsigned)(T * k)) continue;  // dropped pair
         const float4 v = reinterpret_cast<const float4*>(y_rows + (size_t)rows[j] * H)[c];
         const float pj = ps[j];
         acc.x += pj * v.x; acc.y += pj * v.y; acc.z += pj * v.z; acc.w += pj * v.w;

@@ -3,11 +3,15 @@
 // Prompt chunks run as grouped expert GEMMs (648news 07-nano-cuda-moe-qwen38-release, section
 // "speed comparison and accuracy check", 8K-token chunks), which need the pairs of each expert
 // contiguous. Deterministic and atomic-free on the order:
-//   1. per chunk of 64 tokens, per-expert counts (LDS histogram; counts do not depend on order);
-//   2. one block scans counts expert-major, chunk-minor -> offsets[e] and each chunk's base[c][e];
+//   1. per chunk of 64 tokens, per-expert counts (LDS histogram; counts do not depend on order),
+//      stored expert-major: counts[e][c];
+//   2. one block turns counts[e][c] into its exclusive prefix sum in that (expert, chunk) order,
+//      which is at once offsets[e] (the value at c = 0) and each chunk's first slot base[e][c];
 //   3. per chunk, a pair's rank inside its expert is the number of earlier tokens of the chunk
 //      that chose the same expert: a 64-bit LDS mask of tokens per expert, popcount below the lane.
 // Token t's k choices are distinct (top-k output), so each token adds at most one pair per expert.
+// A pair whose id lies outside [0, E) is dropped: no slot, inv = -1, and offsets[E] counts only
+// the kept pairs.
 #include "kernels.h"
 
 namespace moe {
@@ -24,38 +28,76 @@ __global__ __launch_bounds__(64) void k_perm_hist(const int32_t* __restrict__ id
     __syncthreads();
     const int t = c * kChunk + lane;
     if (t < T)
-        for (int j = 0; j < k; ++j) atomicAdd(&cnt[ids[(size_t)t * k + j]], 1);
+        for (int j = 0; j < k; ++j) {
+            const int e = ids[(size_t)t * k + j];
+            if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+        }
     __syncthreads();
-    for (int e = lane; e < E; e += kWave) counts[(size_t)c * E + e] = cnt[e];
+    const int nc = gridDim.x;
+    for (int e = lane; e < E; e += kWave) counts[(size_t)e * nc + c] = cnt[e];
 }
 
-// One block of 1024 threads, one thread per expert.
-__global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts, int nchunks, int E, int total,
+// One block of 1024 threads: thread i owns the contiguous segment [i * per, (i + 1) * per) of the
+// n = E * nchunks counts (per a multiple of 16), sums it, a block scan of the 1024 sums gives each
+// segment's start, and a second pass writes the exclusive prefix in place. Both passes move 16
+// counts per step with four independent 16-byte accesses.
+__global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts, int nchunks, int E,
                                                     int32_t* __restrict__ offsets) {
     __shared__ int32_t part[1024];
-    const int e = threadIdx.x;
-    int tot = 0;
-    if (e < E)
-        for (int c = 0; c < nchunks; ++c) tot += counts[(size_t)c * E + e];
-    part[e] = e < E ? tot : 0;
+    const int tid = threadIdx.x;
+    const int n = E * nchunks;
+    const int per = ((n + 1023) / 1024 + 15) & ~15;
+    const int lo = min(tid * per, n), hi = min(lo + per, n);
+    auto load16 = [&](int i, int (&v)[16]) {
+        if (i + 16 <= hi) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int4 w = reinterpret_cast<const int4*>(counts + i)[q];
+                v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = i + j < hi ? counts[i + j] : 0;
+        }
+    };
+    int sum = 0;
+    for (int i = lo; i < hi; i += 16) {
+        int v[16];
+        load16(i, v);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sum += v[j];
+    }
+    part[tid] = sum;
     __syncthreads();
-    // inclusive Hillis-Steele scan over 1024 entries
     for (int d = 1; d < 1024; d <<= 1) {
-        const int v = e >= d ? part[e - d] : 0;
+        const int v = tid >= d ? part[tid - d] : 0;
         __syncthreads();
-        part[e] += v;
+        part[tid] += v;
         __syncthreads();
     }
-    if (e < E) {
-        int base = part[e] - tot;  // exclusive
-        offsets[e] = base;
-        for (int c = 0; c < nchunks; ++c) {
-            const int v = counts[(size_t)c * E + e];
-            counts[(size_t)c * E + e] = base;
-            base += v;
+    int run = part[tid] - sum;
+    int e = lo / nchunks, c = lo - e * nchunks;
+    for (int i = lo; i < hi; i += 16) {
+        int v[16], o[16];
+        load16(i, v);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            o[j] = run;
+            if (c == 0 && i + j < hi) offsets[e] = run;
+            run += v[j];
+            if (++c == nchunks) { c = 0; ++e; }
+        }
+        if (i + 16 <= hi) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                reinterpret_cast<int4*>(counts + i)[q] = make_int4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (i + j < hi) counts[i + j] = o[j];
         }
     }
-    if (e == 0) offsets[E] = total;
+    if (tid == 1023) offsets[E] = run;   // = total when every id is in range
 }
 
 __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__ ids, int T, int k, int E,
@@ -67,14 +109,21 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
     __syncthreads();
     const int t = c * kChunk + lane;
     if (t < T)
-        for (int j = 0; j < k; ++j) atomicOr(&tokmask[ids[(size_t)t * k + j]], 1ull << lane);
+        for (int j = 0; j < k; ++j) {
+            const int e = ids[(size_t)t * k + j];
+            if ((unsigned)e < (unsigned)E) atomicOr(&tokmask[e], 1ull << lane);
+        }
     __syncthreads();
     if (t < T) {
         const unsigned long long below = (1ull << lane) - 1ull;
         for (int j = 0; j < k; ++j) {
             const int q = t * k + j;
             const int e = ids[q];
-            const int pos = base[(size_t)c * E + e] + __popcll(tokmask[e] & below);
+            if ((unsigned)e >= (unsigned)E) {
+                inv[q] = -1;
+                continue;
+            }
+            const int pos = base[(size_t)e * gridDim.x + c] + __popcll(tokmask[e] & below);
             perm[pos] = q;
             inv[q] = pos;
         }
@@ -86,7 +135,7 @@ moe_status launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
     const int nc = perm_chunks(T);
     hipLaunchKernelGGL(k_perm_hist, dim3(nc), dim3(64), E * sizeof(int32_t), s, ids, T, k, E, scratch);
     MOE_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, scratch, nc, E, T * k, offsets);
+    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, scratch, nc, E, offsets);
     MOE_LAUNCH_CHECK();
     hipLaunchKernelGGL(k_perm_scatter, dim3(nc), dim3(64), E * sizeof(unsigned long long), s, ids, T, k, E,
                        scratch, perm, inv);

@@ -8,53 +8,128 @@
 namespace moe {
 
 // ----------------------------------------------------------------------------- prefill GEMM
-// logits[T][E] = x[T][H] * W_r[E][H]^T + b, fp32 FMA tiles of 64 tokens x 64 experts.
-constexpr int kRgTile = 64, kRgK = 32;
+// logits[T][E] = x[T][H] * W_r[E][H]^T + b on the bf16 matrix cores at fp32 accuracy: x is bf16
+// already, and each fp32 weight is split into three bf16 terms w = w1 + w2 + w3 (w1 = bf16(w),
+// w2 = bf16(w - w1), w3 = bf16(w - w1 - w2); 3 x 8 significant bits hold all 24 of the fp32
+// value). Every product x * wi is exact in fp32, so the three MFMAs per fragment pair give the
+// fp32 dot product up to the order of the fp32 additions.
+//
+// Tiles of 64 tokens x 64 experts, four waves of 32 x 32, K steps of 32 through double-buffered
+// LDS (rows padded to 80 bytes), loads kept two steps ahead in registers. Blocks that share token
+// rows are placed on one XCD so that x is read once into that XCD's L2.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ w_r, const float* __restrict__ bias,
-                                                     const uint16_t* __restrict__ x, int T, int H, int E,
-                                                     float* __restrict__ logits) {
-    __shared__ float xs[kRgK][kRgTile + 4];
-    __shared__ float ws[kRgK][kRgTile + 4];
-    const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * kRgTile, e0 = blockIdx.y * kRgTile;
-    const int ty = tid / 16, tx = tid % 16;
-    float acc[4][4] = {};
-    for (int k0 = 0; k0 < H; k0 += kRgK) {
-        // 64 rows x 32 k of each operand: 8 elements per thread
+constexpr int kRtM = 64, kRtN = 64, kRtK = 32, kRtLds = kRtK + 8, kRtXcds = 8;
+
+struct RouterSlot {
+    u32x4 a;          // 8 bf16 of x
+    floatx4 b0, b1;   // 8 fp32 of W_r
+};
+
+__global__ __launch_bounds__(256, 2) void k_router_mfma(const float* __restrict__ w_r, const float* __restrict__ bias,
+                                                        const uint16_t* __restrict__ x, int T, int H, int E,
+                                                        float* __restrict__ logits) {
+    __shared__ __attribute__((aligned(16))) __bf16 As[2][kRtM * kRtLds];
+    __shared__ __attribute__((aligned(16))) __bf16 Bs[2][3][kRtN * kRtLds];
+    const int mt = (T + kRtM - 1) / kRtM, nt = (E + kRtN - 1) / kRtN;
+    const int total = mt * nt, per_xcd = (total + kRtXcds - 1) / kRtXcds;
+    const int idx = (int)(blockIdx.x / kRtXcds);
+    if (idx >= per_xcd) return;
+    const int w = (int)(blockIdx.x % kRtXcds) * per_xcd + idx;
+    if (w >= total) return;
+    const int t0 = (w / nt) * kRtM, e0 = (w % nt) * kRtN;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wm = wave / 2, wn = wave % 2;
+
+    // loader: thread -> row tid / 4, K chunk 8 * (tid % 4); rows past T or E are clamped (their
+    // outputs are never stored)
+    const int lr = tid >> 2, lc = 8 * (tid & 3);
+    const uint16_t* ap = x + (size_t)min(t0 + lr, T - 1) * H + lc;
+    const float* bp = w_r + (size_t)min(e0 + lr, E - 1) * H + lc;
+    const int nk = H / kRtK;
+    auto gload = [&](RouterSlot& sl, int ks) __attribute__((always_inline)) {
+        ks = min(ks, nk - 1);
+        sl.a = *reinterpret_cast<const u32x4*>(ap + ks * kRtK);
+        sl.b0 = *reinterpret_cast<const floatx4*>(bp + ks * kRtK);
+        sl.b1 = *reinterpret_cast<const floatx4*>(bp + ks * kRtK + 4);
+    };
+    auto lstore = [&](const RouterSlot& sl, int st) __attribute__((always_inline)) {
+        *reinterpret_cast<u32x4*>(&As[st][lr * kRtLds + lc]) = sl.a;
+        const float v[8] = {sl.b0.x, sl.b0.y, sl.b0.z, sl.b0.w, sl.b1.x, sl.b1.y, sl.b1.z, sl.b1.w};
+        bf16x8 p1, p2, p3;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int idx = tid + 256 * i;
-            const int r = idx / kRgK, kk = idx % kRgK;
-            const int t = t0 + r, e = e0 + r;
-            xs[kk][r] = t < T ? bf16_to_f32(x[(size_t)t * H + k0 + kk]) : 0.f;
-            ws[kk][r] = e < E ? w_r[(size_t)e * H + k0 + kk] : 0.f;
+            const __bf16 h1 = (__bf16)v[i];
+            const float r1 = v[i] - (float)h1;
+            const __bf16 h2 = (__bf16)r1;
+            const float r2 = r1 - (float)h2;
+            p1[i] = h1;
+            p2[i] = h2;
+            p3[i] = (__bf16)r2;
         }
+        *reinterpret_cast<bf16x8*>(&Bs[st][0][lr * kRtLds + lc]) = p1;
+        *reinterpret_cast<bf16x8*>(&Bs[st][1][lr * kRtLds + lc]) = p2;
+        *reinterpret_cast<bf16x8*>(&Bs[st][2][lr * kRtLds + lc]) = p3;
+    };
+
+    floatx4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int kofs = 8 * (lane / 16);
+    auto kstep = [&](int ks, const RouterSlot& next_sl, RouterSlot& refill) __attribute__((always_inline)) {
+        const int cur = ks & 1;
+        bf16x8 a[2], b[3][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            a[i] = *reinterpret_cast<const bf16x8*>(&As[cur][(wm * 32 + 16 * i + lane % 16) * kRtLds + kofs]);
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                b[p][j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][p][(wn * 32 + 16 * j + lane % 16) * kRtLds + kofs]);
+        // smallest terms first
+#pragma unroll
+        for (int p = 2; p >= 0; --p)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[p][j], acc[i][j], 0, 0, 0);
+        lstore(next_sl, cur ^ 1);
+        gload(refill, ks + 3);
         __syncthreads();
-#pragma unroll 8
-        for (int kk = 0; kk < kRgK; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx * 4 + j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
-        }
-        __syncthreads();
+    };
+    // two register slots: s0 holds even steps, s1 odd steps
+    RouterSlot s0, s1;
+    gload(s0, 0);
+    gload(s1, 1);
+    lstore(s0, 0);
+    gload(s0, 2);
+    __syncthreads();
+    int ks = 0;
+    for (; ks + 2 <= nk; ks += 2) {
+        kstep(ks, s1, s1);       // writes step ks + 1 (odd), refills s1 with ks + 3
+        kstep(ks + 1, s0, s0);   // writes step ks + 2 (even), refills s0 with ks + 4
     }
+    if (ks < nk) kstep(ks, s1, s1);
+
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + ty * 4 + i;
-        if (t >= T) continue;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = e0 + tx * 4 + j;
-            if (e < E) logits[(size_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.f);
+        for (int j = 0; j < 2; ++j) {
+            const int e = e0 + wn * 32 + 16 * j + lane % 16;
+            if (e >= E) continue;
+            const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = t0 + wm * 32 + 16 * i + 4 * (lane / 16) + r;
+                if (t < T) logits[(size_t)t * E + e] = acc[i][j][r] + b;
+            }
         }
-    }
 }
 
 // ----------------------------------------------------------------------------- top-k + softmax
@@ -78,8 +153,9 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
 
 moe_status launch_router(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
                          float* logits, hipStream_t s) {
-    dim3 grid((T + kRgTile - 1) / kRgTile, (E + kRgTile - 1) / kRgTile);
-    hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, s, w_r, bias, x, T, H, E, logits);
+    const int blocks = ((T + kRtM - 1) / kRtM) * ((E + kRtN - 1) / kRtN);
+    const int grid = ((blocks + kRtXcds - 1) / kRtXcds) * kRtXcds;
+    hipLaunchKernelGGL(k_router_mfma, dim3(grid), dim3(256), 0, s, w_r, bias, x, T, H, E, logits);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -50,9 +50,8 @@ def test_workspace_sizes():
     with pytest.raises(moe.MoeError) as e:
         moe.moe_workspace_size(d, 5, moe.MOE_CALL_EXPERTS_DECODE)
     assert e.value.status == moe.MOE_ERR_UNSUPPORTED
-    with pytest.raises(moe.MoeError) as e:
-        moe.moe_workspace_size(D(H=96), 8, moe.MOE_CALL_EXPERTS_PREFILL)      # 96 % 64 != 0
-    assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+    # the prefill tiles take any H, I, Is that are multiples of 32
+    assert moe.moe_workspace_size(D(H=96, I=32, Is=32), 8, moe.MOE_CALL_EXPERTS_PREFILL) > 0
 
 
 @pytest.mark.parametrize("bad", [dict(k=0), dict(k=17, E=32), dict(k=9, E=8), dict(E=1025), dict(H=100),
@@ -100,10 +99,9 @@ def test_host_validation_rejects_before_launch():
     assert _raw("moe_permute", ref(d.c), fake, 4, None, fake, fake, fake, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
     # combine with misaligned rows
     assert _raw("moe_combine", ref(d.c), 1, fake, fake + 4, None, None, fake, None) == moe.MOE_ERR_INVALID_ARG
-    # prefill with a shape the MFMA path does not tile
-    d96 = D(H=96, I=64, Is=0)
-    assert _raw("moe_experts_prefill", ref(d96.c), ref(w), fake, 8, fake, fake, fake, None, fake, 1 << 40, None) == \
-        moe.MOE_ERR_UNSUPPORTED
+    # prefill with a shared expert but no y_shared
+    assert _raw("moe_experts_prefill", ref(d.c), ref(w), fake, 8, fake, fake, fake, None, fake, 1 << 40, None) == \
+        moe.MOE_ERR_INVALID_ARG
 
 
 def test_binding_refuses_host_tensors():

@@ -152,6 +152,57 @@ def test_golden_examples_on_gpu():
         np.testing.assert_allclose(Y[0], want, rtol=1e-5, atol=1e-6, err_msg=path)
 
 
+# ------------------------------------------------------------------------- router accuracy
+
+@pytest.mark.parametrize("T,E", [(3, 256), (300, 200), (1000, 512)])
+def test_router_fp32_error_bound(T, E):
+    """Router logits (GEMV for T <= 4, bf16x3 MFMA GEMM above) stay within the worst-case fp32
+    summation bound of the oracle's fp64 logits: |err| <= 3H * 2^-24 * sum_h |x_h w_h| + 2^-24 |b|
+    (3H additions: three bf16 terms per weight on the matrix-core path)."""
+    _need_gpu()
+    spec = synth.LayerSpec("rt", T=T, H=2048, E=E, k=8, I=32, Is=0, fmt=synth.Q8, zipf=True, cfg_id=60)
+    d = synth.make_layer(spec)
+    say("router bound T=%d E=%d" % (T, E))
+    O = orc_layer(spec, d)
+    L = dev_layer(spec, d)
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    moe.moe_route(L, dev_x(d["x"]), logits=logits)
+    torch.cuda.synchronize()
+    g = logits.cpu().numpy().astype(np.float64)
+    o = O.router(d["x"])
+    xf = oracle.bf16_to_f64(d["x"])
+    w = d["w_router"].astype(np.float64)
+    b = d["router_bias"].astype(np.float64) if d["router_bias"] is not None else np.zeros(E)
+    bound = 3 * spec.H * 2.0 ** -24 * (np.abs(xf) @ np.abs(w).T) + 2.0 ** -24 * np.abs(b)[None, :]
+    err = np.abs(g - o)
+    assert np.all(err <= bound), "max err/bound %.3f" % float(np.max(err / bound))
+
+
+@pytest.mark.parametrize("T", [3, 300])
+def test_router_exact_on_representable_sums(T):
+    """Inputs whose every partial sum is exact in fp32: x in {-1, 0, 1}, w = m * 2^-17 with
+    m in [2^16, 2^17) (17 significant bits, so all three bf16 terms of the split are needed),
+    H = 96 (|sum| < 2^24 * 2^-17). Any fp32 evaluation order gives the exact value, so the
+    logits must equal the oracle's bit for bit."""
+    _need_gpu()
+    E, H = 200, 96
+    spec = synth.LayerSpec("rx", T=T, H=H, E=E, k=4, I=32, Is=0, fmt=synth.Q8, zipf=False, cfg_id=61)
+    d = synth.make_layer(spec)
+    rng = np.random.default_rng(7)
+    xv = rng.integers(-1, 2, size=(T, H)).astype(np.float32)
+    d["x"] = (xv.view(np.uint32) >> 16).astype(np.uint16)
+    m = rng.integers(1 << 16, 1 << 17, size=(E, H)) * rng.choice([-1, 1], size=(E, H))
+    d["w_router"] = (m * 2.0 ** -17).astype(np.float32)
+    d["router_bias"] = (rng.integers(-64, 64, size=E) * 2.0 ** -6).astype(np.float32)
+    say("router exact T=%d" % T)
+    O = orc_layer(spec, d)
+    L = dev_layer(spec, d)
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    moe.moe_route(L, dev_x(d["x"]), logits=logits)
+    torch.cuda.synchronize()
+    assert np.array_equal(logits.cpu().numpy().astype(np.float64), O.router(d["x"]))
+
+
 # ------------------------------------------------------------------------- prefill
 
 def small_prefill_spec(fmt, T, E=16, k=4, Is=64, H=256, I=128, zipf=True):
@@ -166,6 +217,21 @@ def test_layer_prefill_small(fmt, T):
     spec = small_prefill_spec(fmt, T)
     d = synth.make_layer(spec)
     say("prefill small", synth.FMT_NAMES[fmt], "T=%d" % T)
+    O = orc_layer(spec, d)
+    g_logits, g_ids, g_p, Y = run_layer(spec, d)
+    check_routing(O, d["x"], g_logits, g_ids, g_p)
+    ref = oracle_tokens(O, d["x"], g_logits, range(T))
+    assert_float_match(Y, ref["Y"], "Y")
+
+
+@pytest.mark.parametrize("fmt", [synth.Q8, synth.Q4, synth.Q2])
+def test_layer_prefill_ragged_shapes(fmt):
+    """H, I, Is that leave partial weight-row tiles (H = 800 = 3 * 256 + 32, I = 160, Is = 96)."""
+    _need_gpu()
+    T = 200
+    spec = small_prefill_spec(fmt, T, E=16, k=4, Is=96, H=800, I=160)
+    d = synth.make_layer(spec)
+    say("prefill ragged", synth.FMT_NAMES[fmt], "T=%d H=800 I=160 Is=96" % T)
     O = orc_layer(spec, d)
     g_logits, g_ids, g_p, Y = run_layer(spec, d)
     check_routing(O, d["x"], g_logits, g_ids, g_p)
@@ -281,6 +347,33 @@ def test_permute_edges(T, E, k):
 
 
 # ------------------------------------------------------------------------- special cases
+
+def test_permute_drops_out_of_range_ids():
+    """Ids outside [0, E) are dropped: no slot, inv = -1, offsets count the kept pairs, and the
+    kept pairs keep the stable expert order."""
+    _need_gpu()
+    T, E, k = 300, 64, 4
+    spec = synth.LayerSpec("permbad", T=T, H=64, E=E, k=k, I=64, Is=0, fmt=synth.Q8, zipf=False)
+    rng = np.random.default_rng(11)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    bad = rng.random(ids.shape) < 0.05
+    ids[bad] = rng.choice([-1, E, E + 7, -(1 << 30)], size=int(bad.sum()))
+    class _L:  # moe_permute only needs the descriptor
+        pass
+    lay = _L()
+    lay.desc = moe.LayerDesc.from_spec(spec)
+    offsets, perm, inv = moe.moe_permute(lay, torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    flat = ids.reshape(-1)
+    keep = np.nonzero((flat >= 0) & (flat < E))[0]
+    order = keep[np.argsort(flat[keep], kind="stable")]
+    want_off = np.concatenate([[0], np.cumsum(np.bincount(flat[keep], minlength=E))])
+    assert np.array_equal(offsets.cpu().numpy(), want_off)
+    assert np.array_equal(perm.cpu().numpy()[:len(order)], order)
+    want_inv = np.full(T * k, -1)
+    want_inv[order] = np.arange(len(order))
+    assert np.array_equal(inv.cpu().numpy(), want_inv)
+
 
 def test_ties_and_signed_zero():
     """Equal logits pick the lower expert index; -0 and +0 are one value."""
