@@ -67,6 +67,51 @@ def dev_x(x):
     return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
 
 
+# Kernel sources behind each measured stage: a recorded HBM-traffic figure (profiles/*_traffic.md,
+# from rocprofv3 FETCH_SIZE / WRITE_SIZE runs) is reported only while these files are unchanged.
+STAGE_SOURCES = {
+    "decode": ["csrc/decode.hip", "csrc/common.h", "csrc/kernels.h"],
+    "prefill": ["csrc/prefill.hip", "csrc/common.h", "csrc/kernels.h"],
+}
+
+
+def sources_digest(stage: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in STAGE_SOURCES[stage]:
+        with open(os.path.join(ROOT, "quantized_expert_ffn_moe_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str, stage: str):
+    """HBM bytes per launch recorded in profiles/<workload>_traffic.md, or None when absent or when
+    the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "%s_traffic.md" % workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip().strip("`")
+            if "=" in line and line.split("=")[0].strip() in ("traffic_bytes_per_launch", "sources_sha256"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("sources_sha256") != sources_digest(stage) or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(float(vals["traffic_bytes_per_launch"]))
+
+
+def calibrate_copy(mib: int = 256, reps: int = 3):
+    """Plain device-to-device copies of a known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: %d x %d MiB device-to-device" % (reps, mib))
+
+
 def time_calls(fn_list, warmup: int, reps: int) -> float:
     """Average duration (ms) of one launch from a list of zero-arg launches, played back to back
     reps times between two HIP events on torch's current stream (the stream the library uses)."""
@@ -136,7 +181,7 @@ def decode_workload(name: str, steps: int, warmup: int):
     bytes_per_launch = float(np.mean([expert_weight_bytes(spec, u) for u in nU]))
     achieved = bytes_per_launch / (avg_ms / 1e3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(name, "decode"),
             "kernel": "moe_experts_decode (k_dec_gateup + k_dec_down), back-to-back over the resident copies",
             "bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(avg_ms * 1e3, 2),
             "distinct_experts_per_call": float(np.mean(nU))}
@@ -178,8 +223,8 @@ def prefill_workload(steps: int, warmup: int):
     flops = 6.0 * spec.H * spec.I * (T * spec.k) + 6.0 * spec.H * spec.Is * T
     achieved = flops / (avg_ms / 1e3) / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_F16_PEAK_TFS, 4), "traffic": None,
-            "kernel": "moe_experts_prefill (tiles + x->fp16 + k_prefill_gateup + k_prefill_down)",
+            "frac": round(achieved / MFMA_F16_PEAK_TFS, 4), "traffic": recorded_traffic("prefill8k", "prefill"),
+            "kernel": "moe_experts_prefill (k_build_tiles + k_x_to_f16 + k_grouped_gemm gate/up + k_grouped_gemm down)",
             "flops_per_launch": flops, "avg_launch_us": round(avg_ms * 1e3, 1)}
     return {"metric": "MoE-layer tokens/s (8192-token prefill chunk)", "value": round(value, 1),
             "unit": "tokens/s", "dtype": "f16", "ms_per_step": round(ms_per_step, 4), "roofline": roof,
@@ -216,6 +261,8 @@ def main():
     ap.add_argument("--workload", default="decode1", choices=["decode1", "verify4", "stack48", "prefill8k"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary 8K prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first copy 256 MiB device-to-device 3 times (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (expert parallelism is a design "
@@ -225,6 +272,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     moe.lib()
+    if args.calibrate_copy:
+        calibrate_copy()
 
     if args.workload == "prefill8k":
         r = prefill_workload(args.steps, args.warmup)
