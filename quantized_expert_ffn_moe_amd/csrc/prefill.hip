@@ -6,12 +6,13 @@
 //     (group, first row) covers every group with 128-row tiles, the shared expert being one more
 //     group of all T tokens;
 //   - one kernel template, two uses: gate/up (A = x rows gathered through perm, B = 128 gate rows
-//     and 128 up rows interleaved in 16-row granules so that g and u of the same (row, n) meet in
+//     and 128 up rows interleaved in 32-row granules so that g and u of the same (row, n) meet in
 //     one lane; SwiGLU epilogue writes h in fp16) and down (A = h rows in sorted order, B = 256
 //     down rows; fp32 output rows);
 //   - block tile 128 x 256, four waves of 64 x 128, K steps of 32 through double-buffered LDS
-//     (rows padded to 80 bytes: the 16-byte fragment reads of 16 lanes hit distinct banks), one
-//     v_mfma_f32_16x16x32_f16 per 16 x 16 output tile and K step;
+//     (rows padded to 80 bytes: the 16-byte fragment reads of 16 lanes hit distinct banks), two
+//     v_mfma_f32_32x32x16_f16 per 32 x 32 output tile and K step (on this chip the 32 x 32 form
+//     sustains a far higher rate than 16 x 16 x 32);
 //   - weights are dequantised in registers: the code is OR-ed into the mantissa of 1024.0, the
 //     offset subtracted (an exact fp16 level) and multiplied by the fp16 scale with packed fp16
 //     arithmetic, i.e. level * scale rounded once to fp16. The pairs come out in an order that
@@ -27,16 +28,14 @@ namespace moe {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 128;      // rows (pairs) per tile
 constexpr int kBN = 256;      // weight rows per tile
-constexpr int kBK = 32;       // K per step (one scale block)
-constexpr int kLds = kBK + 8; // fp16 per LDS row (80 bytes)
+constexpr int kAS = 64 + 8;   // fp16 per A row in LDS: one step of K = 64, padded to 144 bytes
 constexpr int kXcds = 8;
-constexpr int kPD = 3;        // K steps of global loads in flight
 
 struct TileDesc {
     int group;  // expert id, or E for the shared expert
@@ -126,67 +125,77 @@ constexpr uint32_t kMagic16 = 0x64006400u;   // (1024.0, 1024.0) as fp16 pair
 __device__ __forceinline__ uint32_t h2bits(half2v v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ half2v bits2h(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
-// One 32-element block -> 16 fp16 pairs (level * scale, rounded once), in K-permuted order.
+// Codes of one 32-element block held by a lane: Q4 16 bytes (c0), Q8 32 bytes (c0, c1), Q2 8 bytes
+// (c0.xy).
+struct BlockCodes {
+    u32x4 c0, c1;
+};
+
 template <int FMT>
-__device__ __forceinline__ void dequant16(const uint32_t (&w)[8], uint16_t sbits, uint32_t (&o)[16]) {
-    const _Float16 s = __builtin_bit_cast(_Float16, sbits);
-    const half2v sv = {s, s};
+__device__ __forceinline__ void load_codes(const uint8_t* p, BlockCodes& b) {
+    if constexpr (FMT == MOE_Q8_B32) {
+        b.c0 = reinterpret_cast<const u32x4*>(p)[0];
+        b.c1 = reinterpret_cast<const u32x4*>(p)[1];
+    } else if constexpr (FMT == MOE_Q4_B32) {
+        b.c0 = reinterpret_cast<const u32x4*>(p)[0];
+    } else {
+        const u32x2 v = reinterpret_cast<const u32x2*>(p)[0];
+        b.c0.x = v.x;
+        b.c0.y = v.y;
+    }
+}
+
+__device__ __forceinline__ uint32_t dword_of(const BlockCodes& b, int d) {
+    switch (d) {
+        case 0: return b.c0.x;
+        case 1: return b.c0.y;
+        case 2: return b.c0.z;
+        case 3: return b.c0.w;
+        case 4: return b.c1.x;
+        case 5: return b.c1.y;
+        case 6: return b.c1.z;
+        default: return b.c1.w;
+    }
+}
+
+// Pairs 4 kk .. 4 kk + 3 of a block (K-permuted positions 8 kk .. 8 kk + 7) as level * scale,
+// each rounded once to fp16. Pair p of a block holds elements (j, j + G/2) of its G-group:
+//   Q4: dword d = elements 8d .. 8d+7, pair 4d + j = nibbles (j, j + 4), offset 1032 = 1024 + 8;
+//   Q8: dword d = elements 4d .. 4d+3, pairs 2d (bytes 0, 2) and 2d + 1 (bytes 1, 3), offset 1152;
+//   Q2: dword d = elements 16d .. 16d+15, pair 8d + j = crumbs (j, j + 8) as 2c + 1024, offset
+//       1027 = 1024 + 2 * 1.5, times s / 2.
+template <int FMT, int KK>
+__device__ __forceinline__ half8 dequant8(const BlockCodes& b, half2v sv) {
+    uint32_t o[4];
     if constexpr (FMT == MOE_Q4_B32) {
         const half2v off = {(_Float16)1032.f, (_Float16)1032.f};
+        const uint32_t u = dword_of(b, KK) ^ 0x88888888u;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t u = w[d] ^ 0x88888888u;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[4 * d + j] = h2bits((bits2h(((u >> (4 * j)) & 0x000F000Fu) | kMagic16) - off) * sv);
-        }
+        for (int j = 0; j < 4; ++j) o[j] = h2bits((bits2h(((u >> (4 * j)) & 0x000F000Fu) | kMagic16) - off) * sv);
     } else if constexpr (FMT == MOE_Q8_B32) {
         const half2v off = {(_Float16)1152.f, (_Float16)1152.f};
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            const uint32_t u = w[d] ^ 0x80808080u;
-            o[2 * d] = h2bits((bits2h((u & 0x00FF00FFu) | kMagic16) - off) * sv);
-            o[2 * d + 1] = h2bits((bits2h(((u >> 8) & 0x00FF00FFu) | kMagic16) - off) * sv);
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t u = dword_of(b, 2 * KK + h) ^ 0x80808080u;
+            o[2 * h] = h2bits((bits2h((u & 0x00FF00FFu) | kMagic16) - off) * sv);
+            o[2 * h + 1] = h2bits((bits2h(((u >> 8) & 0x00FF00FFu) | kMagic16) - off) * sv);
         }
     } else {
-        // 1024 + 2c - 1027 = 2 (c - 1.5), times s / 2
         const half2v off = {(_Float16)1027.f, (_Float16)1027.f};
         const half2v s2 = sv * half2v{(_Float16)0.5f, (_Float16)0.5f};
+        const uint32_t u = dword_of(b, KK / 2);
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-            const uint32_t u = w[d];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t t = j == 0 ? (u << 1) : (u >> (2 * j - 1));
-                o[8 * d + j] = h2bits((bits2h((t & 0x00060006u) | kMagic16) - off) * s2);
-            }
+        for (int jj = 0; jj < 4; ++jj) {
+            constexpr int j0 = 4 * (KK % 2);
+            const int j = j0 + jj;
+            const uint32_t t = j == 0 ? (u << 1) : (u >> (2 * j - 1));
+            o[jj] = h2bits((bits2h((t & 0x00060006u) | kMagic16) - off) * s2);
         }
     }
-}
-
-template <int FMT>
-__device__ __forceinline__ void load_block_codes(const uint8_t* p, uint32_t (&w)[8]) {
-    if constexpr (FMT == MOE_Q8_B32) {
-        const uint4 a = reinterpret_cast<const uint4*>(p)[0], b = reinterpret_cast<const uint4*>(p)[1];
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    } else if constexpr (FMT == MOE_Q4_B32) {
-        const uint4 a = reinterpret_cast<const uint4*>(p)[0];
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-    } else {
-        const uint2 a = reinterpret_cast<const uint2*>(p)[0];
-        w[0] = a.x; w[1] = a.y;
-    }
+    return __builtin_bit_cast(half8, u32x4{o[0], o[1], o[2], o[3]});
 }
 
 // -------------------------------------------------------------------------------- grouped GEMM
-
-// Registers holding one K step of global loads: two 16-byte A chunks, one block of codes (16 bytes
-// for Q4, 32 for Q8, 8 for Q2) and its scale. Plain members, no arrays: a slot must never be
-// indexed at run time, or it would leave the registers.
-struct LoadSlot {
-    u32x4 a0, a1;
-    u32x4 b0, b1;
-    uint32_t s;
-};
 
 // f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{})
 template <typename F, int... I>
@@ -197,20 +206,31 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// One pipeline step of loads (K = 64, two 32-blocks): four 16-byte chunks of A for the LDS stage,
+// and for each of the lane's two weight tiles the codes and the scale of the lane's own block.
+// Plain members only: a slot must never be indexed at run time, or it would leave the registers.
+struct StepSlot {
+    u32x4 a0, a1, a2, a3;
+    BlockCodes b0, b1;
+    uint32_t s0, s1;
+};
+
 template <int FMT, bool GATEUP>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm(LayerView L, int T, const TileDesc* __restrict__ tiles,
-                                                         const int32_t* __restrict__ ntiles, int n_ntile, const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ ntiles, int n_ntile,
+                                                         const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ perm,
                                                          const _Float16* __restrict__ asrc, _Float16* __restrict__ h16,
                                                          float* __restrict__ y_sorted, float* __restrict__ y_shared) {
-    __shared__ __attribute__((aligned(16))) _Float16 As[2][kBM * kLds];
-    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kBN * kLds];
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][kBM * kAS];
     constexpr int G = perm_group<FMT>();
+    constexpr int BB = FMT == MOE_Q8_B32 ? 32 : FMT == MOE_Q4_B32 ? 16 : 8;   // bytes per block
 
     // XCD-aware work index: block b runs on XCD b % 8, and consecutive work items go to the same
     // XCD. Work items are ordered tile-major: the weight-row tiles of one row tile (same A rows)
     // run side by side, and so do the row tiles of one expert (same weights). The grid is sized for
-    // tiles_max tiles; the split uses the real count so that every XCD gets an equal share.
+    // the largest possible tile count; the split uses the real count so that every XCD gets an
+    // equal share.
     const int nt = *ntiles;
     const int total = nt * n_ntile;
     const int per_xcd = (total + kXcds - 1) / kXcds;
@@ -238,169 +258,170 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(LayerView L, int T, con
     group_rows(offsets, L.E, T, Tk, td.group, base, count);
     const int nrows = min(kBM, count - td.row0);
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave / 2, wn = wave % 2;
+    const int frow = lane % 32, g = lane / 32;
+    const int nb = K / 32;                    // scale blocks along K
+    const int nsteps = (nb + 1) / 2;
 
     // Operand rows past the tile's valid rows or columns are clamped to a valid row: they only feed
     // output rows or columns that are never stored, and every load stays unconditional (so the
-    // compiler can keep several K steps of loads in flight).
-    // A: thread -> two 16-byte chunks (rows tid/4 and tid/4 + 64, quarter tid % 4) of every K step
-    const _Float16* aptr[2];
-    int arow[2];
-    const int aq = tid & 3;
+    // compiler can keep several steps of loads in flight).
+    // A: thread -> 16-byte chunk c = tid % 8 of rows tid / 8 + 32 q (q = 0..3) of every step
+    const int ac = tid & 7;
+    const _Float16* arow[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = (tid >> 2) + 64 * i;
-        arow[i] = r;
+    for (int q = 0; q < 4; ++q) {
+        const int r = (tid >> 3) + 32 * q;
         const int pos = td.row0 + min(r, nrows - 1);
         if constexpr (GATEUP) {
-            const int q = shared ? pos * L.k : perm[base + pos];
-            const int tok = (unsigned)q < (unsigned)Tk ? q / L.k : 0;
-            aptr[i] = asrc + (size_t)tok * H + aq * 8;
+            const int qq = shared ? pos * L.k : perm[base + pos];
+            const int tok = (unsigned)qq < (unsigned)Tk ? qq / L.k : 0;
+            arow[q] = asrc + (size_t)tok * H;
         } else {
             const int64_t hrow = shared ? (int64_t)Tk + pos : (int64_t)base + pos;
-            aptr[i] = asrc + (size_t)hrow * Imax + aq * 8;
+            arow[q] = asrc + (size_t)hrow * Imax;
         }
     }
-    // B: thread -> LDS row tid (one weight row; one 32-block per K step)
-    const uint8_t* bcodes;
-    const uint16_t* bscales;
-    if constexpr (GATEUP) {
-        const int gran = tid / 16;
-        const bool is_up = gran & 1;
-        const int n = min(n0 + (gran / 2) * 16 + tid % 16, N - 1);
-        const int64_t rb = row_bytes(FMT, H);
-        if (shared) {
-            bcodes = (is_up ? L.su_codes : L.sg_codes) + (int64_t)n * rb;
-            bscales = (is_up ? L.su_scales : L.sg_scales) + (int64_t)n * (H / 32);
-        } else {
-            const int64_t row = (int64_t)td.group * L.I + n;
-            bcodes = (is_up ? L.u_codes : L.g_codes) + row * rb;
-            bscales = (is_up ? L.u_scales : L.g_scales) + row * (H / 32);
-        }
-    } else {
-        const int m = min(n0 + tid, H - 1);
-        const int64_t rb = row_bytes(FMT, K);
-        if (shared) {
-            bcodes = L.sd_codes + (int64_t)m * rb;
-            bscales = L.sd_scales + (int64_t)m * (K / 32);
-        } else {
-            const int64_t row = (int64_t)td.group * H + m;
-            bcodes = L.d_codes + row * rb;
-            bscales = L.d_scales + row * (K / 32);
-        }
-    }
-
-    // Global loads run kPD K steps ahead through a ring of register slots: slot r holds step j
-    // with j % kPD == r (steps past the end reload the last one). LDS is double-buffered: stage
-    // ks & 1 holds step ks. Slots are only ever named with compile-time indices so that they stay
-    // in registers.
-    LoadSlot ring0, ring1, ring2;
-    auto ring = [&](auto rc) __attribute__((always_inline)) -> LoadSlot& {
-        constexpr int i = decltype(rc)::value;
-        static_assert(i < 3, "at most three slots");
-        if constexpr (i == 0) return ring0;
-        else if constexpr (i == 1) return ring1;
-        else return ring2;
-    };
-    const int nk = K / kBK;
-    auto gload = [&](LoadSlot& sl, int ks) __attribute__((always_inline)) {
-        ks = min(ks, nk - 1);
-        sl.a0 = *reinterpret_cast<const u32x4*>(aptr[0] + ks * kBK);
-        sl.a1 = *reinterpret_cast<const u32x4*>(aptr[1] + ks * kBK);
-        const uint8_t* c = bcodes + (int64_t)ks * block_bytes(FMT);
-        if constexpr (FMT == MOE_Q8_B32) {
-            sl.b0 = reinterpret_cast<const u32x4*>(c)[0];
-            sl.b1 = reinterpret_cast<const u32x4*>(c)[1];
-        } else if constexpr (FMT == MOE_Q4_B32) {
-            sl.b0 = reinterpret_cast<const u32x4*>(c)[0];
-        } else {
-            const u32x2 v = reinterpret_cast<const u32x2*>(c)[0];
-            sl.b0.x = v.x;
-            sl.b0.y = v.y;
-        }
-        sl.s = bscales[ks];
-    };
-    auto lstore = [&](const LoadSlot& sl, int st) __attribute__((always_inline)) {
-        *reinterpret_cast<u32x4*>(&As[st][arow[0] * kLds + aq * 8]) = sl.a0;
-        *reinterpret_cast<u32x4*>(&As[st][arow[1] * kLds + aq * 8]) = sl.a1;
-        const uint32_t w[8] = {sl.b0.x, sl.b0.y, sl.b0.z, sl.b0.w, sl.b1.x, sl.b1.y, sl.b1.z, sl.b1.w};
-        uint32_t o[16];
-        dequant16<FMT>(w, (uint16_t)sl.s, o);
-        u32x4* dst = reinterpret_cast<u32x4*>(&Bs[st][tid * kLds]);
+    // B: wave w owns weight rows 64 w .. 64 w + 63 of the tile as two 32-row MFMA tiles; lane
+    // (frow, g) loads, for each tile, block 2 s + g of its row at step s and dequantises it
+    // straight into its MFMA operand (no LDS). Gate/up: tile 0 = gate rows, tile 1 = up rows of
+    // the same h columns n0 + 32 w + [0, 32); down: output columns n0 + 64 w + [0, 64).
+    const uint8_t* bc[2];
+    const uint16_t* bs[2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dst[c] = u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
+    for (int j = 0; j < 2; ++j) {
+        if constexpr (GATEUP) {
+            const int n = min(n0 + 32 * wave + frow, N - 1);
+            const int64_t rb = (int64_t)nb * BB;
+            if (shared) {
+                bc[j] = (j ? L.su_codes : L.sg_codes) + (int64_t)n * rb;
+                bs[j] = (j ? L.su_scales : L.sg_scales) + (int64_t)n * nb;
+            } else {
+                const int64_t row = (int64_t)td.group * L.I + n;
+                bc[j] = (j ? L.u_codes : L.g_codes) + row * rb;
+                bs[j] = (j ? L.u_scales : L.g_scales) + row * nb;
+            }
+        } else {
+            const int m = min(n0 + 64 * wave + 32 * j + frow, H - 1);
+            const int64_t rb = (int64_t)nb * BB;
+            if (shared) {
+                bc[j] = L.sd_codes + (int64_t)m * rb;
+                bs[j] = L.sd_scales + (int64_t)m * nb;
+            } else {
+                const int64_t row = (int64_t)td.group * H + m;
+                bc[j] = L.d_codes + row * rb;
+                bs[j] = L.d_scales + row * nb;
+            }
+        }
+    }
+
+    StepSlot ring0, ring1;
+    auto ring = [&](auto rc) __attribute__((always_inline)) -> StepSlot& {
+        if constexpr (decltype(rc)::value == 0) return ring0;
+        else return ring1;
+    };
+    auto gload = [&](StepSlot& sl, int s) __attribute__((always_inline)) {
+        s = min(s, nsteps - 1);
+        const int ka = min(64 * s + 8 * ac, K - 8);   // a chunk past K reloads the last one (zeroed in lstore)
+        sl.a0 = *reinterpret_cast<const u32x4*>(arow[0] + ka);
+        sl.a1 = *reinterpret_cast<const u32x4*>(arow[1] + ka);
+        sl.a2 = *reinterpret_cast<const u32x4*>(arow[2] + ka);
+        sl.a3 = *reinterpret_cast<const u32x4*>(arow[3] + ka);
+        const int b = min(2 * s + g, nb - 1);
+        load_codes<FMT>(bc[0] + (int64_t)b * BB, sl.b0);
+        load_codes<FMT>(bc[1] + (int64_t)b * BB, sl.b1);
+        sl.s0 = bs[0][b];
+        sl.s1 = bs[1][b];
+    };
+    // A chunk past K (the second half of a last step when K % 64 == 32) is written as zeros
+    auto lstore = [&](const StepSlot& sl, int st, int s) __attribute__((always_inline)) {
+        const bool live = 64 * s + 8 * ac < K;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        _Float16* dst = &As[st][(tid >> 3) * kAS + 8 * ac];
+        *reinterpret_cast<u32x4*>(dst) = live ? sl.a0 : z;
+        *reinterpret_cast<u32x4*>(dst + 32 * kAS) = live ? sl.a1 : z;
+        *reinterpret_cast<u32x4*>(dst + 64 * kAS) = live ? sl.a2 : z;
+        *reinterpret_cast<u32x4*>(dst + 96 * kAS) = live ? sl.a3 : z;
     };
 
-    floatx4 acc[4][8];
+    floatx16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int kofs = 8 * (lane / 16);
-    // one K step: MFMAs on LDS stage ks & 1, then step ks + 1 from slot (ks + 1) % kPD into the
-    // other stage, refill that slot with step ks + 1 + kPD, barrier
-    auto kstep = [&](int ks, auto rc) __attribute__((always_inline)) {
-        constexpr int next = (decltype(rc)::value + 1) % kPD;
-        const int cur = ks & 1;
-        half8 a[4], b[8];
+    // one step: dequantise this lane's blocks of slot s % 2, MFMAs against LDS stage s & 1
+    // (A fragment of lane (frow, g) for sub-step kk: row 32 i + frow, K offset 32 g + 8 kk), then
+    // A of step s + 1 into the other stage, refill the slot with step s + 2, barrier
+    auto kstep = [&](int s, auto rc) __attribute__((always_inline)) {
+        StepSlot& cur_sl = ring(rc);
+        StepSlot& nxt_sl = ring(std::integral_constant<int, 1 - decltype(rc)::value>{});
+        const int cur = s & 1;
+        const bool blive = 2 * s + g < nb;     // a block past K contributes zero
+        const _Float16 s0 = blive ? __builtin_bit_cast(_Float16, (uint16_t)cur_sl.s0) : (_Float16)0.f;
+        const _Float16 s1 = blive ? __builtin_bit_cast(_Float16, (uint16_t)cur_sl.s1) : (_Float16)0.f;
+        const half2v sv0 = {s0, s0}, sv1 = {s1, s1};
+        static_for<4>([&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            const half8 b0 = dequant8<FMT, kk>(cur_sl.b0, sv0);
+            const half8 b1 = dequant8<FMT, kk>(cur_sl.b1, sv1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a[i] = *reinterpret_cast<const half8*>(&As[cur][(wm * 64 + 16 * i + lane % 16) * kLds + kofs]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            b[j] = *reinterpret_cast<const half8*>(&Bs[cur][(wn * 128 + 16 * j + lane % 16) * kLds + kofs]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-        lstore(ring(std::integral_constant<int, next>{}), cur ^ 1);
-        gload(ring(std::integral_constant<int, next>{}), ks + 1 + kPD);
+            for (int i = 0; i < 4; ++i) {
+                const half8 a = *reinterpret_cast<const half8*>(&As[cur][(32 * i + frow) * kAS + 32 * g + 8 * kk]);
+                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[i][0], 0, 0, 0);
+                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[i][1], 0, 0, 0);
+            }
+        });
+        gload(cur_sl, s + 2);
+        __builtin_amdgcn_sched_barrier(0);   // issue the refill before waiting on the next step's A
+        lstore(nxt_sl, cur ^ 1, s + 1);
         __syncthreads();
     };
-    static_for<kPD>([&](auto rc) { gload(ring(rc), decltype(rc)::value); });
-    lstore(ring0, 0);
-    gload(ring0, kPD);
+    gload(ring0, 0);
+    gload(ring1, 1);
+    lstore(ring0, 0, 0);
     __syncthreads();
-    int kb = 0;
-    for (; kb + kPD <= nk; kb += kPD) static_for<kPD>([&](auto rc) { kstep(kb + decltype(rc)::value, rc); });
-    static_for<kPD - 1>([&](auto rc) {
-        if (kb + decltype(rc)::value < nk) kstep(kb + decltype(rc)::value, rc);
-    });
+    // the slot of step s + 1 (read by lstore) must be complete before its refill: within a step,
+    // the refill targets slot s % 2 and lstore reads slot (s + 1) % 2
+    int s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+        kstep(s, std::integral_constant<int, 0>{});
+        kstep(s + 1, std::integral_constant<int, 1>{});
+    }
+    if (s < nsteps) kstep(s, std::integral_constant<int, 0>{});
 
+    const int rq = 4 * g;
     if constexpr (GATEUP) {
-        // tiles j = 2jj (gate) and 2jj + 1 (up) of a wave cover h columns (4 wn + jj) * 16 + [0, 16)
+        const int n = n0 + 32 * wave + frow;
+        if (n < N) {
+            const int np = kperm(n, G);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int n = n0 + (4 * wn + jj) * 16 + lane % 16;
-                if (n >= N) continue;
-                const int np = kperm(n, G);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = wm * 64 + 16 * i + 4 * (lane / 16) + r;
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
                     if (row >= nrows) continue;
-                    const float hv = silu_mul(acc[i][2 * jj][r], acc[i][2 * jj + 1][r]);
+                    const float hv = silu_mul(acc[i][0][r], acc[i][1][r]);
                     const int64_t hrow = shared ? (int64_t)Tk + td.row0 + row : (int64_t)base + td.row0 + row;
                     h16[hrow * Imax + np] = (_Float16)hv;
                 }
-            }
+        }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 2; ++j) {
+            const int m = n0 + 64 * wave + 32 * j + frow;
+            if (m >= H) continue;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int m = n0 + wn * 128 + 16 * j + lane % 16;
-                if (m >= H) continue;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = wm * 64 + 16 * i + 4 * (lane / 16) + r;
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
                     if (row >= nrows) continue;
                     if (shared) y_shared[(int64_t)(td.row0 + row) * H + m] = acc[i][j][r];
                     else y_sorted[((int64_t)base + td.row0 + row) * H + m] = acc[i][j][r];
                 }
-            }
+        }
     }
 }
 
