@@ -162,12 +162,16 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 template <int KPL>
 __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, int k, int& my_id, float& my_p) {
     const int lane = threadIdx.x % kWave;
+    // all KPL loads issued unconditionally before any is used (the empty asm pins each value, so the
+    // compiler cannot sink a load into the e < E branch and serialise the round trips)
+    float lv[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) lv[i] = l[min(lane + kWave * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) asm volatile("" : "+v"(lv[i]));
     uint32_t key[KPL];
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const int e = lane + kWave * i;
-        key[i] = e < E ? ordered_key(l[e]) : 0u;
-    }
+    for (int i = 0; i < KPL; ++i) key[i] = lane + kWave * i < E ? ordered_key(lv[i]) : 0u;
     int mine = 0;
     uint32_t mykey = 0u;
     for (int j = 0; j < k; ++j) {

@@ -245,6 +245,24 @@ __device__ __forceinline__ void stage_pairs(const float (&v)[32], uint4* dst, si
     }
 }
 
+// One activation h[row][n] written straight into the staged layout that stage_pairs<FMT, 2> builds
+// for a whole 32-block: row = [8][nbm] uint4 (pairs 0..15 as fp16 hi, then as fp16 lo), pair p of
+// block b at uint4 (p / 4) * nbm + b, component p % 4, half 0 for e0 and 1 for e1.
+template <int FMT>
+__device__ __forceinline__ void put_staged(_Float16* row, int nbm, int n, float v) {
+    using F = Fmt<FMT>;
+    const int b = n / 32, e = n % 32;
+    constexpr int GS = 32 / F::ND;           // elements per dword: 8 (Q4), 4 (Q8), 16 (Q2)
+    const int d = e / GS, r = e % GS;
+    const int j = r % F::NP, half = r / F::NP;
+    const int pidx = d * F::NP + j;
+    const float a = v * F::xs(j);
+    const _Float16 hi = (_Float16)a;
+    const _Float16 lo = (_Float16)(a - (float)hi);
+    row[((size_t)(pidx / 4) * nbm + b) * 8 + 2 * (pidx % 4) + half] = hi;
+    row[((size_t)(4 + pidx / 4) * nbm + b) * 8 + 2 * (pidx % 4) + half] = lo;
+}
+
 __device__ __forceinline__ void bf16x32_to_f32(const uint4 (&raw)[4], float (&v)[32]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -268,11 +286,13 @@ static size_t gateup_smem_bytes(int T, int H, int E) { return lds_head(E) + (siz
 
 // Per block: top-k of every token (given logits) or the given ids, the union of the chosen experts,
 // x as fp16 pairs; per wave: R consecutive rows of one expert's gate and up, all loads issued before
-// use, h = silu(g) * u written for each token that chose the expert.
+// use, h = silu(g) * u written for each token that chose the expert, already in the staged fp16
+// hi/lo layout the down kernel reads. Block 0 publishes ids, p and the plan (plan_g).
 template <int FMT, int T, bool ROUTE, int KPL>
 __global__ __launch_bounds__(256) void k_dec_gateup(LayerView L, const uint16_t* __restrict__ x,
                                                     const float* __restrict__ logits, int32_t* __restrict__ ids,
-                                                    float* __restrict__ p, float* __restrict__ h) {
+                                                    float* __restrict__ p, float* __restrict__ h,
+                                                    DecodePlan* __restrict__ plan_g) {
     constexpr int R = kGateUpRows;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     DecodePlan& P = *reinterpret_cast<DecodePlan*>(smem);
@@ -299,7 +319,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(LayerView L, const uint16_t*
     }
     const int32_t* ids_src = ids;
     if constexpr (ROUTE) {
-        // top-k of token `wave` from the router logits, recomputed by every block
+        // top-k of every token from the router logits (wave t: token t), recomputed by every block
         if (wave < T) {
             int id;
             float pr;
@@ -316,7 +336,12 @@ __global__ __launch_bounds__(256) void k_dec_gateup(LayerView L, const uint16_t*
         __syncthreads();
         ids_src = ids_s;
     }
-    build_plan(ids_src, nullptr, T, L.k, L.E, P, first);
+    build_plan(ids_src, ROUTE ? p_s : nullptr, T, L.k, L.E, P, first);
+    if (blockIdx.x == 0) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(&P);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(plan_g);
+        for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += blockDim.x) dst[i] = src[i];
+    }
 
 #pragma unroll
     for (int s = 0; s < kMaxStage; ++s) {
@@ -372,13 +397,19 @@ __global__ __launch_bounds__(256) void k_dec_gateup(LayerView L, const uint16_t*
     for (int b = lane; b < nb; b += kWave) {
         uint32_t wg[R][8], wu[R][8];
         uint16_t sgb[R], sub[R];
+        // every load of the step issued before any is used (scales first: the compiler would
+        // otherwise sink them behind the code arithmetic, costing a second round trip)
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            sgb[i] = gs[i * nb + b];
+            sub[i] = us[i * nb + b];
+        }
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             load_codes<FMT>(gc + i * rb + (int64_t)b * block_bytes(FMT), wg[i]);
             load_codes<FMT>(uc + i * rb + (int64_t)b * block_bytes(FMT), wu[i]);
-            sgb[i] = gs[i * nb + b];
-            sub[i] = us[i * nb + b];
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             uint32_t xr[16];
@@ -408,7 +439,8 @@ __global__ __launch_bounds__(256) void k_dec_gateup(LayerView L, const uint16_t*
             const float us_ = wave_sum(u[i][t]);
             if (lane == 0 && ((mask >> t) & 1u)) {
                 const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
-                h[(size_t)row * Imax + n0 + i] = silu_mul(gs_, us_);
+                put_staged<FMT>(reinterpret_cast<_Float16*>(h + (size_t)row * Imax), Imax / 32, n0 + i,
+                                silu_mul(gs_, us_));
             }
         }
 }
@@ -424,37 +456,50 @@ static size_t down_smem_bytes(int T, int k, int E, int Imax, int items_max, bool
 }
 
 // Each wave owns RPW output rows m; lane items are (slot, 32-block) pairs of those rows; a lane
-// issues the loads of up to MAXJ items of every row before using any of them. h is fetched while
-// the plan is built and kept in LDS as fp16 hi + lo pairs (about 22 bits), so the dot products run
-// on v_dot2_f32_f16 with fp32 accumulation.
+// issues the loads of up to MAXJ items of every row before using any of them. The plan and h (fp16
+// hi + lo pairs, about 22 bits, already in the LDS layout) come from the gate/up kernel and are
+// copied into LDS first, so the dot products run on v_dot2_f32_f16 with fp32 accumulation.
 template <int FMT, int T, bool COMBINE>
-__global__ __launch_bounds__(256) void k_dec_down(LayerView L, const int32_t* __restrict__ ids,
-                                                  const float* __restrict__ p, const float* __restrict__ h,
-                                                  float* __restrict__ out, float* __restrict__ y_pairs,
-                                                  float* __restrict__ y_shared, int items_max) {
+__global__ __launch_bounds__(256) void k_dec_down(LayerView L, const DecodePlan* __restrict__ plan_g,
+                                                  const float* __restrict__ h, float* __restrict__ out,
+                                                  float* __restrict__ y_pairs, float* __restrict__ y_shared,
+                                                  int items_max) {
     constexpr int RPW = kDownRows, MAXJ = kDownJ;
-    constexpr int kPre = 1;   // (row, block) items of h per thread loaded before the plan is built
     extern __shared__ __attribute__((aligned(16))) char smem[];
     DecodePlan& P = *reinterpret_cast<DecodePlan*>(smem);
-    int* first = reinterpret_cast<int*>(smem + align_up(sizeof(DecodePlan), 16));
     uint4* hq = reinterpret_cast<uint4*>(smem + lds_head(L.E));
     const int Imax = L.Imax();
     const int nbm = Imax / 32;
     const int npairs = T * L.k;
     const int nrows_h = npairs + (L.Is > 0 ? T : 0);
     float* part = reinterpret_cast<float*>(hq + (size_t)(npairs + T) * 8 * nbm);
-
-    float4 hpre[kPre][8];
+    // the plan first (the weight addresses depend on it), h (already staged) in flight behind it
+    constexpr int kPlanWords = (int)(sizeof(DecodePlan) / 4);
+    constexpr int kHBatch = 5;   // uint4 of h per thread held in registers across the weight loads
+    const uint4* hs = reinterpret_cast<const uint4*>(h);
+    const int n4 = nrows_h * 8 * nbm;
+    const uint32_t* ps = reinterpret_cast<const uint32_t*>(plan_g);
+    uint32_t pw[(kPlanWords + 255) / 256];
 #pragma unroll
-    for (int i = 0; i < kPre; ++i) {
-        const int rbk = threadIdx.x + i * blockDim.x;
-        if (rbk < nrows_h * nbm) {
-            const float4* hp = reinterpret_cast<const float4*>(h + (size_t)(rbk / nbm) * Imax + (size_t)(rbk % nbm) * 32);
+    for (int i = 0; i < (kPlanWords + 255) / 256; ++i) {
+        const int w = (int)threadIdx.x + 256 * i;
+        pw[i] = ps[min(w, kPlanWords - 1)];   // unconditional loads stay in flight together
+    }
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // (a HIP uint4 array would live in scratch)
+    const u32x4_t* hs4 = reinterpret_cast<const u32x4_t*>(h);
+    u32x4_t hv0[kHBatch];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) hpre[i][c] = hp[c];
+    for (int b = 0; b < kHBatch; ++b) hv0[b] = hs4[min((int)threadIdx.x + 256 * b, n4 - 1)];
+    __builtin_amdgcn_sched_barrier(0);   // h loads are issued before the wait on the plan words
+    {
+        uint32_t* pd = reinterpret_cast<uint32_t*>(&P);
+#pragma unroll
+        for (int i = 0; i < (kPlanWords + 255) / 256; ++i) {
+            const int w = (int)threadIdx.x + 256 * i;
+            if (w < kPlanWords) pd[w] = pw[i];
         }
     }
-    build_plan(ids, COMBINE ? p : nullptr, T, L.k, L.E, P, first);
+    __syncthreads();
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int H = L.H;
     const int nbI = L.I / 32, nbS = L.Is / 32;
@@ -476,6 +521,10 @@ __global__ __launch_bounds__(256) void k_dec_down(LayerView L, const int32_t* __
         uint16_t sdb[RPW][MAXJ];
         int slot_[MAXJ], b_[MAXJ];
         bool ok[RPW][MAXJ];
+        const uint8_t* dcp[RPW][MAXJ];
+        const uint16_t* dsp[RPW][MAXJ];
+        // addresses first; an item past the end reads expert 0's first row (valid memory, result
+        // unused), so that every load below is unconditional and all of them stay in flight together
 #pragma unroll
         for (int jj = 0; jj < MAXJ; ++jj) {
             const int it = lane + kWave * (j0 + jj);
@@ -487,50 +536,42 @@ __global__ __launch_bounds__(256) void k_dec_down(LayerView L, const int32_t* __
             }
             slot_[jj] = slot;
             b_[jj] = b;
+            const int e = P.expert[slot < 64 ? slot : 0];
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
-                const int m = m0 + r;
-                ok[r][jj] = iv && m < H;
-                sdb[r][jj] = 0;
-                if (ok[r][jj]) {
-                    const uint8_t* dc;
-                    if (slot < 64) {
-                        const int64_t row = (int64_t)P.expert[slot] * H + m;
-                        dc = L.d_codes + row * rbI + (int64_t)b * block_bytes(FMT);
-                        sdb[r][jj] = L.d_scales[row * nbI + b];
-                    } else {
-                        dc = L.sd_codes + (int64_t)m * rbS + (int64_t)b * block_bytes(FMT);
-                        sdb[r][jj] = L.sd_scales[(int64_t)m * nbS + b];
-                    }
-                    load_codes<FMT>(dc, w[r][jj]);
+                const int m = min(m0 + r, H - 1);
+                ok[r][jj] = iv && m0 + r < H;
+                if (!iv) {
+                    dcp[r][jj] = L.d_codes;
+                    dsp[r][jj] = L.d_scales;
+                } else if (slot < 64) {
+                    const int64_t row = (int64_t)e * H + m;
+                    dcp[r][jj] = L.d_codes + row * rbI + (int64_t)b * block_bytes(FMT);
+                    dsp[r][jj] = L.d_scales + row * nbI + b;
+                } else {
+                    dcp[r][jj] = L.sd_codes + (int64_t)m * rbS + (int64_t)b * block_bytes(FMT);
+                    dsp[r][jj] = L.sd_scales + (int64_t)m * nbS + b;
                 }
             }
         }
+#pragma unroll
+        for (int jj = 0; jj < MAXJ; ++jj)
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) sdb[r][jj] = *dsp[r][jj];
+#pragma unroll
+        for (int jj = 0; jj < MAXJ; ++jj)
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) load_codes<FMT>(dcp[r][jj], w[r][jj]);
+        __builtin_amdgcn_sched_barrier(0);
         if (j0 == 0) {
-            // h into LDS as fp16 hi/lo pairs in code-pair order
+            // h into LDS behind the first weight loads
+            u32x4_t* hq4 = reinterpret_cast<u32x4_t*>(hq);
 #pragma unroll
-            for (int i = 0; i < kPre; ++i) {
-                const int rbk = threadIdx.x + i * blockDim.x;
-                if (rbk < nrows_h * nbm) {
-                    float v[32];
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        v[4 * c] = hpre[i][c].x; v[4 * c + 1] = hpre[i][c].y;
-                        v[4 * c + 2] = hpre[i][c].z; v[4 * c + 3] = hpre[i][c].w;
-                    }
-                    stage_pairs<FMT, 2>(v, hq + (size_t)(rbk / nbm) * 8 * nbm + rbk % nbm, nbm);
-                }
+            for (int b = 0; b < kHBatch; ++b) {
+                const int i = (int)threadIdx.x + 256 * b;
+                if (i < n4) hq4[i] = hv0[b];
             }
-            for (int rbk = threadIdx.x + kPre * blockDim.x; rbk < nrows_h * nbm; rbk += blockDim.x) {
-                const float4* hp = reinterpret_cast<const float4*>(h + (size_t)(rbk / nbm) * Imax + (size_t)(rbk % nbm) * 32);
-                float v[32];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const float4 q = hp[c];
-                    v[4 * c] = q.x; v[4 * c + 1] = q.y; v[4 * c + 2] = q.z; v[4 * c + 3] = q.w;
-                }
-                stage_pairs<FMT, 2>(v, hq + (size_t)(rbk / nbm) * 8 * nbm + rbk % nbm, nbm);
-            }
+            for (int i = (int)threadIdx.x + 256 * kHBatch; i < n4; i += 256) hq[i] = hs[i];
             __syncthreads();
         }
 #pragma unroll
@@ -606,8 +647,6 @@ __global__ __launch_bounds__(256) void k_dec_down(LayerView L, const int32_t* __
 
 // ----------------------------------------------------------------------------------- launchers
 
-static int kpl_for(int E) { return E <= 64 ? 1 : E <= 128 ? 2 : E <= 256 ? 4 : E <= 512 ? 8 : 16; }
-
 moe_status launch_route_gemv(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
                              float* logits, hipStream_t s) {
     const dim3 grid((E + 3) / 4), block(256);
@@ -622,8 +661,12 @@ moe_status launch_route_gemv(const float* w_r, const float* bias, const uint16_t
     return MOE_OK;
 }
 
-// h rows: T*k pairs then T shared tokens, Imax floats each
-size_t decode_scratch_floats(const LayerView& L, int T) { return (size_t)(T * L.k + T) * L.Imax(); }
+// h rows (T*k pairs then T shared tokens, Imax floats each, holding the staged fp16 hi/lo pairs),
+// then the plan published by the gate/up kernel
+static size_t h_floats(const LayerView& L, int T) { return (size_t)(T * L.k + T) * L.Imax(); }
+size_t decode_scratch_floats(const LayerView& L, int T) {
+    return h_floats(L, T) + align_up(sizeof(DecodePlan), 256) / 4;
+}
 
 static int down_items_max(const LayerView& L, int T) {
     const int slots = min(T * L.k, L.E);
@@ -647,13 +690,13 @@ static bool allow_smem(K kernel, size_t bytes) {
 
 template <int FMT, int T, bool ROUTE, int KPL>
 static moe_status launch_gateup(const LayerView& L, const uint16_t* x, const float* logits, int32_t* ids, float* p,
-                                float* h, hipStream_t s) {
+                                float* h, DecodePlan* plan_g, hipStream_t s) {
     const int64_t rows1 = (int64_t)T * L.k * L.I + L.Is;
     const int64_t waves1 = (rows1 + kGateUpRows - 1) / kGateUpRows;
     const size_t sm = gateup_smem_bytes(T, L.H, L.E);
     auto kern = k_dec_gateup<FMT, T, ROUTE, KPL>;
     if (!allow_smem(kern, sm)) return MOE_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(kern, dim3((unsigned)((waves1 + 3) / 4)), dim3(256), sm, s, L, x, logits, ids, p, h);
+    hipLaunchKernelGGL(kern, dim3((unsigned)((waves1 + 3) / 4)), dim3(256), sm, s, L, x, logits, ids, p, h, plan_g);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -661,18 +704,14 @@ static moe_status launch_gateup(const LayerView& L, const uint16_t* x, const flo
 template <int FMT, int T>
 static moe_status launch_experts_t(const LayerView& L, const uint16_t* x, const float* logits, int32_t* ids, float* p,
                                    float* h, float* out, float* y_pairs, float* y_shared, hipStream_t s) {
+    DecodePlan* plan_g = reinterpret_cast<DecodePlan*>(h + h_floats(L, T));
     moe_status st;
-    if (logits) {
-        switch (kpl_for(L.E)) {
-            case 1: st = launch_gateup<FMT, T, true, 1>(L, x, logits, ids, p, h, s); break;
-            case 2: st = launch_gateup<FMT, T, true, 2>(L, x, logits, ids, p, h, s); break;
-            case 4: st = launch_gateup<FMT, T, true, 4>(L, x, logits, ids, p, h, s); break;
-            case 8: st = launch_gateup<FMT, T, true, 8>(L, x, logits, ids, p, h, s); break;
-            default: st = launch_gateup<FMT, T, true, 16>(L, x, logits, ids, p, h, s); break;
-        }
-    } else {
-        st = launch_gateup<FMT, T, false, 1>(L, x, nullptr, ids, nullptr, h, s);
-    }
+    if (!logits) st = launch_gateup<FMT, T, false, 1>(L, x, nullptr, ids, nullptr, h, plan_g, s);
+    else if (L.E <= 64) st = launch_gateup<FMT, T, true, 1>(L, x, logits, ids, p, h, plan_g, s);
+    else if (L.E <= 128) st = launch_gateup<FMT, T, true, 2>(L, x, logits, ids, p, h, plan_g, s);
+    else if (L.E <= 256) st = launch_gateup<FMT, T, true, 4>(L, x, logits, ids, p, h, plan_g, s);
+    else if (L.E <= 512) st = launch_gateup<FMT, T, true, 8>(L, x, logits, ids, p, h, plan_g, s);
+    else st = launch_gateup<FMT, T, true, 16>(L, x, logits, ids, p, h, plan_g, s);
     if (st != MOE_OK) return st;
     const int items_max = down_items_max(L, T);
     const int blocks = (L.H + 4 * kDownRows - 1) / (4 * kDownRows);
@@ -680,11 +719,11 @@ static moe_status launch_experts_t(const LayerView& L, const uint16_t* x, const 
     const size_t sm = down_smem_bytes(T, L.k, L.E, L.Imax(), items_max, combine);
     if (combine) {
         if (!allow_smem(k_dec_down<FMT, T, true>, sm)) return MOE_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL((k_dec_down<FMT, T, true>), dim3(blocks), dim3(256), sm, s, L, ids, p, h, out, nullptr,
+        hipLaunchKernelGGL((k_dec_down<FMT, T, true>), dim3(blocks), dim3(256), sm, s, L, plan_g, h, out, nullptr,
                            nullptr, items_max);
     } else {
         if (!allow_smem(k_dec_down<FMT, T, false>, sm)) return MOE_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL((k_dec_down<FMT, T, false>), dim3(blocks), dim3(256), sm, s, L, ids, nullptr, h, nullptr,
+        hipLaunchKernelGGL((k_dec_down<FMT, T, false>), dim3(blocks), dim3(256), sm, s, L, plan_g, h, nullptr,
                            y_pairs, y_shared, items_max);
     }
     MOE_LAUNCH_CHECK();

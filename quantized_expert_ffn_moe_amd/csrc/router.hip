@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const float* __restrict_
 template <int KPL>
 __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ logits, int T, int E, int k,
                                                       int32_t* __restrict__ ids, float* __restrict__ p) {
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
     int id;
     float pr;
