@@ -7,7 +7,8 @@ combine + shared expert) over one batch of seeded synthetic input, as ``moe_laye
   decode1 (default): 1 token, H 2048, 256 experts top-8 + shared (I 512), 4-bit experts. The layer
       is replicated 48 times at distinct HBM addresses (all 256 experts of each copy resident) and
       one step is 48 sequential ``moe_layer`` calls, one per copy, so every call streams its
-      experts from HBM rather than from the 256 MB Infinity Cache.
+      experts from HBM rather than from the 256 MB Infinity Cache. The step is captured once as a
+      HIP graph and replayed (``--eager`` launches every call from Python instead).
   verify4: the same with 4 tokens and 8-bit experts.
   stack48: 48 distinct layers of 512 experts top-10, 2-bit experts, 1 token (36 GB resident).
   prefill8k: one 8192-token chunk through one layer (256 experts, 4-bit, shared expert).
@@ -112,24 +113,40 @@ def calibrate_copy(mib: int = 256, reps: int = 3):
     log("copy calibration: %d x %d MiB device-to-device" % (reps, mib))
 
 
-def time_calls(fn_list, warmup: int, reps: int) -> float:
+def capture(fn_list):
+    """One HIP graph holding the launches of fn_list in order (the library launches on torch's
+    current stream, which is the capture stream inside torch.cuda.graph)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fn_list:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_calls(fn_list, warmup: int, reps: int, graph: bool = False) -> float:
     """Average duration (ms) of one launch from a list of zero-arg launches, played back to back
-    reps times between two HIP events on torch's current stream (the stream the library uses)."""
+    reps times between two HIP events on torch's current stream (the stream the library uses);
+    with graph=True the list is captured once and the graph replayed."""
     for _ in range(warmup):
         for f in fn_list:
             f()
     torch.cuda.synchronize()
+    g = capture(fn_list) if graph else None
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
-        for f in fn_list:
-            f()
+        if g is not None:
+            g.replay()
+        else:
+            for f in fn_list:
+                f()
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / (reps * len(fn_list))
 
 
-def decode_workload(name: str, steps: int, warmup: int):
+def decode_workload(name: str, steps: int, warmup: int, graph: bool = True):
     spec = synth.CONFIGS[name]
     layers = []
     xs = []
@@ -160,10 +177,16 @@ def decode_workload(name: str, steps: int, warmup: int):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # one step (all layer calls) captured as a HIP graph and replayed: the launches of a decode
+    # step are issued once, as a serving loop would
+    g = capture(calls) if graph else None
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(steps):
-        step()
+        if g is not None:
+            g.replay()
+        else:
+            step()
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b)
@@ -177,17 +200,19 @@ def decode_workload(name: str, steps: int, warmup: int):
     ews = moe.Workspace()
     ecalls = [lambda L=L, x=x, i=i: moe.moe_experts_decode(L, x, i, y_pairs=ypairs, y_shared=ysh, ws=ews)
               for L, x, i in zip(layers, xs, ids)]
-    avg_ms = time_calls(ecalls, 2, max(3, steps))
+    avg_ms = time_calls(ecalls, 2, max(3, steps), graph=graph)
     bytes_per_launch = float(np.mean([expert_weight_bytes(spec, u) for u in nU]))
     achieved = bytes_per_launch / (avg_ms / 1e3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(name, "decode"),
-            "kernel": "moe_experts_decode (k_dec_gateup + k_dec_down), back-to-back over the resident copies",
+            "kernel": "moe_experts_decode (k_dec_gateup + k_dec_down), back-to-back over the resident copies"
+                      + (" (one HIP graph)" if graph else ""),
             "bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(avg_ms * 1e3, 2),
             "distinct_experts_per_call": float(np.mean(nU))}
     cfg = {"workload": name, "tokens_per_call": T, "hidden": spec.H, "experts": spec.E, "top_k": spec.k,
            "inter": spec.I, "shared_inter": spec.Is, "format": synth.FMT_NAMES[spec.fmt],
-           "layer_calls_per_step": len(layers), "resident_layers": len(layers)}
+           "layer_calls_per_step": len(layers), "resident_layers": len(layers),
+           "launch": "hip_graph" if graph else "eager"}
     return value, ms_per_step, roof, cfg
 
 
@@ -261,6 +286,8 @@ def main():
     ap.add_argument("--workload", default="decode1", choices=["decode1", "verify4", "stack48", "prefill8k"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary 8K prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every decode call from Python instead of replaying one captured HIP graph per step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 256 MiB device-to-device 3 times (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -280,7 +307,7 @@ def main():
         value, ms, roof, cfg, metric = r["value"], r["ms_per_step"], r["roofline"], r["config"], r["metric"]
         secondary = None
     else:
-        value, ms, roof, cfg = decode_workload(args.workload, args.steps, args.warmup)
+        value, ms, roof, cfg = decode_workload(args.workload, args.steps, args.warmup, graph=not args.eager)
         metric = "MoE-layer tokens/s (decode, %% HBM peak on expert-weight bytes)"
         secondary = None if args.no_prefill else prefill_workload(max(3, args.steps // 4), 2)
     line = {"metric": metric.replace("%%", "%"), "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,

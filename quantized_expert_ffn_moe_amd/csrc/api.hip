@@ -103,8 +103,8 @@ struct LayerWs {
     float* logits;
     int32_t* ids;
     float* p;
-    float* y_rows;     // y_pairs (decode) or y_sorted (prefill), [T*k][H]
-    float* y_shared;   // [T][H]
+    _Float16* y_rows;    // y_sorted (prefill), [T*k][H], fp16 inside the fused layer
+    _Float16* y_shared;  // [T][H]
     int32_t *offsets, *perm, *inv, *chunks;  // prefill only
     float* h;          // decode only
     void* prefill;     // prefill only
@@ -119,8 +119,8 @@ LayerWs carve_layer(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
     if (T <= 4) {
         r.h = c.take<float>(decode_scratch_floats(shape_view(d), T));
     } else {
-        r.y_rows = c.take<float>(P * d->hidden);
-        r.y_shared = c.take<float>((size_t)T * d->hidden);
+        r.y_rows = c.take<_Float16>(P * d->hidden);
+        r.y_shared = c.take<_Float16>((size_t)T * d->hidden);
         r.offsets = c.take<int32_t>((size_t)d->num_experts + 1);
         r.perm = c.take<int32_t>(P);
         r.inv = c.take<int32_t>(P);
@@ -244,7 +244,7 @@ moe_status moe_experts_prefill(const moe_layer_desc* d, const moe_layer_weights*
     size_t need = 0;
     carve_prefill_ws(d, T, nullptr, &need);
     MOE_TRY(check_ws(ws, ws_bytes, need));
-    return launch_prefill_experts(view(d, w), x, T, offsets, perm, y_sorted, y_shared,
+    return launch_prefill_experts(view(d, w), x, T, offsets, perm, y_sorted, y_shared, false,
                                   carve_prefill_ws(d, T, ws, nullptr).scratch, (hipStream_t)stream);
 }
 
@@ -279,12 +279,14 @@ moe_status moe_layer(const moe_layer_desc* d, const moe_layer_weights* w, const 
         MOE_TRY(launch_route_gemv(w->w_router, w->router_bias, x, T, L.H, L.E, lg, s));
         return launch_decode_experts(L, x, T, lg, id, pr, lw.h, out, nullptr, nullptr, s);
     }
-    const float* ysh = d->shared_inter > 0 ? lw.y_shared : nullptr;
+    // the expert outputs between the down GEMM and the combine are fp16 rows here (half the bytes
+    // of the largest stream); the combine sums them in fp32
+    const _Float16* ysh = d->shared_inter > 0 ? lw.y_shared : nullptr;
     MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, L.H, L.E, lg, s));
     MOE_TRY(launch_topk(lg, T, L.E, L.k, id, pr, s));
     MOE_TRY(launch_permute(id, T, L.k, L.E, lw.offsets, lw.perm, lw.inv, lw.chunks, s));
-    MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, lw.prefill, s));
-    return launch_combine(T, L.k, L.H, pr, lw.y_rows, lw.inv, ysh, out, s);
+    MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, true, lw.prefill, s));
+    return launch_combine_f16(T, L.k, L.H, pr, lw.y_rows, lw.inv, ysh, out, s);
 }
 
 }  // extern "C"

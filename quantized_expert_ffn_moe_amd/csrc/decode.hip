@@ -22,6 +22,8 @@
 //                    hi/lo pairs, laid out so that lanes reading consecutive 32-blocks hit
 //                    consecutive banks), weighted by the routing probability and summed with the
 //                    shared expert (combine fused), or written per pair for moe_experts_decode.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace moe {
@@ -39,40 +41,40 @@ struct DecodePlan {
     float pw[64][4];         // slot, token -> routing probability of that pair (0 if none)
 };
 
-// first: LDS scratch of E ints. ids outside [0, E) are ignored (no memory access with them).
-__device__ void build_plan(const int32_t* __restrict__ ids, const float* __restrict__ p, int T, int k, int E,
-                           DecodePlan& P, int* first) {
-    const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += blockDim.x) first[e] = 64;
-    for (int i = tid; i < 64; i += blockDim.x) {
-        P.tokmask[i] = 0u;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) { P.pair_of[i][t] = -1; P.pw[i][t] = 0.f; }
-    }
-    __syncthreads();
+// Built by one wave (lane q = pair q = t*k + j; T*k <= 64), LDS only, no block barrier: the caller
+// publishes P to the other waves with one. first: LDS scratch of E ints. ids outside [0, E) are
+// ignored (no memory access with them).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ void build_plan_wave(const int32_t* __restrict__ ids, const float* __restrict__ p, int T, int k, int E,
+                                DecodePlan& P, int* first) {
+    const int lane = threadIdx.x % kWave;
     const int npairs = T * k;
-    const int q = tid;
-    int e = -1;
-    bool valid = false;
-    if (tid < 64) {
-        e = q < npairs ? ids[q] : -1;
-        valid = q < npairs && e >= 0 && e < E;
-        if (valid) atomicMin(&first[e], q);
+    const int q = lane;
+    const int e = q < npairs ? ids[q] : -1;
+    const float pq = p && q < npairs ? p[q] : 0.f;
+    for (int i = lane; i < E; i += kWave) first[i] = 64;
+    P.tokmask[lane] = 0u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) { P.pair_of[lane][t] = -1; P.pw[lane][t] = 0.f; }
+    wave_lds_sync();
+    const bool valid = q < npairs && e >= 0 && e < E;
+    if (valid) atomicMin(&first[e], q);
+    wave_lds_sync();
+    const int fq = valid ? first[e] : 63;
+    const uint64_t firsts = __ballot(valid && fq == q);
+    const int slot = __popcll(firsts & ((1ull << fq) - 1ull));
+    if (valid) {
+        if (fq == q) P.expert[slot] = e;
+        atomicOr(&P.tokmask[slot], 1u << (q / k));
+        P.pair_of[slot][q / k] = q;
+        P.pw[slot][q / k] = pq;
     }
-    __syncthreads();
-    if (tid < 64) {
-        const int fq = valid ? first[e] : 63;
-        const uint64_t firsts = __ballot(valid && fq == q);
-        const int slot = __popcll(firsts & ((1ull << fq) - 1ull));
-        if (valid) {
-            if (fq == q) P.expert[slot] = e;
-            atomicOr(&P.tokmask[slot], 1u << (q / k));
-            P.pair_of[slot][q / k] = q;
-            P.pw[slot][q / k] = p ? p[q] : 0.f;
-        }
-        if (tid == 0) P.nU = __popcll(firsts);
-    }
-    __syncthreads();
+    if (lane == 0) P.nU = __popcll(firsts);
 }
 
 // ----------------------------------------------------------------------------------- K1 router
@@ -275,7 +277,9 @@ __device__ __forceinline__ void bf16x32_to_f32(const uint4 (&raw)[4], float (&v)
 // ----------------------------------------------------------------------------------- K2 gate/up
 
 constexpr int kGateUpRows = 2;    // gate/up rows per K2 wave
-constexpr int kDownRows = 2;      // output rows per K3 wave
+constexpr int kDownRows = 1;      // output rows per K3 wave
+constexpr int kDownWaves = 8;     // waves per K3 block (two per SIMD hide each other's latency)
+constexpr int kDownThreads = kDownWaves * kWave;
 constexpr int kDownJ = 4;         // down items per row whose loads a K3 lane issues together
 
 // LDS of k_dec_gateup: plan | first[E] | ids_s[64] | p_s[64] | xq[T][4][nb] uint4
@@ -289,7 +293,7 @@ static size_t gateup_smem_bytes(int T, int H, int E) { return lds_head(E) + (siz
 // use, h = silu(g) * u written for each token that chose the expert, already in the staged fp16
 // hi/lo layout the down kernel reads. Block 0 publishes ids, p and the plan (plan_g).
 template <int FMT, int T, bool ROUTE, int KPL>
-__global__ __launch_bounds__(256) void k_dec_gateup(LayerView L, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(1024) void k_dec_gateup(LayerView L, const uint16_t* __restrict__ x,
                                                     const float* __restrict__ logits, int32_t* __restrict__ ids,
                                                     float* __restrict__ p, float* __restrict__ h,
                                                     DecodePlan* __restrict__ plan_g) {
@@ -333,16 +337,10 @@ __global__ __launch_bounds__(256) void k_dec_gateup(LayerView L, const uint16_t*
                 }
             }
         }
-        __syncthreads();
         ids_src = ids_s;
     }
-    build_plan(ids_src, ROUTE ? p_s : nullptr, T, L.k, L.E, P, first);
-    if (blockIdx.x == 0) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(&P);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(plan_g);
-        for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += blockDim.x) dst[i] = src[i];
-    }
 
+    // x staging (the waves without a top-k start at once)
 #pragma unroll
     for (int s = 0; s < kMaxStage; ++s) {
         const int tb = threadIdx.x + s * blockDim.x;
@@ -361,9 +359,16 @@ __global__ __launch_bounds__(256) void k_dec_gateup(LayerView L, const uint16_t*
         bf16x32_to_f32(raw, v);
         stage_pairs<FMT, 1>(v, xq + (size_t)(tb / nb) * 4 * nb + tb % nb, nb);
     }
-    __syncthreads();
+    if constexpr (ROUTE) __syncthreads();   // every token's choices in ids_s
+    if (wave == 0) build_plan_wave(ids_src, ROUTE ? p_s : nullptr, T, L.k, L.E, P, first);
+    __syncthreads();                        // the plan and the staged x
+    if (blockIdx.x == 0) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(&P);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(plan_g);
+        for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += blockDim.x) dst[i] = src[i];
+    }
 
-    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave;
     const int64_t r0 = gw * R;
     int slot = -1, n0 = 0;
     const uint8_t *gc = nullptr, *uc = nullptr;
@@ -451,7 +456,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(LayerView L, const uint16_t*
 // lanes reading consecutive 32-blocks hit consecutive banks) | partials [4][RPW][T][items]
 static size_t down_smem_bytes(int T, int k, int E, int Imax, int items_max, bool combine) {
     size_t b = lds_head(E) + (size_t)(T * k + T) * (Imax / 32) * 128;
-    if (!combine) b += (size_t)4 * kDownRows * T * items_max * 4;
+    if (!combine) b += (size_t)kDownWaves * kDownRows * T * items_max * 4;
     return b;
 }
 
@@ -460,7 +465,7 @@ static size_t down_smem_bytes(int T, int k, int E, int Imax, int items_max, bool
 // hi + lo pairs, about 22 bits, already in the LDS layout) come from the gate/up kernel and are
 // copied into LDS first, so the dot products run on v_dot2_f32_f16 with fp32 accumulation.
 template <int FMT, int T, bool COMBINE>
-__global__ __launch_bounds__(256) void k_dec_down(LayerView L, const DecodePlan* __restrict__ plan_g,
+__global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const DecodePlan* __restrict__ plan_g,
                                                   const float* __restrict__ h, float* __restrict__ out,
                                                   float* __restrict__ y_pairs, float* __restrict__ y_shared,
                                                   int items_max) {
@@ -475,27 +480,27 @@ __global__ __launch_bounds__(256) void k_dec_down(LayerView L, const DecodePlan*
     float* part = reinterpret_cast<float*>(hq + (size_t)(npairs + T) * 8 * nbm);
     // the plan first (the weight addresses depend on it), h (already staged) in flight behind it
     constexpr int kPlanWords = (int)(sizeof(DecodePlan) / 4);
-    constexpr int kHBatch = 5;   // uint4 of h per thread held in registers across the weight loads
+    constexpr int kHBatch = 3;   // uint4 of h per thread held in registers across the weight loads
     const uint4* hs = reinterpret_cast<const uint4*>(h);
     const int n4 = nrows_h * 8 * nbm;
     const uint32_t* ps = reinterpret_cast<const uint32_t*>(plan_g);
-    uint32_t pw[(kPlanWords + 255) / 256];
+    uint32_t pw[(kPlanWords + kDownThreads - 1) / kDownThreads];
 #pragma unroll
-    for (int i = 0; i < (kPlanWords + 255) / 256; ++i) {
-        const int w = (int)threadIdx.x + 256 * i;
+    for (int i = 0; i < (kPlanWords + kDownThreads - 1) / kDownThreads; ++i) {
+        const int w = (int)threadIdx.x + kDownThreads * i;
         pw[i] = ps[min(w, kPlanWords - 1)];   // unconditional loads stay in flight together
     }
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // (a HIP uint4 array would live in scratch)
     const u32x4_t* hs4 = reinterpret_cast<const u32x4_t*>(h);
     u32x4_t hv0[kHBatch];
 #pragma unroll
-    for (int b = 0; b < kHBatch; ++b) hv0[b] = hs4[min((int)threadIdx.x + 256 * b, n4 - 1)];
+    for (int b = 0; b < kHBatch; ++b) hv0[b] = hs4[min((int)threadIdx.x + kDownThreads * b, n4 - 1)];
     __builtin_amdgcn_sched_barrier(0);   // h loads are issued before the wait on the plan words
     {
         uint32_t* pd = reinterpret_cast<uint32_t*>(&P);
 #pragma unroll
-        for (int i = 0; i < (kPlanWords + 255) / 256; ++i) {
-            const int w = (int)threadIdx.x + 256 * i;
+        for (int i = 0; i < (kPlanWords + kDownThreads - 1) / kDownThreads; ++i) {
+            const int w = (int)threadIdx.x + kDownThreads * i;
             if (w < kPlanWords) pd[w] = pw[i];
         }
     }
@@ -507,7 +512,7 @@ __global__ __launch_bounds__(256) void k_dec_down(LayerView L, const DecodePlan*
     const int items = nU * nbI + nbS;
     const int nit = (items + kWave - 1) / kWave;
     const int64_t rbI = row_bytes(FMT, L.I), rbS = row_bytes(FMT, L.Is);
-    const int m0 = (blockIdx.x * 4 + wave) * RPW;
+    const int m0 = (blockIdx.x * kDownWaves + wave) * RPW;
     float* mypart = part + (size_t)wave * RPW * T * items_max;
 
     float acc[RPW][T];
@@ -568,10 +573,10 @@ __global__ __launch_bounds__(256) void k_dec_down(LayerView L, const DecodePlan*
             u32x4_t* hq4 = reinterpret_cast<u32x4_t*>(hq);
 #pragma unroll
             for (int b = 0; b < kHBatch; ++b) {
-                const int i = (int)threadIdx.x + 256 * b;
+                const int i = (int)threadIdx.x + kDownThreads * b;
                 if (i < n4) hq4[i] = hv0[b];
             }
-            for (int i = (int)threadIdx.x + 256 * kHBatch; i < n4; i += 256) hq[i] = hs[i];
+            for (int i = (int)threadIdx.x + kDownThreads * kHBatch; i < n4; i += kDownThreads) hq[i] = hs[i];
             __syncthreads();
         }
 #pragma unroll
@@ -696,7 +701,10 @@ static moe_status launch_gateup(const LayerView& L, const uint16_t* x, const flo
     const size_t sm = gateup_smem_bytes(T, L.H, L.E);
     auto kern = k_dec_gateup<FMT, T, ROUTE, KPL>;
     if (!allow_smem(kern, sm)) return MOE_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(kern, dim3((unsigned)((waves1 + 3) / 4)), dim3(256), sm, s, L, x, logits, ids, p, h, plan_g);
+    // waves per block chosen so that the blocks spread evenly over the 256 CUs (4..16 waves)
+    const int64_t wpb = std::min<int64_t>(16, std::max<int64_t>(4, (waves1 + 255) / 256));
+    hipLaunchKernelGGL(kern, dim3((unsigned)((waves1 + wpb - 1) / wpb)), dim3((unsigned)(wpb * kWave)), sm, s, L, x,
+                       logits, ids, p, h, plan_g);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
@@ -714,16 +722,16 @@ static moe_status launch_experts_t(const LayerView& L, const uint16_t* x, const 
     else st = launch_gateup<FMT, T, true, 16>(L, x, logits, ids, p, h, plan_g, s);
     if (st != MOE_OK) return st;
     const int items_max = down_items_max(L, T);
-    const int blocks = (L.H + 4 * kDownRows - 1) / (4 * kDownRows);
+    const int blocks = (L.H + kDownWaves * kDownRows - 1) / (kDownWaves * kDownRows);
     const bool combine = out != nullptr;
     const size_t sm = down_smem_bytes(T, L.k, L.E, L.Imax(), items_max, combine);
     if (combine) {
         if (!allow_smem(k_dec_down<FMT, T, true>, sm)) return MOE_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL((k_dec_down<FMT, T, true>), dim3(blocks), dim3(256), sm, s, L, plan_g, h, out, nullptr,
+        hipLaunchKernelGGL((k_dec_down<FMT, T, true>), dim3(blocks), dim3(kDownThreads), sm, s, L, plan_g, h, out, nullptr,
                            nullptr, items_max);
     } else {
         if (!allow_smem(k_dec_down<FMT, T, false>, sm)) return MOE_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL((k_dec_down<FMT, T, false>), dim3(blocks), dim3(256), sm, s, L, plan_g, h, nullptr,
+        hipLaunchKernelGGL((k_dec_down<FMT, T, false>), dim3(blocks), dim3(kDownThreads), sm, s, L, plan_g, h, nullptr,
                            y_pairs, y_shared, items_max);
     }
     MOE_LAUNCH_CHECK();

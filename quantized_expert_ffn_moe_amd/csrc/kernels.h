@@ -40,11 +40,14 @@ moe_status launch_decode_experts(const LayerView& L, const uint16_t* x, int T, c
 
 // prefill experts
 size_t prefill_scratch_bytes(const LayerView& L, int T);
+// y_sorted / y_shared: fp32 rows, or fp16 rows when y16 (the fused layer's internal buffers).
 moe_status launch_prefill_experts(const LayerView& L, const uint16_t* x, int T, const int32_t* offsets,
-                                  const int32_t* perm, float* y_sorted, float* y_shared, void* scratch,
+                                  const int32_t* perm, void* y_sorted, void* y_shared, bool y16, void* scratch,
                                   hipStream_t s);
 
 moe_status launch_combine(int T, int k, int H, const float* p, const float* y_rows, const int32_t* row_of_pair,
                           const float* y_shared, float* out, hipStream_t s);
+moe_status launch_combine_f16(int T, int k, int H, const float* p, const _Float16* y_rows,
+                              const int32_t* row_of_pair, const _Float16* y_shared, float* out, hipStream_t s);
 
 }  // namespace moe

@@ -215,13 +215,14 @@ struct StepSlot {
     uint32_t s0, s1;
 };
 
-template <int FMT, bool GATEUP>
+// YT: type of the down outputs (float, or _Float16 for the fused layer's internal rows).
+template <int FMT, bool GATEUP, typename YT = float>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm(LayerView L, int T, const TileDesc* __restrict__ tiles,
                                                          const int32_t* __restrict__ ntiles, int n_ntile,
                                                          const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ perm,
                                                          const _Float16* __restrict__ asrc, _Float16* __restrict__ h16,
-                                                         float* __restrict__ y_sorted, float* __restrict__ y_shared) {
+                                                         YT* __restrict__ y_sorted, YT* __restrict__ y_shared) {
     __shared__ __attribute__((aligned(16))) _Float16 As[2][kBM * kAS];
     constexpr int G = perm_group<FMT>();
     constexpr int BB = FMT == MOE_Q8_B32 ? 32 : FMT == MOE_Q4_B32 ? 16 : 8;   // bytes per block
@@ -418,8 +419,8 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(LayerView L, int T, con
                 for (int r = 0; r < 16; ++r) {
                     const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
                     if (row >= nrows) continue;
-                    if (shared) y_shared[(int64_t)(td.row0 + row) * H + m] = acc[i][j][r];
-                    else y_sorted[((int64_t)base + td.row0 + row) * H + m] = acc[i][j][r];
+                    if (shared) y_shared[(int64_t)(td.row0 + row) * H + m] = (YT)acc[i][j][r];
+                    else y_sorted[((int64_t)base + td.row0 + row) * H + m] = (YT)acc[i][j][r];
                 }
         }
     }
@@ -453,8 +454,8 @@ size_t prefill_scratch_bytes(const LayerView& L, int T) {
 
 template <int FMT>
 static moe_status launch_prefill_f(const LayerView& L, const uint16_t* x, int T, const int32_t* offsets,
-                                   const int32_t* perm, float* y_sorted, float* y_shared, const PrefillScratch& s,
-                                   hipStream_t st) {
+                                   const int32_t* perm, void* y_sorted, void* y_shared, bool y16,
+                                   const PrefillScratch& s, hipStream_t st) {
     constexpr int G = perm_group<FMT>();
     const int64_t n16 = (int64_t)T * L.H / 16;
     hipLaunchKernelGGL(k_x_to_f16<G>, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st, x, n16, s.x16);
@@ -463,27 +464,33 @@ static moe_status launch_prefill_f(const LayerView& L, const uint16_t* x, int T,
     const int nt1 = (L.Imax() + kBN / 2 - 1) / (kBN / 2);
     const int g1 = ((mt * nt1 + kXcds - 1) / kXcds) * kXcds;
     hipLaunchKernelGGL((k_grouped_gemm<FMT, true>), dim3(g1), dim3(256), 0, st, L, T, s.tiles, s.ntiles, nt1,
-                       offsets, perm, s.x16, s.h16, nullptr, nullptr);
+                       offsets, perm, s.x16, s.h16, (float*)nullptr, (float*)nullptr);
     MOE_LAUNCH_CHECK();
     const int nt2 = (L.H + kBN - 1) / kBN;
     const int g2 = ((mt * nt2 + kXcds - 1) / kXcds) * kXcds;
-    hipLaunchKernelGGL((k_grouped_gemm<FMT, false>), dim3(g2), dim3(256), 0, st, L, T, s.tiles, s.ntiles, nt2,
-                       offsets, perm, s.h16, nullptr, y_sorted, y_shared);
+    if (y16)
+        hipLaunchKernelGGL((k_grouped_gemm<FMT, false, _Float16>), dim3(g2), dim3(256), 0, st, L, T, s.tiles,
+                           s.ntiles, nt2, offsets, perm, s.h16, nullptr, static_cast<_Float16*>(y_sorted),
+                           static_cast<_Float16*>(y_shared));
+    else
+        hipLaunchKernelGGL((k_grouped_gemm<FMT, false, float>), dim3(g2), dim3(256), 0, st, L, T, s.tiles,
+                           s.ntiles, nt2, offsets, perm, s.h16, nullptr, static_cast<float*>(y_sorted),
+                           static_cast<float*>(y_shared));
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
 
 moe_status launch_prefill_experts(const LayerView& L, const uint16_t* x, int T, const int32_t* offsets,
-                                  const int32_t* perm, float* y_sorted, float* y_shared, void* scratch,
+                                  const int32_t* perm, void* y_sorted, void* y_shared, bool y16, void* scratch,
                                   hipStream_t st) {
     const PrefillScratch s = carve_prefill(L, T, scratch, nullptr);
     hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, st, offsets, L.E, T, L.k, L.Is > 0 ? 1 : 0,
                        max_tiles(T, L.k, L.E), s.tiles, s.ntiles);
     MOE_LAUNCH_CHECK();
     switch (L.fmt) {
-        case MOE_Q8_B32: return launch_prefill_f<MOE_Q8_B32>(L, x, T, offsets, perm, y_sorted, y_shared, s, st);
-        case MOE_Q4_B32: return launch_prefill_f<MOE_Q4_B32>(L, x, T, offsets, perm, y_sorted, y_shared, s, st);
-        case MOE_Q2_B32: return launch_prefill_f<MOE_Q2_B32>(L, x, T, offsets, perm, y_sorted, y_shared, s, st);
+        case MOE_Q8_B32: return launch_prefill_f<MOE_Q8_B32>(L, x, T, offsets, perm, y_sorted, y_shared, y16, s, st);
+        case MOE_Q4_B32: return launch_prefill_f<MOE_Q4_B32>(L, x, T, offsets, perm, y_sorted, y_shared, y16, s, st);
+        case MOE_Q2_B32: return launch_prefill_f<MOE_Q2_B32>(L, x, T, offsets, perm, y_sorted, y_shared, y16, s, st);
         default: return MOE_ERR_INVALID_ARG;
     }
 }

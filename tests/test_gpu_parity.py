@@ -420,6 +420,33 @@ def test_determinism():
         assert np.array_equal(u, v)
 
 
+def test_decode_layer_in_hip_graph():
+    """moe_layer captured in a HIP graph: every replay (with eager work and syncs in between) gives
+    the eager result bit for bit (the graph holds no memset nodes)."""
+    _need_gpu()
+    spec, d = host_layer("decode1")
+    L = dev_layer(spec, d)
+    x = dev_x(d["x"])
+    ws = moe.Workspace()
+    out = torch.empty((spec.T, spec.H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((spec.T, spec.k), dtype=torch.int32, device="cuda")
+    moe.moe_layer(L, x, out=out, ids=ids, ws=ws)
+    torch.cuda.synchronize()
+    want_out, want_ids = out.clone(), ids.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_layer(L, x, out=out, ids=ids, ws=ws)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        ids.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ids, want_ids), rep
+        assert torch.equal(out, want_out), rep
+        moe.moe_layer(L, x, out=torch.empty_like(out), ws=moe.Workspace())   # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_error_statuses_on_gpu():
     _need_gpu()
     spec, d = host_layer("tiny")
