@@ -71,6 +71,10 @@ def load(path: str):
     L.orc_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
     L.orc_dense_masked.restype = ctypes.c_int
     L.orc_dense_masked.argtypes = [ctypes.POINTER(_Layer), vp, i32, vp]
+    L.orc_f32_to_f16.restype = ctypes.c_uint16
+    L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+    L.orc_kv_encode.argtypes = [vp, i32, i32, vp, vp]
+    L.orc_kv_gather.argtypes = [vp, vp, i32, i32, vp, i32, vp]
     return L
 
 
@@ -230,3 +234,29 @@ def expert_ffn(fmt, H, I, gate, up, down, x):
     y = np.empty(H)
     lib().orc_expert(fmt, H, I, _p(g[0]), _p(g[1]), _p(u[0]), _p(u[1]), _p(d[0]), _p(d[1]), _p(xd), _p(h), _p(y))
     return h, y
+
+
+def f32_to_f16(q: float) -> int:
+    """fp32 value -> fp16 bits, round to nearest even (the KV codec's scale rounding)."""
+    return int(lib().orc_f32_to_f16(float(q)))
+
+
+def kv_encode(src_bf16: np.ndarray):
+    """bf16 bits [rows][D] -> (int8 codes [rows][D], fp16 scale bits [rows][D/32])."""
+    x = np.ascontiguousarray(src_bf16, np.uint16)
+    rows, D = x.shape
+    assert D % 32 == 0
+    codes = np.empty((rows, D), np.int8)
+    scales = np.empty((rows, D // 32), np.uint16)
+    lib().orc_kv_encode(_p(x), rows, D, _p(codes), _p(scales))
+    return codes, scales
+
+
+def kv_gather(codes: np.ndarray, scales: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Dequantised rows idx of the int8 cache (fp64; rows outside the cache give zeros)."""
+    c = np.ascontiguousarray(codes, np.int8)
+    s = np.ascontiguousarray(scales, np.uint16)
+    i = np.ascontiguousarray(idx, np.int32).ravel()
+    out = np.empty((len(i), c.shape[1]), np.float64)
+    lib().orc_kv_gather(_p(c), _p(s), c.shape[0], c.shape[1], _p(i), len(i), _p(out))
+    return out

@@ -317,3 +317,71 @@ int orc_dense_masked(const orc_layer* L, const uint16_t* x, int32_t T, double* Y
     free(xd); free(l); free(soft); free(m); free(y);
     return 0;
 }
+
+/* ------------------------------------------------------------------ KV cache codec */
+
+/* fp32 -> fp16 bits, round to nearest, ties to even, from the definition: for |q| in
+ * [2^e, 2^(e+1)) with e >= -14 the fp16 step is 2^(e-10) (below 2^-14 it is 2^-24), so the
+ * result is the nearest multiple of that step (ties to the even multiple); 65520 and above
+ * overflow to infinity. q / step is exact in double, nearbyint rounds it in the default mode. */
+uint16_t orc_f32_to_f16(float q) {
+    double a = fabs((double)q);
+    uint16_t sign = (signbit(q) ? 0x8000u : 0u);
+    if (isnan(q)) return (uint16_t)(sign | 0x7E00u);
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+    if (a == 0.0) return sign;
+    int e = (int)floor(log2(a));
+    if (ldexp(1.0, e) > a) e -= 1;          /* guard against log2 rounding */
+    if (ldexp(1.0, e + 1) <= a) e += 1;
+    if (e < -14) e = -14;                   /* subnormal range: fixed step 2^-24 */
+    double step = ldexp(1.0, e - 10);
+    double m = nearbyint(a / step);         /* multiple of the step */
+    double r = m * step;
+    /* encode r: normal if r >= 2^-14 */
+    if (r >= ldexp(1.0, -14)) {
+        int er = (int)floor(log2(r));
+        if (ldexp(1.0, er) > r) er -= 1;
+        if (ldexp(1.0, er + 1) <= r) er += 1;
+        if (er > 15) return (uint16_t)(sign | 0x7C00u);
+        uint16_t frac = (uint16_t)(r / ldexp(1.0, er - 10) - 1024.0);
+        return (uint16_t)(sign | ((uint16_t)(er + 15) << 10) | frac);
+    }
+    return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+}
+
+void orc_kv_encode(const uint16_t* src, int32_t rows, int32_t D, int8_t* codes, uint16_t* scales) {
+    for (int32_t r = 0; r < rows; ++r)
+        for (int32_t b = 0; b < D / 32; ++b) {
+            const uint16_t* v = src + (int64_t)r * D + 32 * b;
+            float m = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf((float)orc_bf16(v[i]));   /* bf16 values are exact in fp32 */
+                if (a > m) m = a;
+            }
+            float q = m / 127.0f;
+            uint16_t sb = orc_f32_to_f16(q);
+            float sf = (float)orc_f16(sb);
+            scales[(int64_t)r * (D / 32) + b] = sb;
+            for (int i = 0; i < 32; ++i) {
+                int c = 0;
+                if (sf != 0.0f) {
+                    float t = rintf((float)orc_bf16(v[i]) / sf);
+                    c = t > 127.0f ? 127 : t < -127.0f ? -127 : (int)t;
+                }
+                codes[(int64_t)r * D + 32 * b + i] = (int8_t)c;
+            }
+        }
+}
+
+void orc_kv_gather(const int8_t* codes, const uint16_t* scales, int32_t n_rows, int32_t D, const int32_t* idx,
+                   int32_t n_idx, double* out) {
+    for (int32_t j = 0; j < n_idx; ++j) {
+        int32_t r = idx[j];
+        for (int32_t d = 0; d < D; ++d) {
+            double v = 0.0;
+            if (r >= 0 && r < n_rows)
+                v = (double)codes[(int64_t)r * D + d] * orc_f16(scales[(int64_t)r * (D / 32) + d / 32]);
+            out[(int64_t)j * D + d] = v;
+        }
+    }
+}

@@ -110,7 +110,7 @@ def golden_layer(g):
     return L, xb
 
 
-GOLDEN_FILES = sorted(glob.glob(os.path.join(GOLDEN, "*.json")))
+GOLDEN_FILES = sorted(f for f in glob.glob(os.path.join(GOLDEN, "*.json")) if not os.path.basename(f).startswith("kv_"))
 
 
 # ---------------------------------------------------------------- pins
@@ -333,6 +333,107 @@ def pin_combine_alone():
                                atol=1e-14)
 
 
+# ------------------------------------------------------------------------- KV int8 block codec
+
+def pin_kv_f16_rounding():
+    """The codec's fp32 -> fp16 rounding against numpy's IEEE conversion (round to nearest even):
+    random bit patterns over the whole fp32 range, the subnormal range, ties and the overflow edge."""
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 1 << 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    edge = np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+                     2.0 ** -14, 2.0 ** -14 * (1 - 2 ** -11), 1 + 2 ** -11, 1 + 3 * 2 ** -11, 1 / 127,
+                     7.0e-9, 1.0e-7], np.float32)
+    small = (rng.standard_normal(5000) * 1e-5).astype(np.float32)
+    for v in np.concatenate([vals, edge, small]):
+        want = int(np.float32(v).astype(np.float16).view(np.uint16))
+        assert oracle.f32_to_f16(float(v)) == want, (float(v), hex(want))
+
+
+def pin_kv_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "kv_b32_example.json")))
+    src = np.array(g["src_bf16"], np.uint16)
+    codes, scales = oracle.kv_encode(src)
+    assert scales.tolist() == g["expect_scales"]
+    assert codes[0, :4].tolist() == g["expect_codes_block0_head"]
+    assert np.all(codes[0, 4:] == 0)
+    out = oracle.kv_gather(codes, scales, np.array([0]))
+    assert out[0, :4].tolist() == g["expect_dequant_block0_head"]
+    assert np.all(out[0, 4:] == 0.0)
+
+
+def _bf16_rows(rng, rows, D, sigma=1.0):
+    v = (rng.standard_normal((rows, D)) * sigma).astype(np.float32)
+    return (v.view(np.uint32) >> 16).astype(np.uint16)   # truncation is fine: any bf16 is a valid input
+
+
+def pin_kv_round_trip():
+    """|v - code * s| <= s / 2 (rounding to the nearest level; no clamping happens because
+    s >= m / 127 up to fp16 rounding), codes within [-127, 127], the block maximum maps to +-127
+    (or +-126/128 within one fp16 rounding of s)."""
+    rng = np.random.default_rng(6)
+    for sigma in (1e-3, 1.0, 300.0):
+        src = _bf16_rows(rng, 40, 256, sigma)
+        codes, scales = oracle.kv_encode(src)
+        deq = oracle.kv_gather(codes, scales, np.arange(40))
+        v = oracle.bf16_to_f64(src)
+        s = np.repeat(oracle.f16_to_f64(scales), 32, axis=1)
+        assert np.all(np.abs(codes.astype(int)) <= 127)
+        assert np.all(np.abs(v - deq) <= 0.5 * s * (1 + 2.0 ** -20) + 1e-300)
+        blockmax = np.abs(codes.astype(int)).reshape(40, -1, 32).max(axis=2)
+        assert np.all(blockmax >= 126)
+
+
+def pin_kv_symmetry():
+    """encode(-v) = (-codes, same scale); encode(2^j v) = (same codes, scale * 2^j) away from the
+    fp16 subnormal and overflow ranges."""
+    rng = np.random.default_rng(7)
+    src = _bf16_rows(rng, 16, 128)
+    c, s = oracle.kv_encode(src)
+    cn, sn = oracle.kv_encode(src ^ np.uint16(0x8000))
+    assert np.array_equal(sn, s) and np.array_equal(cn, -c)
+    for j in (-3, 4):
+        scaled = src.copy()
+        e = ((scaled >> 7) & 0xFF).astype(int)
+        nz = e != 0
+        scaled[nz] = ((scaled[nz].astype(int) & ~(0xFF << 7)) | ((e[nz] + j) << 7)).astype(np.uint16)
+        c2, s2 = oracle.kv_encode(scaled)
+        assert np.array_equal(c2, c)
+        assert np.allclose(oracle.f16_to_f64(s2), oracle.f16_to_f64(s) * 2.0 ** j, rtol=0, atol=0)
+
+
+def pin_kv_gather():
+    rng = np.random.default_rng(8)
+    src = _bf16_rows(rng, 50, 96)
+    codes, scales = oracle.kv_encode(src)
+    full = np.array([[codes[r, d] * oracle.f16_to_f64(np.array([scales[r, d // 32]], np.uint16))[0]
+                      for d in range(96)] for r in range(50)])
+    idx = np.array([3, 3, 49, 0, -1, 50, 1 << 30, 17])
+    out = oracle.kv_gather(codes, scales, idx)
+    for j, r in enumerate(idx):
+        if 0 <= r < 50:
+            assert np.array_equal(out[j], full[r])
+        else:
+            assert np.all(out[j] == 0.0)
+
+
+def pin_kv_ties_to_even():
+    """s = 2^-7 exactly (m = 127 * 2^-7), so v / s = 2.5, 3.5, 1.5, -2.5 are exact ties: the code
+    rounding is to nearest, ties to even (2, 4, 2, -2), not away from zero."""
+    vals = np.zeros((1, 32), np.float32)
+    vals[0, :5] = [127 * 2.0 ** -7, 2.5 * 2.0 ** -7, 3.5 * 2.0 ** -7, 1.5 * 2.0 ** -7, -2.5 * 2.0 ** -7]
+    src = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.bf16_to_f64(src)[0, :5], vals[0, :5].astype(np.float64))
+    codes, scales = oracle.kv_encode(src)
+    assert oracle.f16_to_f64(scales)[0, 0] == 2.0 ** -7
+    assert codes[0, :5].tolist() == [127, 2, 4, 2, -2]
+
+
+KV_PINS = [("kv_f16_rounding", pin_kv_f16_rounding), ("kv_worked_example", pin_kv_worked_example),
+           ("kv_round_trip", pin_kv_round_trip), ("kv_symmetry", pin_kv_symmetry), ("kv_gather", pin_kv_gather),
+           ("kv_ties_to_even", pin_kv_ties_to_even)]
+
 ALL_PINS = (
     [("golden:" + os.path.basename(f), (lambda f=f: pin_golden(f))) for f in GOLDEN_FILES]
     + [("f16_reader", pin_f16_reader), ("bf16_reader", pin_bf16_reader), ("levels", pin_levels_exhaustive)]
@@ -343,6 +444,7 @@ ALL_PINS = (
     + [("dense_masked:" + synth.FMT_NAMES[f], (lambda f=f: pin_dense_masked(f))) for f in (synth.Q8, synth.Q4, synth.Q2)]
     + [("full_mixture", pin_full_mixture), ("k1_single_ffn", pin_k1_single_ffn), ("relabel", pin_relabel),
        ("scale_down", pin_scale_down), ("logits_override", pin_logits_override), ("combine_alone", pin_combine_alone)]
+    + KV_PINS
 )
 
 
@@ -367,3 +469,5 @@ def test_golden_closed_forms():
     assert byname["w1b_q8_tie.json"]["expect_Y"]["1"] == pytest.approx(0.5 * sig(1), rel=1e-15)
     assert byname["w2_q2_top1.json"]["expect_Y_all"] == pytest.approx(-27 * sig(3), rel=1e-15)
     assert byname["w3_q4_k2_shared.json"]["expect_Y"]["0"] == pytest.approx(0.5 * sig(1) + 3.5 * sig(7), rel=1e-15)
+
+
