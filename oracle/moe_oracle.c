@@ -360,6 +360,7 @@ void orc_kv_encode(const uint16_t* src, int32_t rows, int32_t D, int8_t* codes, 
             }
             float q = m / 127.0f;
             uint16_t sb = orc_f32_to_f16(q);
+            if (sb == 0x7C00u) sb = 0x7BFFu;   /* scale saturates at the largest finite fp16, 65504 */
             float sf = (float)orc_f16(sb);
             scales[(int64_t)r * (D / 32) + b] = sb;
             for (int i = 0; i < 32; ++i) {

@@ -83,9 +83,9 @@ int orc_dense_masked(const orc_layer* L, const uint16_t* x, int32_t T, double* Y
  * KV cache codec (648news "nano-cuda-moe" article, section on the VRAM/RAM memory hierarchy: the
  * KV cache is int8 with one scale per 32 values, and an indexer picks 2048 positions per query).
  * A row of D values (D a multiple of 32) is cut into blocks of 32; per block, in fp32 as the
- * device does it: m = max |v|, s = fp16(m / 127) (round to nearest even), code = rne(v / s)
- * clamped to [-127, 127], or 0 when s is 0. The quantisation decision is taken in fp32 on both
- * sides (the pages fix no precision for it).
+ * device does it: m = max |v|, s = fp16(m / 127) (round to nearest even; a result beyond the fp16
+ * range saturates at 65504), code = rne(v / s) clamped to [-127, 127], or 0 when s is 0. The
+ * quantisation decision is taken in fp32 on both sides (the pages fix no precision for it).
  *   src bf16 [rows][D] -> codes int8 [rows][D], scales fp16 bits [rows][D/32]
  */
 uint16_t orc_f32_to_f16(float q);

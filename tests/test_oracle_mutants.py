@@ -32,6 +32,7 @@ MUTANTS = {
     "permutation_unstable": ("int32_t pos = offsets[e] + seen[e];", "int32_t pos = offsets[e + 1] - 1 - seen[e];"),
     "combine_alone_row_map": ("int64_t r = row_of_pair ? row_of_pair[q] : q;", "int64_t r = q;"),
     "kv_scale_divisor": ("float q = m / 127.0f;", "float q = m / 128.0f;"),
+    "kv_scale_overflow": ("if (sb == 0x7C00u) sb = 0x7BFFu;", ";"),
     "kv_ties_away": ("float t = rintf((float)orc_bf16(v[i]) / sf);", "float t = roundf((float)orc_bf16(v[i]) / sf);"),
     "kv_f16_truncation": ("double m = nearbyint(a / step);", "double m = floor(a / step);"),
     "kv_gather_block_index": ("orc_f16(scales[(int64_t)r * (D / 32) + d / 32])", "orc_f16(scales[(int64_t)r * (D / 32) + d % (D / 32)])"),

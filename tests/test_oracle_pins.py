@@ -430,7 +430,21 @@ def pin_kv_ties_to_even():
     assert codes[0, :5].tolist() == [127, 2, 4, 2, -2]
 
 
-KV_PINS = [("kv_f16_rounding", pin_kv_f16_rounding), ("kv_worked_example", pin_kv_worked_example),
+def pin_kv_scale_saturates():
+    """A block maximum beyond 127 * 65504 would need an fp16 scale past the range: the scale
+    saturates at 65504 (0x7BFF) and the codes clamp at +-127, so no code times the scale is NaN."""
+    vals = np.zeros((1, 32), np.float32)
+    vals[0, :3] = [1.0e7, -2.0e7, 65504.0 * 3]
+    src = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    codes, scales = oracle.kv_encode(src)
+    assert int(scales[0, 0]) == 0x7BFF
+    v = oracle.bf16_to_f64(src)[0, :3]
+    assert codes[0, :3].tolist() == [127, -127, 3]
+    assert np.all(np.isfinite(oracle.kv_gather(codes, scales, np.array([0]))))
+    assert abs(v[2] - 3 * 65504.0) < 0.5 * 65504.0   # the truncated bf16 input still rounds to code 3
+
+
+KV_PINS = [("kv_scale_saturates", pin_kv_scale_saturates), ("kv_f16_rounding", pin_kv_f16_rounding), ("kv_worked_example", pin_kv_worked_example),
            ("kv_round_trip", pin_kv_round_trip), ("kv_symmetry", pin_kv_symmetry), ("kv_gather", pin_kv_gather),
            ("kv_ties_to_even", pin_kv_ties_to_even)]
 
