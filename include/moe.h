@@ -186,6 +186,29 @@ moe_status moe_layer(const moe_layer_desc* desc, const moe_layer_weights* w, con
                      float* out, float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes,
                      void* stream);
 
+/*
+ * KV cache codec: the same block-32 int8 format as the Q8 weights, for the attention cache (648news
+ * 07-nano-cuda-moe-qwen38-release, section "memory hierarchy spanning VRAM and RAM": the KV cache is
+ * int8 with one scale per 32 values, and an indexer selects 2048 positions per query). Per block of
+ * 32 values of a row, in fp32: m = max |v|, s = fp16(m / 127) rounded to nearest even and
+ * saturating at 65504, code = rne(v / s) clamped to [-127, 127], or 0 when s is 0 (codes of NaN
+ * inputs are unspecified).
+ *   src bf16 [rows][D] -> codes int8 [rows][D], scales fp16 bits [rows][D/32]
+ * D a multiple of 32, 32 <= D <= 65536; rows >= 0 (0 enqueues nothing). src and codes 16-byte
+ * aligned, scales 2-byte aligned. No workspace.
+ */
+moe_status moe_kv_encode(const uint16_t* src, int32_t rows, int32_t D, int8_t* codes, uint16_t* scales,
+                         void* stream);
+
+/*
+ * Sparse gather from the int8 cache of n_rows rows: out[j][d] = codes[idx[j]][d] * s(idx[j], d / 32)
+ * in fp32 (exact: an int8 times an fp16 fits fp32), for j < n_idx; an index outside [0, n_rows)
+ * yields a zero row (no access with it). idx int32 [n_idx] on the device, e.g. the 2048 positions
+ * of each of several queries; out fp32 [n_idx][D], 16-byte aligned. No workspace.
+ */
+moe_status moe_kv_gather(const int8_t* codes, const uint16_t* scales, int32_t n_rows, int32_t D,
+                         const int32_t* idx, int32_t n_idx, float* out, void* stream);
+
 /* Bytes of workspace an entry point needs for this shape (host only; no GPU work). */
 moe_status moe_workspace_size(const moe_layer_desc* desc, int32_t T, moe_call call, size_t* bytes);
 

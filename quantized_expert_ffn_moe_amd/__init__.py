@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "MoeError", "LayerDesc", "DeviceLayer", "Workspace", "lib", "library_path",
     "moe_route", "moe_permute", "moe_experts_decode", "moe_experts_prefill", "moe_combine", "moe_layer",
+    "moe_kv_encode", "moe_kv_gather",
     "moe_workspace_size", "moe_status_string", "moe_abi_version",
     "MOE_Q8_B32", "MOE_Q4_B32", "MOE_Q2_B32",
     "MOE_CALL_ROUTE", "MOE_CALL_PERMUTE", "MOE_CALL_EXPERTS_DECODE", "MOE_CALL_EXPERTS_PREFILL",
@@ -74,6 +75,10 @@ def lib():
         L.moe_permute.argtypes = [D, vp, i32, vp, vp, vp, vp, sz, vp]
         L.moe_experts_decode.restype = st
         L.moe_experts_decode.argtypes = [D, W, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.moe_kv_encode.restype = st
+        L.moe_kv_encode.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_kv_gather.restype = st
+        L.moe_kv_gather.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp]
         L.moe_experts_prefill.restype = st
         L.moe_experts_prefill.argtypes = [D, W, vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_combine.restype = st
@@ -269,4 +274,26 @@ def moe_layer(layer: DeviceLayer, x, out=None, logits=None, ids=None, p=None, ws
     buf, nb = _ws(d, T, MOE_CALL_LAYER, ws)
     _check(lib().moe_layer(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(out), _ptr(logits),
                            _ptr(ids), _ptr(p), _ptr(buf), nb, _stream(stream)), "moe_layer")
+    return out
+
+
+def moe_kv_encode(src, codes=None, scales=None, stream=None):
+    """bf16 rows [rows][D] (torch bf16 or int16 bits) -> (int8 codes [rows][D], fp16 scale bits as
+    int16 [rows][D/32])."""
+    bits = _x_bits(src)
+    rows, D = bits.shape
+    dev = bits.device
+    codes = torch.empty((rows, D), dtype=torch.int8, device=dev) if codes is None else codes
+    scales = torch.empty((rows, D // 32), dtype=torch.int16, device=dev) if scales is None else scales
+    _check(lib().moe_kv_encode(_ptr(bits), rows, D, _ptr(codes), _ptr(scales), _stream(stream)), "moe_kv_encode")
+    return codes, scales
+
+
+def moe_kv_gather(codes, scales, idx, out=None, stream=None):
+    """Dequantised rows idx of the int8 cache as fp32 [n_idx][D] (rows outside the cache are 0)."""
+    n_rows, D = codes.shape
+    n_idx = idx.numel()
+    out = torch.empty((n_idx, D), dtype=torch.float32, device=codes.device) if out is None else out
+    _check(lib().moe_kv_gather(_ptr(codes), _ptr(scales), n_rows, D, _ptr(idx), n_idx, _ptr(out), _stream(stream)),
+           "moe_kv_gather")
     return out

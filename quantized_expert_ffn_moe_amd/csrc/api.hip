@@ -257,6 +257,25 @@ moe_status moe_combine(const moe_layer_desc* d, int32_t T, const float* p, const
     return launch_combine(T, d->top_k, d->hidden, p, y_rows, row_of_pair, y_shared, out, (hipStream_t)stream);
 }
 
+moe_status moe_kv_encode(const uint16_t* src, int32_t rows, int32_t D, int8_t* codes, uint16_t* scales,
+                         void* stream) {
+    if (rows < 0 || D < 32 || D > 65536 || D % 32 != 0) return MOE_ERR_INVALID_ARG;
+    if (rows == 0) return MOE_OK;
+    if (!src || !codes || !scales || !aligned16(src) || !aligned16(codes) || ((uintptr_t)scales & 1u))
+        return MOE_ERR_INVALID_ARG;
+    return launch_kv_encode(src, rows, D, codes, scales, (hipStream_t)stream);
+}
+
+moe_status moe_kv_gather(const int8_t* codes, const uint16_t* scales, int32_t n_rows, int32_t D, const int32_t* idx,
+                         int32_t n_idx, float* out, void* stream) {
+    if (n_rows < 0 || n_idx < 0 || D < 32 || D > 65536 || D % 32 != 0) return MOE_ERR_INVALID_ARG;
+    if (n_idx == 0) return MOE_OK;
+    if (!idx || !out || ((uintptr_t)idx & 3u) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+    if (n_rows > 0 && (!codes || !scales || !aligned16(codes) || ((uintptr_t)scales & 1u)))
+        return MOE_ERR_INVALID_ARG;
+    return launch_kv_gather(codes, scales, n_rows, D, idx, n_idx, out, (hipStream_t)stream);
+}
+
 moe_status moe_layer(const moe_layer_desc* d, const moe_layer_weights* w, const uint16_t* x, int32_t T, float* out,
                      float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes, void* stream) {
     MOE_TRY(check_desc(d));

@@ -50,4 +50,10 @@ moe_status launch_combine(int T, int k, int H, const float* p, const float* y_ro
 moe_status launch_combine_f16(int T, int k, int H, const float* p, const _Float16* y_rows,
                               const int32_t* row_of_pair, const _Float16* y_shared, float* out, hipStream_t s);
 
+// KV cache codec
+moe_status launch_kv_encode(const uint16_t* src, int32_t rows, int32_t D, int8_t* codes, uint16_t* scales,
+                            hipStream_t s);
+moe_status launch_kv_gather(const int8_t* codes, const uint16_t* scales, int32_t n_rows, int32_t D,
+                            const int32_t* idx, int32_t n_idx, float* out, hipStream_t s);
+
 }  // namespace moe

@@ -28,7 +28,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"moe_route", "moe_permute", "moe_experts_decode", "moe_experts_prefill", "moe_combine", "moe_layer",
-            "moe_workspace_size", "moe_status_string", "moe_abi_version"} <= set(names)
+            "moe_workspace_size", "moe_status_string", "moe_abi_version", "moe_kv_encode", "moe_kv_gather"} <= set(names)
     L = ctypes.CDLL(moe.library_path)
     for n in names:
         assert hasattr(L, n), n
@@ -102,6 +102,18 @@ def test_host_validation_rejects_before_launch():
     # prefill with a shared expert but no y_shared
     assert _raw("moe_experts_prefill", ref(d.c), ref(w), fake, 8, fake, fake, fake, None, fake, 1 << 40, None) == \
         moe.MOE_ERR_INVALID_ARG
+
+
+def test_kv_validation_rejects_before_launch():
+    fake = 0x10000
+    assert _raw("moe_kv_encode", fake, 4, 48, fake, fake, None) == moe.MOE_ERR_INVALID_ARG        # D % 32
+    assert _raw("moe_kv_encode", fake, -1, 64, fake, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert _raw("moe_kv_encode", fake + 2, 4, 64, fake, fake, None) == moe.MOE_ERR_INVALID_ARG    # src align
+    assert _raw("moe_kv_encode", None, 0, 64, None, None, None) == moe.MOE_OK                     # nothing to do
+    assert _raw("moe_kv_gather", fake, fake, 10, 64, fake + 2, 8, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert _raw("moe_kv_gather", fake, fake, 10, 64, fake, 8, fake + 4, None) == moe.MOE_ERR_INVALID_ARG
+    assert _raw("moe_kv_gather", fake, fake, 10, 64, fake, -3, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert _raw("moe_kv_gather", None, None, 10, 64, None, 0, None, None) == moe.MOE_OK
 
 
 def test_binding_refuses_host_tensors():

@@ -447,6 +447,86 @@ def test_decode_layer_in_hip_graph():
         torch.cuda.synchronize()
 
 
+# ------------------------------------------------------------------------- KV int8 codec
+
+def _kv_rows(rng, rows, D):
+    """bf16 rows mixing the cases the codec must get right: normal blocks, all-zero blocks, blocks
+    whose scale is subnormal or rounds to 0, blocks near the fp16 scale overflow, signed zeros."""
+    v = rng.standard_normal((rows, D)).astype(np.float32)
+    nb = D // 32
+    kind = rng.integers(0, 8, size=(rows, nb))
+    for r in range(rows):
+        for b in range(nb):
+            blk = v[r, 32 * b:32 * b + 32]
+            if kind[r, b] == 0:
+                blk[:] = 0.0
+            elif kind[r, b] == 1:
+                blk *= 1e-6                  # scale subnormal in fp16
+            elif kind[r, b] == 2:
+                blk *= 1e-9                  # scale rounds to 0
+            elif kind[r, b] == 3:
+                blk *= 5e6                   # scale near / above the fp16 range
+            elif kind[r, b] == 4:
+                blk[::3] = -0.0
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_kv_encode_bit_exact():
+    _need_gpu()
+    rng = np.random.default_rng(21)
+    src = _kv_rows(rng, 300, 512)
+    say("kv encode 300 x 512")
+    codes, scales = moe.moe_kv_encode(dev_x(src))
+    torch.cuda.synchronize()
+    o_codes, o_scales = oracle.kv_encode(src)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), o_scales)
+    assert np.array_equal(codes.cpu().numpy(), o_codes)
+
+
+def test_kv_gather_exact():
+    _need_gpu()
+    rng = np.random.default_rng(22)
+    n_rows, D = 4096, 256
+    src = _kv_rows(rng, n_rows, D)
+    o_codes, o_scales = oracle.kv_encode(src)
+    codes = torch.from_numpy(o_codes).cuda()
+    scales = torch.from_numpy(o_scales.view(np.int16)).cuda()
+    idx = rng.integers(0, n_rows, size=2048 * 3).astype(np.int32)
+    idx[:5] = [0, n_rows - 1, -1, n_rows, 1 << 30]    # edges and out-of-range rows
+    idx[5:9] = 17                                      # repeats
+    say("kv gather %d rows of %d" % (len(idx), n_rows))
+    out = moe.moe_kv_gather(codes, scales, torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    want = oracle.kv_gather(o_codes, o_scales, idx)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert np.array_equal(got, want)
+
+
+def test_kv_full_size_sampled():
+    """Cache of 131072 positions x 512 (the size the benchmark gathers from): GPU encode of every
+    row, checked bit for bit on 256 sampled rows; gather of 16 x 2048 positions checked exactly."""
+    _need_gpu()
+    rng = np.random.default_rng(23)
+    n_rows, D = 131072, 512
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.randn((n_rows, D), generator=g, device="cuda").to(torch.bfloat16)
+    say("kv full size encode %d x %d" % (n_rows, D))
+    codes, scales = moe.moe_kv_encode(x)
+    idx = torch.from_numpy(rng.integers(0, n_rows, size=16 * 2048).astype(np.int32)).cuda()
+    out = moe.moe_kv_gather(codes, scales, idx)
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(n_rows, 256, replace=False))
+    xs = x[torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
+    o_codes, o_scales = oracle.kv_encode(xs)
+    assert np.array_equal(codes[torch.from_numpy(rows).cuda()].cpu().numpy(), o_codes)
+    assert np.array_equal(scales[torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16), o_scales)
+    pick = rng.choice(len(idx), 512, replace=False)
+    ii = idx.cpu().numpy()[pick]
+    want = oracle.kv_gather(codes.cpu().numpy(), scales.cpu().numpy().view(np.uint16), ii)
+    assert np.array_equal(out.cpu().numpy()[pick].astype(np.float64), want)
+
+
 def test_error_statuses_on_gpu():
     _need_gpu()
     spec, d = host_layer("tiny")
