@@ -258,6 +258,66 @@ def prefill_workload(steps: int, warmup: int):
                        "format": synth.FMT_NAMES[spec.fmt]}}
 
 
+def kv_workload(reps: int = 20):
+    """The int8 block-32 KV codec on a cache of 131072 positions x 512 values (bf16 in): encode of
+    the whole cache, and the sparse gather of 16 queries x 2048 positions (exact fp32 rows out).
+    Both are HBM streams: bytes moved per launch over the HIP-event-timed duration."""
+    n_rows, D, n_idx = 131072, 512, 16 * 2048
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn((n_rows, D), generator=g, device="cuda").to(torch.bfloat16)
+    codes = torch.empty((n_rows, D), dtype=torch.int8, device="cuda")
+    scales = torch.empty((n_rows, D // 32), dtype=torch.int16, device="cuda")
+    idx = torch.randint(0, n_rows, (n_idx,), generator=g, device="cuda", dtype=torch.int32)
+    out = torch.empty((n_idx, D), dtype=torch.float32, device="cuda")
+    enc_ms = time_calls([lambda: moe.moe_kv_encode(x, codes, scales)], 3, reps)
+    gat_ms = time_calls([lambda: moe.moe_kv_gather(codes, scales, idx, out=out)], 3, reps)
+    enc_bytes = n_rows * D * 2 + n_rows * D + n_rows * (D // 32) * 2
+    gat_bytes = n_idx * 4 + n_idx * D + n_idx * (D // 32) * 2 + n_idx * D * 4
+
+    def roof(nbytes, ms, kernel):
+        a = nbytes / (ms / 1e3) / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel,
+                "bytes_per_launch": int(nbytes), "avg_launch_us": round(ms * 1e3, 2)}
+    return {"workload": "int8 block-32 KV cache, 131072 positions x 512, gather 16 x 2048 positions",
+            "encode": roof(enc_bytes, enc_ms, "k_kv_encode"), "gather": roof(gat_bytes, gat_ms, "k_kv_gather")}
+
+
+def sweep_tokens(reps: int = 10):
+    """Mid-size batches: moe_layer time per call for T = 1 .. 8192 tokens on the prefill8k layer
+    (hidden 2048, 256 experts top-8 + shared, 4-bit), with the path moe_layer takes at each T
+    (decode kernels for T <= 4, the grouped-GEMM path above), and the grouped-GEMM path forced
+    through the separate entry points at T <= 4 for the crossover."""
+    spec = synth.CONFIGS["prefill8k"]
+    d = synth.make_layer(spec)
+    L = upload(spec, d)
+    xs_all = dev_x(d["x"])
+    rows = []
+    for T in [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192]:
+        x = xs_all[:T].contiguous()
+        ws = moe.Workspace()
+        out = torch.empty((T, spec.H), dtype=torch.float32, device="cuda")
+        ms = time_calls([lambda: moe.moe_layer(L, x, out=out, ws=ws)], 2, reps)
+        row = {"T": T, "path": "decode" if T <= 4 else "grouped_gemm", "us_per_call": round(ms * 1e3, 2),
+               "tokens_per_s": round(T / (ms / 1e3), 1)}
+        if T <= 4:
+            lg = torch.empty((T, spec.E), dtype=torch.float32, device="cuda")
+            w1, w2, w3, w4 = moe.Workspace(), moe.Workspace(), moe.Workspace(), moe.Workspace()
+            ys = torch.empty((T * spec.k, spec.H), dtype=torch.float32, device="cuda")
+            ysh = torch.empty((T, spec.H), dtype=torch.float32, device="cuda")
+
+            def forced():
+                _, ids, p = moe.moe_route(L, x, logits=lg, ws=w1)
+                off, perm, inv = moe.moe_permute(L, ids, ws=w2)
+                moe.moe_experts_prefill(L, x, off, perm, y_sorted=ys, y_shared=ysh, ws=w3)
+                moe.moe_combine(L, p, ys, inv, ysh, out=out)
+            ms2 = time_calls([forced], 2, reps)
+            row["grouped_gemm_us_per_call"] = round(ms2 * 1e3, 2)
+        rows.append(row)
+        log("T=%d: %s" % (T, row))
+    return rows
+
+
 def cpu_baseline(name: str, budget_s: float = 12.0):
     """The fp64 oracle (single thread) on a bounded sample of the workload's tokens."""
     import oracle
@@ -286,8 +346,11 @@ def main():
     ap.add_argument("--workload", default="decode1", choices=["decode1", "verify4", "stack48", "prefill8k"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary 8K prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kv", action="store_true", help="skip the secondary KV-codec measurement")
     ap.add_argument("--eager", action="store_true",
                     help="launch every decode call from Python instead of replaying one captured HIP graph per step")
+    ap.add_argument("--sweep-tokens", action="store_true",
+                    help="print moe_layer time per call for T = 1 .. 8192 (mid-size batches) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 256 MiB device-to-device 3 times (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -301,6 +364,10 @@ def main():
     moe.lib()
     if args.calibrate_copy:
         calibrate_copy()
+    if args.sweep_tokens:
+        print(json.dumps({"sweep": "moe_layer time per call vs tokens per call", "layer": "prefill8k shape",
+                          "rows": sweep_tokens()}), flush=True)
+        return
 
     if args.workload == "prefill8k":
         r = prefill_workload(args.steps, args.warmup)
@@ -318,6 +385,8 @@ def main():
             "config": cfg, "roofline": roof}
     if secondary is not None:
         line["prefill"] = secondary
+    if not args.no_kv and args.workload != "prefill8k":
+        line["kv_cache"] = kv_workload()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload if args.workload != "stack48" else "stack48", 12.0)
     print(json.dumps(line), flush=True)
