@@ -125,7 +125,9 @@ typedef struct {
  *   ids[t][j]    = the j-th expert in the order (logit descending, expert index ascending),
  *                  -0.0 and +0.0 being equal
  *   p[t][j]      = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0) over the chosen k (fp32)
- * logits may be NULL (then they live in the workspace). T >= 1. Workspace: MOE_CALL_ROUTE.
+ * logits may be NULL (then they live in the workspace). T >= 1. Workspace: MOE_CALL_ROUTE (the logits
+ * when logits is NULL and, for T > 4 with few row tiles, the partial sums of the K-split router GEMM,
+ * added in a fixed order so that results are deterministic).
  */
 moe_status moe_route(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x, int32_t T,
                      float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes, void* stream);

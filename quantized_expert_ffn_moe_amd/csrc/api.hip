@@ -63,11 +63,13 @@ LayerView shape_view(const moe_layer_desc* d) {
 
 // ------------------------------------------------------------------ workspace layouts
 
-struct RouteWs { float* logits; };
+struct RouteWs { float* logits; float* part; };
 RouteWs carve_route(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
     Carve c(base);
     RouteWs r;
     r.logits = c.take<float>((size_t)T * d->num_experts);
+    const size_t pb = T > 4 ? router_scratch_bytes(T, d->hidden, d->num_experts) : 0;
+    r.part = pb ? c.take<float>(pb / sizeof(float)) : nullptr;
     if (bytes) *bytes = c.bytes();
     return r;
 }
@@ -108,6 +110,7 @@ struct LayerWs {
     int32_t *offsets, *perm, *inv, *chunks;  // prefill only
     float* h;          // decode only
     void* prefill;     // prefill only
+    float* router_part;  // prefill only: split-K partial sums of the router GEMM (may be null)
 };
 LayerWs carve_layer(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
     Carve c(base);
@@ -126,6 +129,8 @@ LayerWs carve_layer(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
         r.inv = c.take<int32_t>(P);
         r.chunks = c.take<int32_t>((size_t)perm_chunks(T) * d->num_experts);
         r.prefill = c.take<char>(prefill_scratch_bytes(shape_view(d), T));
+        const size_t pb = router_scratch_bytes(T, d->hidden, d->num_experts);
+        r.router_part = pb ? c.take<float>(pb / sizeof(float)) : nullptr;
     }
     if (bytes) *bytes = c.bytes();
     return r;
@@ -194,13 +199,15 @@ moe_status moe_route(const moe_layer_desc* d, const moe_layer_weights* w, const 
     if (logits && ((uintptr_t)logits & 3u)) return MOE_ERR_INVALID_ARG;
     size_t need = 0;
     carve_route(d, T, nullptr, &need);
-    if (!logits) MOE_TRY(check_ws(ws, ws_bytes, need));
-    float* lg = logits ? logits : carve_route(d, T, ws, nullptr).logits;
+    const bool split = T > 4 && router_scratch_bytes(T, d->hidden, d->num_experts) > 0;
+    if (!logits || split) MOE_TRY(check_ws(ws, ws_bytes, need));
+    const RouteWs rw = (!logits || split) ? carve_route(d, T, ws, nullptr) : RouteWs{nullptr, nullptr};
+    float* lg = logits ? logits : rw.logits;
     hipStream_t s = (hipStream_t)stream;
     if (T <= 4)
         MOE_TRY(launch_route_gemv(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, lg, s));
     else
-        MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, lg, s));
+        MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, lg, rw.part, s));
     return launch_topk(lg, T, d->num_experts, d->top_k, ids, p, s);
 }
 
@@ -301,7 +308,7 @@ moe_status moe_layer(const moe_layer_desc* d, const moe_layer_weights* w, const 
     // the expert outputs between the down GEMM and the combine are fp16 rows here (half the bytes
     // of the largest stream); the combine sums them in fp32
     const _Float16* ysh = d->shared_inter > 0 ? lw.y_shared : nullptr;
-    MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, L.H, L.E, lg, s));
+    MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, L.H, L.E, lg, lw.router_part, s));
     MOE_TRY(launch_topk(lg, T, L.E, L.k, id, pr, s));
     MOE_TRY(launch_permute(id, T, L.k, L.E, lw.offsets, lw.perm, lw.inv, lw.chunks, s));
     MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, true, lw.prefill, s));

@@ -18,8 +18,11 @@ struct LayerView {
 };
 
 // router GEMM (any T) and the top-k + softmax kernel (one wave per token)
+// Router GEMM for T > 4; scratch of router_scratch_bytes() (split-K partial sums; none when 0).
+int router_splits(int T, int H, int E);
+size_t router_scratch_bytes(int T, int H, int E);
 moe_status launch_router(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
-                         float* logits, hipStream_t s);
+                         float* logits, float* scratch, hipStream_t s);
 moe_status launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* p, hipStream_t s);
 
 // permutation: counts/bases scratch of chunks(T) * E ints

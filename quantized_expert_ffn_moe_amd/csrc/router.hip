@@ -3,6 +3,8 @@
 // The router is resident and cheap next to the experts; its scores pick a few experts per token
 // (648news 07-nano-cuda-moe-qwen38-release, section "asynchronous CPU/GPU compute"; 8 of 256 in
 // 648news 10-cyber-on-strata-moe-local-inference, section "tiered VRAM/RAM inference").
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace moe {
@@ -28,9 +30,13 @@ struct RouterSlot {
     floatx4 b0, b1;   // 8 fp32 of W_r
 };
 
+// Split K (blockIdx.y = split s of `splits`): with more than one split every block writes fp32 partial
+// sums of its K range to part[s][T][E] and k_router_reduce adds them in split order plus the bias
+// (deterministic); with one split the block writes logits + bias directly.
 __global__ __launch_bounds__(256, 2) void k_router_mfma(const float* __restrict__ w_r, const float* __restrict__ bias,
                                                         const uint16_t* __restrict__ x, int T, int H, int E,
-                                                        float* __restrict__ logits) {
+                                                        float* __restrict__ logits, int splits,
+                                                        float* __restrict__ part) {
     __shared__ __attribute__((aligned(16))) __bf16 As[2][kRtM * kRtLds];
     __shared__ __attribute__((aligned(16))) __bf16 Bs[2][3][kRtN * kRtLds];
     const int mt = (T + kRtM - 1) / kRtM, nt = (E + kRtN - 1) / kRtN;
@@ -46,9 +52,11 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const float* __restrict_
     // loader: thread -> row tid / 4, K chunk 8 * (tid % 4); rows past T or E are clamped (their
     // outputs are never stored)
     const int lr = tid >> 2, lc = 8 * (tid & 3);
-    const uint16_t* ap = x + (size_t)min(t0 + lr, T - 1) * H + lc;
-    const float* bp = w_r + (size_t)min(e0 + lr, E - 1) * H + lc;
-    const int nk = H / kRtK;
+    const int nk_all = H / kRtK;
+    const int kbeg = (int)(((int64_t)nk_all * blockIdx.y) / splits);
+    const int nk = (int)(((int64_t)nk_all * (blockIdx.y + 1)) / splits) - kbeg;
+    const uint16_t* ap = x + (size_t)min(t0 + lr, T - 1) * H + lc + (size_t)kbeg * kRtK;
+    const float* bp = w_r + (size_t)min(e0 + lr, E - 1) * H + lc + (size_t)kbeg * kRtK;
     auto gload = [&](RouterSlot& sl, int ks) __attribute__((always_inline)) {
         ks = min(ks, nk - 1);
         sl.a = *reinterpret_cast<const u32x4*>(ap + ks * kRtK);
@@ -123,13 +131,24 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const float* __restrict_
         for (int j = 0; j < 2; ++j) {
             const int e = e0 + wn * 32 + 16 * j + lane % 16;
             if (e >= E) continue;
-            const float b = bias ? bias[e] : 0.f;
+            const float b = splits == 1 && bias ? bias[e] : 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = t0 + wm * 32 + 16 * i + 4 * (lane / 16) + r;
-                if (t < T) logits[(size_t)t * E + e] = acc[i][j][r] + b;
+                if (t >= T) continue;
+                if (splits == 1) logits[(size_t)t * E + e] = acc[i][j][r] + b;
+                else part[((size_t)blockIdx.y * T + t) * E + e] = acc[i][j][r];
             }
         }
+}
+
+__global__ __launch_bounds__(256) void k_router_reduce(const float* __restrict__ part, int splits, int T, int E,
+                                                       const float* __restrict__ bias, float* __restrict__ logits) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)T * E) return;
+    float acc = 0.f;
+    for (int sp = 0; sp < splits; ++sp) acc += part[(int64_t)sp * T * E + i];
+    logits[i] = acc + (bias ? bias[i % E] : 0.f);
 }
 
 // ----------------------------------------------------------------------------- top-k + softmax
@@ -152,12 +171,35 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
 
 // ----------------------------------------------------------------------------- launchers
 
+// Splits of K for the router GEMM: enough blocks to occupy the GPU when T is small, at least four
+// K steps of 32 per split.
+int router_splits(int T, int H, int E) {
+    const int blocks = ((T + kRtM - 1) / kRtM) * ((E + kRtN - 1) / kRtN);
+    int sp = blocks >= 128 ? 1 : 256 / blocks;
+    sp = std::min(sp, 16);
+    sp = std::min(sp, (H / kRtK) / 4);
+    return std::max(sp, 1);
+}
+
+size_t router_scratch_bytes(int T, int H, int E) {
+    const int sp = router_splits(T, H, E);
+    return sp > 1 ? (size_t)sp * T * E * sizeof(float) : 0;
+}
+
 moe_status launch_router(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
-                         float* logits, hipStream_t s) {
+                         float* logits, float* scratch, hipStream_t s) {
+    const int sp = router_splits(T, H, E);
+    if (sp > 1 && !scratch) return MOE_ERR_WORKSPACE;
     const int blocks = ((T + kRtM - 1) / kRtM) * ((E + kRtN - 1) / kRtN);
     const int grid = ((blocks + kRtXcds - 1) / kRtXcds) * kRtXcds;
-    hipLaunchKernelGGL(k_router_mfma, dim3(grid), dim3(256), 0, s, w_r, bias, x, T, H, E, logits);
+    hipLaunchKernelGGL(k_router_mfma, dim3(grid, sp), dim3(256), 0, s, w_r, bias, x, T, H, E, logits, sp, scratch);
     MOE_LAUNCH_CHECK();
+    if (sp > 1) {
+        const int64_t n = (int64_t)T * E;
+        hipLaunchKernelGGL(k_router_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, scratch, sp, T, E,
+                           bias, logits);
+        MOE_LAUNCH_CHECK();
+    }
     return MOE_OK;
 }
 

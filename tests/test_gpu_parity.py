@@ -178,23 +178,24 @@ def test_router_fp32_error_bound(T, E):
     assert np.all(err <= bound), "max err/bound %.3f" % float(np.max(err / bound))
 
 
-@pytest.mark.parametrize("T", [3, 300])
-def test_router_exact_on_representable_sums(T):
-    """Inputs whose every partial sum is exact in fp32: x in {-1, 0, 1}, w = m * 2^-17 with
-    m in [2^16, 2^17) (17 significant bits, so all three bf16 terms of the split are needed),
-    H = 96 (|sum| < 2^24 * 2^-17). Any fp32 evaluation order gives the exact value, so the
-    logits must equal the oracle's bit for bit."""
+@pytest.mark.parametrize("T,H,mbits", [(3, 96, 17), (300, 96, 17), (40, 256, 16)])
+def test_router_exact_on_representable_sums(T, H, mbits):
+    """Inputs whose every partial sum is exact in fp32: x in {-1, 0, 1}, w = m * 2^-mbits with m in
+    [2^(mbits-1), 2^mbits), H * 2^mbits <= 2^24 (17 bits at H = 96: all three bf16 terms of the
+    split are needed; H = 256 with 16 bits runs the K-split GEMM with its partial-sum reduction).
+    Any fp32 evaluation order gives the exact value, so the logits must equal the oracle's bit for
+    bit."""
     _need_gpu()
-    E, H = 200, 96
+    E = 200
     spec = synth.LayerSpec("rx", T=T, H=H, E=E, k=4, I=32, Is=0, fmt=synth.Q8, zipf=False, cfg_id=61)
     d = synth.make_layer(spec)
     rng = np.random.default_rng(7)
     xv = rng.integers(-1, 2, size=(T, H)).astype(np.float32)
     d["x"] = (xv.view(np.uint32) >> 16).astype(np.uint16)
-    m = rng.integers(1 << 16, 1 << 17, size=(E, H)) * rng.choice([-1, 1], size=(E, H))
-    d["w_router"] = (m * 2.0 ** -17).astype(np.float32)
+    m = rng.integers(1 << (mbits - 1), 1 << mbits, size=(E, H)) * rng.choice([-1, 1], size=(E, H))
+    d["w_router"] = (m * 2.0 ** -mbits).astype(np.float32)
     d["router_bias"] = (rng.integers(-64, 64, size=E) * 2.0 ** -6).astype(np.float32)
-    say("router exact T=%d" % T)
+    say("router exact T=%d H=%d" % (T, H))
     O = orc_layer(spec, d)
     L = dev_layer(spec, d)
     logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
