@@ -2,22 +2,28 @@
 //
 // Prompt processing on the pages runs in 8K-token chunks with GEMMs and grouped expert kernels
 // (648news 07-nano-cuda-moe-qwen38-release, section "speed comparison and accuracy check"). Here:
-//   - the pairs of each expert are contiguous after the permutation; a tile list of
-//     (group, first row) covers every group with 128-row tiles, the shared expert being one more
-//     group of all T tokens;
-//   - one kernel template, two uses: gate/up (A = x rows gathered through perm, B = 128 gate rows
-//     and 128 up rows interleaved in 32-row granules so that g and u of the same (row, n) meet in
-//     one lane; SwiGLU epilogue writes h in fp16) and down (A = h rows in sorted order, B = 256
-//     down rows; fp32 output rows);
-//   - block tile 128 x 256, four waves of 64 x 128, K steps of 32 through double-buffered LDS
-//     (rows padded to 80 bytes: the 16-byte fragment reads of 16 lanes hit distinct banks), two
-//     v_mfma_f32_32x32x16_f16 per 32 x 32 output tile and K step (on this chip the 32 x 32 form
-//     sustains a far higher rate than 16 x 16 x 32);
-//   - weights are dequantised in registers: the code is OR-ed into the mantissa of 1024.0, the
-//     offset subtracted (an exact fp16 level) and multiplied by the fp16 scale with packed fp16
-//     arithmetic, i.e. level * scale rounded once to fp16. The pairs come out in an order that
-//     permutes K inside each 4-, 8- or 16-element group; x (converted from bf16) and h are stored
-//     with the same permutation so the dot products are unchanged;
+//   - the pairs of each expert are contiguous after the permutation; a tile list covers every
+//     group (the shared expert being one more group of all T tokens) with 128-row tiles and one
+//     last tile of 32, 64 or 128 rows for the remainder, so small groups waste little work;
+//   - one kernel template, two uses: gate/up (A = x rows gathered through perm; each wave's two
+//     32-row weight tiles are gate and up rows of the same h columns, so SwiGLU pairs them in one
+//     lane; h is written in fp16 through LDS with full-row stores) and down (A = h rows in sorted
+//     order; outputs stored from the accumulators);
+//   - a block is 4 waves over a tile of up to 128 rows x 256 weight rows, two blocks per CU so that
+//     one block's prologue, barriers and stores overlap the other's MFMAs; each wave computes all
+//     rows of the tile against its own 64 weight rows with v_mfma_f32_32x32x16_f16 (on this chip
+//     the 32 x 32 form sustains a far higher rate than 16 x 16 x 32): every A fragment read from
+//     LDS feeds 2 MFMAs and every dequantised weight fragment up to 4;
+//   - A goes global -> LDS directly (16 bytes per lane, no registers), in a three-stage ring two K
+//     steps ahead, each 128-byte row segment XOR-swizzled in 16-byte slots so that the fragment
+//     reads of 16 lanes hit distinct banks; one barrier per K step of 64;
+//   - weights never touch LDS: each lane loads the codes and scale of one 32-block of its weight
+//     row (two steps ahead, in named register slots) and dequantises them straight into its MFMA
+//     operand: the code is OR-ed into the mantissa of 1024.0, the offset subtracted (an exact fp16
+//     level) and multiplied by the fp16 scale with packed fp16 arithmetic, i.e. level * scale
+//     rounded once to fp16. The pairs come out in an order that permutes K inside each 4-, 8- or
+//     16-element group; x (converted from bf16) and h are stored with the same permutation so the
+//     dot products are unchanged;
 //   - blocks are mapped so that consecutive row tiles of one expert (which share a weight panel)
 //     run on the same XCD and reuse it from that XCD's L2.
 #include <utility>
@@ -31,21 +37,29 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBM = 128;      // rows (pairs) per tile
-constexpr int kBN = 256;      // weight rows per tile
-constexpr int kAS = 64 + 8;   // fp16 per A row in LDS: one step of K = 64, padded to 144 bytes
+constexpr int kTM = 128;                   // rows of a full tile
+constexpr int kGW = 4;                     // waves per block (one per SIMD)
+constexpr int kGT = kGW * kWave;           // threads per block
+constexpr int kStages = 3;                 // A stages in LDS
+constexpr int kStageBytes = kTM * 128;     // one K step (64 fp16) of 128 rows
+constexpr int kHS = 128 + 8;               // fp16 per row of the staged h tile (padded)
 constexpr int kXcds = 8;
 
 struct TileDesc {
     int group;  // expert id, or E for the shared expert
     int row0;   // first row of the tile inside its group
+    int ni;     // 32-row MFMA tiles: 1, 2 or 4
+    int pad;
 };
 
 // -------------------------------------------------------------------------------- tile list
-// One block of 1024 threads: thread e counts the tiles of expert e, a block scan places them,
-// the shared group's tiles follow the routed ones. Offsets are clamped to [0, T*k] and the list
-// to tiles_max entries, so that inconsistent offsets cannot move any access out of bounds.
+// One block of 1024 threads. Thread e < E takes expert e: floor(count / 128) full tiles and, for a
+// remainder, one tile of 32 * ni rows (ni the power of two at or above ceil(rem / 32)). Full tiles
+// come first (expert-major, then the shared group's), remainder tiles after them; block scans
+// place them. Offsets are clamped to [0, T*k] and the list to tiles_max entries, so that
+// inconsistent offsets cannot move any access out of bounds.
 __device__ __forceinline__ void group_rows(const int32_t* offsets, int E, int T, int Tk, int g, int& base,
                                            int& count) {
     if (g == E) { base = 0; count = T; return; }
@@ -53,35 +67,51 @@ __device__ __forceinline__ void group_rows(const int32_t* offsets, int E, int T,
     count = min(max(offsets[g + 1], base), Tk) - base;
 }
 
+__host__ __device__ inline int rem_tile_ni(int rem) {
+    const int n = (rem + 31) / 32;
+    return n <= 1 ? 1 : n <= 2 ? 2 : 4;
+}
+
+__device__ __forceinline__ int block_scan_incl(int* part, int v) {
+    const int e = threadIdx.x;
+    part[e] = v;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int t = e >= d ? part[e - d] : 0;
+        __syncthreads();
+        part[e] += t;
+        __syncthreads();
+    }
+    return part[e];
+}
+
 __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict__ offsets, int E, int T, int k,
                                                       int has_shared, int tiles_max, TileDesc* __restrict__ tiles,
                                                       int32_t* __restrict__ ntiles) {
-    __shared__ int part[1024];
+    __shared__ int pf[1024], pr[1024];
     const int e = threadIdx.x;
     int base = 0, n = 0;
     if (e < E) group_rows(offsets, E, T, T * k, e, base, n);
-    const int nt = (n + kBM - 1) / kBM;
-    part[e] = nt;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int v = e >= d ? part[e - d] : 0;
-        __syncthreads();
-        part[e] += v;
-        __syncthreads();
-    }
-    const int start = part[e] - nt;
-    for (int i = 0; i < nt && start + i < tiles_max; ++i) tiles[start + i] = TileDesc{e, i * kBM};
+    const int nf = n / kTM, rem = n % kTM, hr = rem > 0 ? 1 : 0;
+    const int f_incl = block_scan_incl(pf, nf);
+    const int r_incl = block_scan_incl(pr, hr);
+    const int full_routed = pf[1023], rem_routed = pr[1023];
+    const int sf = has_shared ? T / kTM : 0, srem = has_shared ? T % kTM : 0;
+    const int rem0 = full_routed + sf;   // first remainder slot
+    auto put = [&](int slot, TileDesc d) {
+        if (slot < tiles_max) tiles[slot] = d;
+    };
+    for (int i = 0; i < nf; ++i) put(f_incl - nf + i, TileDesc{e, i * kTM, kTM / 32, 0});
+    if (hr) put(rem0 + r_incl - 1, TileDesc{e, nf * kTM, rem_tile_ni(rem), 0});
     if (e == 1023) {
-        int total = min(part[1023], tiles_max);
-        if (has_shared) {
-            const int ns = (T + kBM - 1) / kBM;
-            for (int i = 0; i < ns && total < tiles_max; ++i) tiles[total++] = TileDesc{E, i * kBM};
-        }
-        *ntiles = total;
+        for (int i = 0; i < sf; ++i) put(full_routed + i, TileDesc{E, i * kTM, kTM / 32, 0});
+        int total = rem0 + rem_routed;
+        if (srem > 0) put(total++, TileDesc{E, sf * kTM, rem_tile_ni(srem), 0});
+        *ntiles = min(total, tiles_max);
     }
 }
 
-int max_tiles(int T, int k, int E) { return (T * k) / kBM + E + (T + kBM - 1) / kBM + 1; }
+int max_tiles(int T, int k, int E) { return (T * k) / kTM + T / kTM + E + 2; }
 
 // -------------------------------------------------------------------------------- K permutation
 
@@ -160,25 +190,32 @@ __device__ __forceinline__ uint32_t dword_of(const BlockCodes& b, int d) {
 
 // Pairs 4 kk .. 4 kk + 3 of a block (K-permuted positions 8 kk .. 8 kk + 7) as level * scale,
 // each rounded once to fp16. Pair p of a block holds elements (j, j + G/2) of its G-group:
-//   Q4: dword d = elements 8d .. 8d+7, pair 4d + j = nibbles (j, j + 4), offset 1032 = 1024 + 8;
-//   Q8: dword d = elements 4d .. 4d+3, pairs 2d (bytes 0, 2) and 2d + 1 (bytes 1, 3), offset 1152;
+//   Q4: dword d = elements 8d .. 8d+7 (offset binary after the xor), pair 4d + j = nibbles
+//       (j, j + 4). Nibbles at bits 0-3 (j = 0, and j = 2 after a shift by 8) land in the mantissa
+//       of 1024.0 (1024 + n, offset 1032); nibbles at bits 4-7 (j = 1, 3) in that of 64.0, whose
+//       last mantissa bit is worth 1/16 (64 + n, offset 72): one and-or per pair, no shifts.
+//   Q8: dword d = elements 4d .. 4d+3, pairs 2d (bytes 0, 2) and 2d + 1 (bytes 1, 3): one byte
+//       permute puts two codes under the exponent byte of 1024.0 (1024 + b, offset 1152).
 //   Q2: dword d = elements 16d .. 16d+15, pair 8d + j = crumbs (j, j + 8) as 2c + 1024, offset
 //       1027 = 1024 + 2 * 1.5, times s / 2.
 template <int FMT, int KK>
 __device__ __forceinline__ half8 dequant8(const BlockCodes& b, half2v sv) {
     uint32_t o[4];
     if constexpr (FMT == MOE_Q4_B32) {
-        const half2v off = {(_Float16)1032.f, (_Float16)1032.f};
-        const uint32_t u = dword_of(b, KK) ^ 0x88888888u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = h2bits((bits2h(((u >> (4 * j)) & 0x000F000Fu) | kMagic16) - off) * sv);
+        const half2v off0 = {(_Float16)1032.f, (_Float16)1032.f}, off1 = {(_Float16)72.f, (_Float16)72.f};
+        const uint32_t u = dword_of(b, KK) ^ 0x88888888u, v = u >> 8;
+        o[0] = h2bits((bits2h((u & 0x000F000Fu) | kMagic16) - off0) * sv);
+        o[1] = h2bits((bits2h((u & 0x00F000F0u) | 0x54005400u) - off1) * sv);
+        o[2] = h2bits((bits2h((v & 0x000F000Fu) | kMagic16) - off0) * sv);
+        o[3] = h2bits((bits2h((v & 0x00F000F0u) | 0x54005400u) - off1) * sv);
     } else if constexpr (FMT == MOE_Q8_B32) {
         const half2v off = {(_Float16)1152.f, (_Float16)1152.f};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t u = dword_of(b, 2 * KK + h) ^ 0x80808080u;
-            o[2 * h] = h2bits((bits2h((u & 0x00FF00FFu) | kMagic16) - off) * sv);
-            o[2 * h + 1] = h2bits((bits2h(((u >> 8) & 0x00FF00FFu) | kMagic16) - off) * sv);
+            // bytes {u0, 0x64, u2, 0x64} and {u1, 0x64, u3, 0x64}
+            o[2 * h] = h2bits((bits2h(__builtin_amdgcn_perm(0x64646464u, u, 0x04020400u)) - off) * sv);
+            o[2 * h + 1] = h2bits((bits2h(__builtin_amdgcn_perm(0x64646464u, u, 0x04030401u)) - off) * sv);
         }
     } else {
         const half2v off = {(_Float16)1027.f, (_Float16)1027.f};
@@ -206,27 +243,290 @@ template <int N, typename F> __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// One pipeline step of loads (K = 64, two 32-blocks): four 16-byte chunks of A for the LDS stage,
-// and for each of the lane's two weight tiles the codes and the scale of the lane's own block.
-// Plain members only: a slot must never be indexed at run time, or it would leave the registers.
-struct StepSlot {
-    u32x4 a0, a1, a2, a3;
-    BlockCodes b0, b1;
-    uint32_t s0, s1;
+// Weight operand of one K step for one lane: the codes and the scale of its 32-block. Plain
+// members only: a slot must never be indexed at run time, or it would leave the registers.
+struct BSlot {
+    BlockCodes b;
+    uint32_t sc;
 };
+
+template <int FMT> constexpr int code_loads() { return FMT == MOE_Q8_B32 ? 2 : 1; }
+
+// Wait until at most VM vector-memory loads of this wave are in flight (and its LDS operations are
+// done), then meet the other waves. Written with the wait visible to the compiler and without a
+// memory fence, which would make the barrier wait for every load in flight; the empty asm
+// statements keep memory operations from moving across it.
+template <int VM> __device__ __forceinline__ void step_barrier() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (0 << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One tile of 32 * NI rows against the block's 256 weight rows (gate/up: 128 h columns).
+template <int FMT, bool GATEUP, typename YT, int NI>
+__device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileDesc& td, int ntile,
+                                          const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+                                          const _Float16* __restrict__ asrc, _Float16* __restrict__ h16,
+                                          YT* __restrict__ y_sorted, YT* __restrict__ y_shared, uint8_t* smem) {
+    constexpr int G = perm_group<FMT>();
+    constexpr int BB = FMT == MOE_Q8_B32 ? 32 : FMT == MOE_Q4_B32 ? 16 : 8;   // bytes per block
+    constexpr int QW = NI;                         // 1 KB (8-row) direct loads per wave and step
+    constexpr int BATCH = QW + 2 * code_loads<FMT>() + 2;   // vector-memory instructions per step
+
+    const bool shared = td.group == L.E;
+    const int H = L.H, Imax = L.Imax();
+    int N, n0, K;
+    if constexpr (GATEUP) {
+        N = shared ? L.Is : L.I;          // h columns of this group
+        n0 = ntile * 128;
+        K = H;
+    } else {
+        N = H;
+        n0 = ntile * 256;
+        K = shared ? L.Is : L.I;
+    }
+    if (n0 >= N) return;
+    const int Tk = T * L.k;
+    int base, count;
+    group_rows(offsets, L.E, T, Tk, td.group, base, count);
+    const int nrows = min(NI * 32, count - td.row0);
+    if (nrows <= 0) return;
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int frow = lane % 32, g = lane / 32;
+    const int nb = K / 32;                    // scale blocks along K
+    const int nsteps = (nb + 1) / 2;
+
+    // A: stage row r (0 .. 32 NI - 1) sits at r * 128 bytes, its 16-byte K chunk c in slot
+    // c ^ ((r >> 1) & 7). Wave load u fills rows 8 q .. 8 q + 7 (q = wave + 4 u); lane l writes
+    // slot l % 8 of row 8 q + l / 8, so it fetches the chunk that belongs there. Rows past the
+    // tile are clamped to a valid row: they only feed output rows that are never stored.
+    const _Float16* arow[QW];
+    int ach[QW];
+#pragma unroll
+    for (int u = 0; u < QW; ++u) {
+        const int q = wave + kGW * u;
+        const int r = 8 * q + lane / 8;
+        ach[u] = 8 * ((lane & 7) ^ ((r >> 1) & 7));
+        const int pos = td.row0 + min(r, nrows - 1);
+        if constexpr (GATEUP) {
+            const int qq = shared ? pos * L.k : perm[base + pos];
+            const int tok = (unsigned)qq < (unsigned)Tk ? qq / L.k : 0;
+            arow[u] = asrc + (size_t)tok * H;
+        } else {
+            const int64_t hrow = shared ? (int64_t)Tk + pos : (int64_t)base + pos;
+            arow[u] = asrc + (size_t)hrow * Imax;
+        }
+    }
+    // fragment of lane (frow, g) for K sub-step kk: row 32 i + frow, chunk 4 g + kk
+    int aoff[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) aoff[kk] = frow * 128 + 16 * ((4 * g + kk) ^ ((frow >> 1) & 7));
+
+    // B: wave w owns weight rows 64 w .. 64 w + 63 of the tile as two 32-row MFMA tiles; lane
+    // (frow, g) loads, for each, block 2 s + g of its row at step s. Gate/up: tile 0 = gate rows,
+    // tile 1 = up rows of the same h columns n0 + 32 w + [0, 32); down: output columns
+    // n0 + 64 w + [0, 64).
+    // Each matrix (one expert's gate, up or down, or the shared expert's) is at most
+    // 4096 x 16384 bytes of codes, so 32-bit lane offsets suffice.
+    const uint8_t* bmat[2];
+    const uint8_t* smat[2];
+    const int64_t rb = (int64_t)nb * BB;
+    int64_t mrows;   // rows of the matrices
+    int wrow[2];     // this lane's row in each
+    if constexpr (GATEUP) {
+        mrows = N;
+        const int n = min(n0 + 32 * wave + frow, N - 1);
+        wrow[0] = wrow[1] = n;
+        if (shared) {
+            bmat[0] = L.sg_codes; bmat[1] = L.su_codes;
+            smat[0] = reinterpret_cast<const uint8_t*>(L.sg_scales);
+            smat[1] = reinterpret_cast<const uint8_t*>(L.su_scales);
+        } else {
+            const int64_t e = td.group;
+            bmat[0] = L.g_codes + e * N * rb; bmat[1] = L.u_codes + e * N * rb;
+            smat[0] = reinterpret_cast<const uint8_t*>(L.g_scales + e * N * nb);
+            smat[1] = reinterpret_cast<const uint8_t*>(L.u_scales + e * N * nb);
+        }
+    } else {
+        mrows = H;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) wrow[j] = min(n0 + 64 * wave + 32 * j + frow, H - 1);
+        if (shared) {
+            bmat[0] = bmat[1] = L.sd_codes;
+            smat[0] = smat[1] = reinterpret_cast<const uint8_t*>(L.sd_scales);
+        } else {
+            const int64_t e = td.group;
+            bmat[0] = bmat[1] = L.d_codes + e * H * rb;
+            smat[0] = smat[1] = reinterpret_cast<const uint8_t*>(L.d_scales + e * H * nb);
+        }
+    }
+    const int64_t bbytes = mrows * rb, sbytes = mrows * nb * 2;
+    // lane offsets of block g of row wrow (tile 0; tile 1 adds its row difference)
+    const int bvo0 = (int)(wrow[0] * rb) + g * BB, svo0 = (wrow[0] * nb + g) * 2;
+    const int bdv = (int)((wrow[1] - wrow[0]) * rb), sdv = (wrow[1] - wrow[0]) * nb * 2;
+
+    BSlot slot0[2], slot1[2], slot2[2];
+    auto slot = [&](auto sc) __attribute__((always_inline)) -> BSlot(&)[2] {
+        constexpr int v = decltype(sc)::value;
+        if constexpr (v == 0) return slot0;
+        else if constexpr (v == 1) return slot1;
+        else return slot2;
+    };
+    // A source of load u at step t: its row + min(128 t + 2 ach, 2 (K - 8)) bytes
+    const char* abase[QW];
+#pragma unroll
+    for (int u = 0; u < QW; ++u) abase[u] = reinterpret_cast<const char*>(arow[u]);
+    const int klim = 2 * (K - 8);
+    // loads of step t (clamped: steps past the end reload the last one, unused) into B slots and
+    // an A stage. Weights come through buffer descriptors whose base moves with the step, so the
+    // lane offsets stay fixed; a block past the end of the matrix reads as zero (bounds-checked).
+    // A chunk past K (the second half of the last step when K % 64 == 32) reloads the row's last
+    // chunk instead (its weights are zero, see below).
+    auto issue = [&](BSlot (&sl)[2], int t, int stage) __attribute__((always_inline)) {
+        t = min(t, nsteps - 1);
+        uint8_t* st = smem + stage * kStageBytes + wave * 1024;
+#pragma unroll
+        for (int u = 0; u < QW; ++u)
+            __builtin_amdgcn_global_load_lds(abase[u] + min(128 * t + 2 * ach[u], klim), (lds_void*)(st + u * kGW * 1024),
+                                             16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int cofs = 2 * t * BB, sofs = 4 * t;
+            const int bvo = bvo0 + j * bdv, svo = svo0 + j * sdv;
+            const __amdgpu_buffer_rsrc_t rc =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(bmat[j] + cofs), (short)0, (int)(bbytes - cofs), 0x00020000);
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(smat[j] + sofs), (short)0, (int)(sbytes - sofs), 0x00020000);
+            if constexpr (FMT == MOE_Q8_B32) {
+                sl[j].b.c0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, bvo, 0, 0));
+                sl[j].b.c1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, bvo + 16, 0, 0));
+            } else if constexpr (FMT == MOE_Q4_B32) {
+                sl[j].b.c0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, bvo, 0, 0));
+            } else {
+                const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, bvo, 0, 0));
+                sl[j].b.c0.x = v.x;
+                sl[j].b.c0.y = v.y;
+            }
+            sl[j].sc = __builtin_amdgcn_raw_buffer_load_b16(rs, svo, 0, 0);
+        }
+    };
+
+    floatx16 acc[NI][2];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // step s: refill the slots and stage of step s + 2, dequantise this lane's blocks of step s
+    // and run its MFMAs against stage s % 3, then wait for the loads of step s + 1 (everything but
+    // the last BATCH vector-memory instructions) and meet the other waves. The barrier is written
+    // out so that no memory fence makes it wait for the loads still in flight.
+    auto kstep = [&](int s, auto sc) __attribute__((always_inline)) {
+        constexpr int SL = decltype(sc)::value;
+        issue(slot(std::integral_constant<int, (SL + 2) % 3>{}), s + 2, (SL + 2) % 3);
+        const BSlot(&cur)[2] = slot(sc);
+        const bool blive = 2 * s + g < nb;     // a block past K contributes zero
+        const _Float16 s0 = blive ? __builtin_bit_cast(_Float16, (uint16_t)cur[0].sc) : (_Float16)0.f;
+        const _Float16 s1 = blive ? __builtin_bit_cast(_Float16, (uint16_t)cur[1].sc) : (_Float16)0.f;
+        const half2v sv0 = {s0, s0}, sv1 = {s1, s1};
+        const uint8_t* st = smem + SL * kStageBytes;
+        // A fragments of sub-step kk + 1 are read while the MFMAs of kk run (two named sets, so
+        // that nothing is indexed at run time); the scheduling fences keep that order.
+        half8 fa[NI], fb[NI];
+        auto frag = [&](auto kc, half8 (&f)[NI]) __attribute__((always_inline)) {
+            constexpr int kk = decltype(kc)::value;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) f[i] = *reinterpret_cast<const half8*>(st + aoff[kk] + i * 4096);
+        };
+        frag(std::integral_constant<int, 0>{}, fa);
+        static_for<4>([&](auto kc) {
+            constexpr int kk = decltype(kc)::value;
+            half8 (&cur_a)[NI] = (kk % 2 == 0) ? fa : fb;
+            half8 (&nxt_a)[NI] = (kk % 2 == 0) ? fb : fa;
+            if constexpr (kk < 3) frag(std::integral_constant<int, kk + 1>{}, nxt_a);
+            __builtin_amdgcn_sched_barrier(0);
+            const half8 b0 = dequant8<FMT, kk>(cur[0].b, sv0);
+            const half8 b1 = dequant8<FMT, kk>(cur[1].b, sv1);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur_a[i], b0, acc[i][0], 0, 0, 0);
+                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur_a[i], b1, acc[i][1], 0, 0, 0);
+            }
+        });
+        step_barrier<BATCH>();
+    };
+
+    issue(slot0, 0, 0);
+    issue(slot1, 1, 1);
+    step_barrier<BATCH>();
+    int s = 0;
+    for (; s + 3 <= nsteps; s += 3) {
+        kstep(s, std::integral_constant<int, 0>{});
+        kstep(s + 1, std::integral_constant<int, 1>{});
+        kstep(s + 2, std::integral_constant<int, 2>{});
+    }
+    if (s < nsteps) kstep(s, std::integral_constant<int, 0>{});
+    if (s + 1 < nsteps) kstep(s + 1, std::integral_constant<int, 1>{});
+    // every direct load has landed and every wave is done with the stages: LDS is free
+    step_barrier<0>();
+
+    const int rq = 4 * g;
+    if constexpr (GATEUP) {
+        // SwiGLU of (gate, up) = (tile 0, tile 1) in every lane; h goes to an LDS tile of the
+        // block's 128 columns, then out in 16-byte pieces of whole rows
+        _Float16* hs = reinterpret_cast<_Float16*>(smem);
+        const int pc = kperm(32 * wave + frow, G);   // n0 is a multiple of 128, so of G
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
+                hs[row * kHS + pc] = (_Float16)silu_mul(acc[i][0][r], acc[i][1][r]);
+            }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 2 * NI; ++it) {
+            const int idx = tid + kGT * it;      // NI * 32 rows x 16 pieces
+            const int row = idx / 16, ch = idx % 16;
+            const int col = n0 + 8 * ch;
+            if (row < nrows && col < N) {
+                const int64_t hrow = shared ? (int64_t)Tk + td.row0 + row : (int64_t)base + td.row0 + row;
+                *reinterpret_cast<u32x4*>(h16 + hrow * Imax + col) =
+                    *reinterpret_cast<const u32x4*>(hs + row * kHS + 8 * ch);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int m = n0 + 64 * wave + 32 * j + frow;
+            if (m >= H) continue;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
+                    if (row >= nrows) continue;
+                    if (shared) y_shared[(int64_t)(td.row0 + row) * H + m] = (YT)acc[i][j][r];
+                    else y_sorted[((int64_t)base + td.row0 + row) * H + m] = (YT)acc[i][j][r];
+                }
+        }
+    }
+}
 
 // YT: type of the down outputs (float, or _Float16 for the fused layer's internal rows).
 template <int FMT, bool GATEUP, typename YT = float>
-__global__ __launch_bounds__(256, 2) void k_grouped_gemm(LayerView L, int T, const TileDesc* __restrict__ tiles,
+__global__ __launch_bounds__(kGT, 2) void k_grouped_gemm(LayerView L, int T, const TileDesc* __restrict__ tiles,
                                                          const int32_t* __restrict__ ntiles, int n_ntile,
                                                          const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ perm,
                                                          const _Float16* __restrict__ asrc, _Float16* __restrict__ h16,
                                                          YT* __restrict__ y_sorted, YT* __restrict__ y_shared) {
-    __shared__ __attribute__((aligned(16))) _Float16 As[2][kBM * kAS];
-    constexpr int G = perm_group<FMT>();
-    constexpr int BB = FMT == MOE_Q8_B32 ? 32 : FMT == MOE_Q4_B32 ? 16 : 8;   // bytes per block
-
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
     // XCD-aware work index: block b runs on XCD b % 8, and consecutive work items go to the same
     // XCD. Work items are ordered tile-major: the weight-row tiles of one row tile (same A rows)
     // run side by side, and so do the row tiles of one expert (same weights). The grid is sized for
@@ -241,188 +541,10 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(LayerView L, int T, con
     if (w >= total) return;
     const int tile = w / n_ntile, ntile = w % n_ntile;
     const TileDesc td = tiles[tile];
-    const bool shared = td.group == L.E;
-    const int H = L.H, Imax = L.Imax();
-    int N, n0, K;
-    if constexpr (GATEUP) {
-        N = shared ? L.Is : L.I;          // h columns of this group
-        n0 = ntile * (kBN / 2);
-        K = H;
-    } else {
-        N = H;
-        n0 = ntile * kBN;
-        K = shared ? L.Is : L.I;
-    }
-    if (n0 >= N) return;
-    const int Tk = T * L.k;
-    int base, count;
-    group_rows(offsets, L.E, T, Tk, td.group, base, count);
-    const int nrows = min(kBM, count - td.row0);
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int frow = lane % 32, g = lane / 32;
-    const int nb = K / 32;                    // scale blocks along K
-    const int nsteps = (nb + 1) / 2;
-
-    // Operand rows past the tile's valid rows or columns are clamped to a valid row: they only feed
-    // output rows or columns that are never stored, and every load stays unconditional (so the
-    // compiler can keep several steps of loads in flight).
-    // A: thread -> 16-byte chunk c = tid % 8 of rows tid / 8 + 32 q (q = 0..3) of every step
-    const int ac = tid & 7;
-    const _Float16* arow[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = (tid >> 3) + 32 * q;
-        const int pos = td.row0 + min(r, nrows - 1);
-        if constexpr (GATEUP) {
-            const int qq = shared ? pos * L.k : perm[base + pos];
-            const int tok = (unsigned)qq < (unsigned)Tk ? qq / L.k : 0;
-            arow[q] = asrc + (size_t)tok * H;
-        } else {
-            const int64_t hrow = shared ? (int64_t)Tk + pos : (int64_t)base + pos;
-            arow[q] = asrc + (size_t)hrow * Imax;
-        }
-    }
-    // B: wave w owns weight rows 64 w .. 64 w + 63 of the tile as two 32-row MFMA tiles; lane
-    // (frow, g) loads, for each tile, block 2 s + g of its row at step s and dequantises it
-    // straight into its MFMA operand (no LDS). Gate/up: tile 0 = gate rows, tile 1 = up rows of
-    // the same h columns n0 + 32 w + [0, 32); down: output columns n0 + 64 w + [0, 64).
-    const uint8_t* bc[2];
-    const uint16_t* bs[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        if constexpr (GATEUP) {
-            const int n = min(n0 + 32 * wave + frow, N - 1);
-            const int64_t rb = (int64_t)nb * BB;
-            if (shared) {
-                bc[j] = (j ? L.su_codes : L.sg_codes) + (int64_t)n * rb;
-                bs[j] = (j ? L.su_scales : L.sg_scales) + (int64_t)n * nb;
-            } else {
-                const int64_t row = (int64_t)td.group * L.I + n;
-                bc[j] = (j ? L.u_codes : L.g_codes) + row * rb;
-                bs[j] = (j ? L.u_scales : L.g_scales) + row * nb;
-            }
-        } else {
-            const int m = min(n0 + 64 * wave + 32 * j + frow, H - 1);
-            const int64_t rb = (int64_t)nb * BB;
-            if (shared) {
-                bc[j] = L.sd_codes + (int64_t)m * rb;
-                bs[j] = L.sd_scales + (int64_t)m * nb;
-            } else {
-                const int64_t row = (int64_t)td.group * H + m;
-                bc[j] = L.d_codes + row * rb;
-                bs[j] = L.d_scales + row * nb;
-            }
-        }
-    }
-
-    StepSlot ring0, ring1;
-    auto ring = [&](auto rc) __attribute__((always_inline)) -> StepSlot& {
-        if constexpr (decltype(rc)::value == 0) return ring0;
-        else return ring1;
-    };
-    auto gload = [&](StepSlot& sl, int s) __attribute__((always_inline)) {
-        s = min(s, nsteps - 1);
-        const int ka = min(64 * s + 8 * ac, K - 8);   // a chunk past K reloads the last one (zeroed in lstore)
-        sl.a0 = *reinterpret_cast<const u32x4*>(arow[0] + ka);
-        sl.a1 = *reinterpret_cast<const u32x4*>(arow[1] + ka);
-        sl.a2 = *reinterpret_cast<const u32x4*>(arow[2] + ka);
-        sl.a3 = *reinterpret_cast<const u32x4*>(arow[3] + ka);
-        const int b = min(2 * s + g, nb - 1);
-        load_codes<FMT>(bc[0] + (int64_t)b * BB, sl.b0);
-        load_codes<FMT>(bc[1] + (int64_t)b * BB, sl.b1);
-        sl.s0 = bs[0][b];
-        sl.s1 = bs[1][b];
-    };
-    // A chunk past K (the second half of a last step when K % 64 == 32) is written as zeros
-    auto lstore = [&](const StepSlot& sl, int st, int s) __attribute__((always_inline)) {
-        const bool live = 64 * s + 8 * ac < K;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        _Float16* dst = &As[st][(tid >> 3) * kAS + 8 * ac];
-        *reinterpret_cast<u32x4*>(dst) = live ? sl.a0 : z;
-        *reinterpret_cast<u32x4*>(dst + 32 * kAS) = live ? sl.a1 : z;
-        *reinterpret_cast<u32x4*>(dst + 64 * kAS) = live ? sl.a2 : z;
-        *reinterpret_cast<u32x4*>(dst + 96 * kAS) = live ? sl.a3 : z;
-    };
-
-    floatx16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    // one step: dequantise this lane's blocks of slot s % 2, MFMAs against LDS stage s & 1
-    // (A fragment of lane (frow, g) for sub-step kk: row 32 i + frow, K offset 32 g + 8 kk), then
-    // A of step s + 1 into the other stage, refill the slot with step s + 2, barrier
-    auto kstep = [&](int s, auto rc) __attribute__((always_inline)) {
-        StepSlot& cur_sl = ring(rc);
-        StepSlot& nxt_sl = ring(std::integral_constant<int, 1 - decltype(rc)::value>{});
-        const int cur = s & 1;
-        const bool blive = 2 * s + g < nb;     // a block past K contributes zero
-        const _Float16 s0 = blive ? __builtin_bit_cast(_Float16, (uint16_t)cur_sl.s0) : (_Float16)0.f;
-        const _Float16 s1 = blive ? __builtin_bit_cast(_Float16, (uint16_t)cur_sl.s1) : (_Float16)0.f;
-        const half2v sv0 = {s0, s0}, sv1 = {s1, s1};
-        static_for<4>([&](auto kc) {
-            constexpr int kk = decltype(kc)::value;
-            const half8 b0 = dequant8<FMT, kk>(cur_sl.b0, sv0);
-            const half8 b1 = dequant8<FMT, kk>(cur_sl.b1, sv1);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const half8 a = *reinterpret_cast<const half8*>(&As[cur][(32 * i + frow) * kAS + 32 * g + 8 * kk]);
-                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[i][0], 0, 0, 0);
-                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[i][1], 0, 0, 0);
-            }
-        });
-        gload(cur_sl, s + 2);
-        __builtin_amdgcn_sched_barrier(0);   // issue the refill before waiting on the next step's A
-        lstore(nxt_sl, cur ^ 1, s + 1);
-        __syncthreads();
-    };
-    gload(ring0, 0);
-    gload(ring1, 1);
-    lstore(ring0, 0, 0);
-    __syncthreads();
-    // the slot of step s + 1 (read by lstore) must be complete before its refill: within a step,
-    // the refill targets slot s % 2 and lstore reads slot (s + 1) % 2
-    int s = 0;
-    for (; s + 2 <= nsteps; s += 2) {
-        kstep(s, std::integral_constant<int, 0>{});
-        kstep(s + 1, std::integral_constant<int, 1>{});
-    }
-    if (s < nsteps) kstep(s, std::integral_constant<int, 0>{});
-
-    const int rq = 4 * g;
-    if constexpr (GATEUP) {
-        const int n = n0 + 32 * wave + frow;
-        if (n < N) {
-            const int np = kperm(n, G);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
-                    if (row >= nrows) continue;
-                    const float hv = silu_mul(acc[i][0][r], acc[i][1][r]);
-                    const int64_t hrow = shared ? (int64_t)Tk + td.row0 + row : (int64_t)base + td.row0 + row;
-                    h16[hrow * Imax + np] = (_Float16)hv;
-                }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int m = n0 + 64 * wave + 32 * j + frow;
-            if (m >= H) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
-                    if (row >= nrows) continue;
-                    if (shared) y_shared[(int64_t)(td.row0 + row) * H + m] = (YT)acc[i][j][r];
-                    else y_sorted[((int64_t)base + td.row0 + row) * H + m] = (YT)acc[i][j][r];
-                }
-        }
+    switch (td.ni) {
+        case 4: gemm_tile<FMT, GATEUP, YT, 4>(L, T, td, ntile, offsets, perm, asrc, h16, y_sorted, y_shared, smem); break;
+        case 2: gemm_tile<FMT, GATEUP, YT, 2>(L, T, td, ntile, offsets, perm, asrc, h16, y_sorted, y_shared, smem); break;
+        default: gemm_tile<FMT, GATEUP, YT, 1>(L, T, td, ntile, offsets, perm, asrc, h16, y_sorted, y_shared, smem); break;
     }
 }
 
@@ -461,19 +583,19 @@ static moe_status launch_prefill_f(const LayerView& L, const uint16_t* x, int T,
     hipLaunchKernelGGL(k_x_to_f16<G>, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st, x, n16, s.x16);
     MOE_LAUNCH_CHECK();
     const int mt = max_tiles(T, L.k, L.E);
-    const int nt1 = (L.Imax() + kBN / 2 - 1) / (kBN / 2);
+    const int nt1 = (L.Imax() + 127) / 128;
     const int g1 = ((mt * nt1 + kXcds - 1) / kXcds) * kXcds;
-    hipLaunchKernelGGL((k_grouped_gemm<FMT, true>), dim3(g1), dim3(256), 0, st, L, T, s.tiles, s.ntiles, nt1,
+    hipLaunchKernelGGL((k_grouped_gemm<FMT, true>), dim3(g1), dim3(kGT), 0, st, L, T, s.tiles, s.ntiles, nt1,
                        offsets, perm, s.x16, s.h16, (float*)nullptr, (float*)nullptr);
     MOE_LAUNCH_CHECK();
-    const int nt2 = (L.H + kBN - 1) / kBN;
+    const int nt2 = (L.H + 255) / 256;
     const int g2 = ((mt * nt2 + kXcds - 1) / kXcds) * kXcds;
     if (y16)
-        hipLaunchKernelGGL((k_grouped_gemm<FMT, false, _Float16>), dim3(g2), dim3(256), 0, st, L, T, s.tiles,
+        hipLaunchKernelGGL((k_grouped_gemm<FMT, false, _Float16>), dim3(g2), dim3(kGT), 0, st, L, T, s.tiles,
                            s.ntiles, nt2, offsets, perm, s.h16, nullptr, static_cast<_Float16*>(y_sorted),
                            static_cast<_Float16*>(y_shared));
     else
-        hipLaunchKernelGGL((k_grouped_gemm<FMT, false, float>), dim3(g2), dim3(256), 0, st, L, T, s.tiles,
+        hipLaunchKernelGGL((k_grouped_gemm<FMT, false, float>), dim3(g2), dim3(kGT), 0, st, L, T, s.tiles,
                            s.ntiles, nt2, offsets, perm, s.h16, nullptr, static_cast<float*>(y_sorted),
                            static_cast<float*>(y_shared));
     MOE_LAUNCH_CHECK();
