@@ -500,7 +500,35 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
                     *reinterpret_cast<const u32x4*>(hs + row * kHS + 8 * ch);
             }
         }
+    } else if constexpr (sizeof(YT) == 2) {
+        // fp16 rows through LDS, one 32-column tile per wave at a time: pass j stages columns
+        // n0 + 64 w + 32 j + [0, 32) of every wave (staged column 32 w + frow), then whole rows
+        // leave in 16-byte pieces
+        _Float16* ys = reinterpret_cast<_Float16*>(smem);
+        YT* ybase = shared ? y_shared + (int64_t)td.row0 * H : y_sorted + ((int64_t)base + td.row0) * H;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (j) __syncthreads();
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
+                    ys[row * kHS + 32 * wave + frow] = (_Float16)acc[i][j][r];
+                }
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < 2 * NI; ++it) {
+                const int idx = tid + kGT * it;      // NI * 32 rows x 16 pieces
+                const int row = idx / 16, ch = idx % 16;
+                const int col = n0 + 64 * (ch / 4) + 32 * j + 8 * (ch % 4);
+                if (row < nrows && col < H)
+                    *reinterpret_cast<u32x4*>(ybase + (int64_t)row * H + col) =
+                        *reinterpret_cast<const u32x4*>(ys + row * kHS + 8 * ch);
+            }
+        }
     } else {
+        // fp32 rows straight from the accumulators: 32 lanes write one 128-byte row segment
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int m = n0 + 64 * wave + 32 * j + frow;
