@@ -238,18 +238,18 @@ def prefill_workload(steps: int, warmup: int):
     torch.cuda.synchronize()
     ms_per_step = a.elapsed_time(b) / steps
     value = T / (ms_per_step / 1e3)
-    # expert stage on its own
+    # expert stage on its own, in the form the layer runs it (fp16 output rows)
     offsets, perm, inv = moe.moe_permute(L, ids)
-    y_sorted = torch.empty((T * spec.k, spec.H), dtype=torch.float32, device="cuda")
-    y_sh = torch.empty((T, spec.H), dtype=torch.float32, device="cuda")
+    y_sorted = torch.empty((T * spec.k, spec.H), dtype=torch.float16, device="cuda")
+    y_sh = torch.empty((T, spec.H), dtype=torch.float16, device="cuda")
     pws = moe.Workspace()
     avg_ms = time_calls([lambda: moe.moe_experts_prefill(L, x, offsets, perm, y_sorted=y_sorted, y_shared=y_sh,
-                                                         ws=pws)], 2, max(3, steps))
+                                                         ws=pws, half=True)], 2, max(3, steps))
     flops = 6.0 * spec.H * spec.I * (T * spec.k) + 6.0 * spec.H * spec.Is * T
     achieved = flops / (avg_ms / 1e3) / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_F16_PEAK_TFS, 4), "traffic": recorded_traffic("prefill8k", "prefill"),
-            "kernel": "moe_experts_prefill (k_build_tiles + k_x_to_f16 + k_grouped_gemm gate/up + k_grouped_gemm down)",
+            "kernel": "moe_experts_prefill_f16 (k_build_tiles + k_x_to_f16 + k_grouped_gemm gate/up + k_grouped_gemm down)",
             "flops_per_launch": flops, "avg_launch_us": round(avg_ms * 1e3, 1)}
     return {"metric": "MoE-layer tokens/s (8192-token prefill chunk)", "value": round(value, 1),
             "unit": "tokens/s", "dtype": "f16", "ms_per_step": round(ms_per_step, 4), "roofline": roof,

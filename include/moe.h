@@ -169,6 +169,16 @@ moe_status moe_experts_prefill(const moe_layer_desc* desc, const moe_layer_weigh
                                float* y_shared, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_experts_prefill with the output rows in fp16 (IEEE binary16 bits, round to nearest even
+ * from the fp32 accumulators): the form the fused layer keeps between its down GEMM and its
+ * combine (half the bytes of the largest stream of the layer). Same kernels, same workspace
+ * (MOE_CALL_EXPERTS_PREFILL); y_sorted and y_shared must be 16-byte aligned.
+ */
+moe_status moe_experts_prefill_f16(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x,
+                                   int32_t T, const int32_t* offsets, const int32_t* perm, uint16_t* y_sorted,
+                                   uint16_t* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Weighted combine, atomic-free and deterministic:
  *   out[t] = sum_{j=0}^{k-1} p[t][j] * y_rows[r(t,j)] + y_shared[t]     (slot order, then shared)
  * with r(t,j) = row_of_pair[t*k+j] (e.g. inv from moe_permute) or t*k+j when row_of_pair is NULL;

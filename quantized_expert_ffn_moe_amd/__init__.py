@@ -81,6 +81,8 @@ def lib():
         L.moe_kv_gather.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp]
         L.moe_experts_prefill.restype = st
         L.moe_experts_prefill.argtypes = [D, W, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_experts_prefill_f16.restype = st
+        L.moe_experts_prefill_f16.argtypes = [D, W, vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_combine.restype = st
         L.moe_combine.argtypes = [D, i32, vp, vp, vp, vp, vp, vp]
         L.moe_layer.restype = st
@@ -244,17 +246,24 @@ def moe_experts_decode(layer: DeviceLayer, x, ids, y_pairs=None, y_shared=None, 
     return y_pairs, y_shared
 
 
-def moe_experts_prefill(layer: DeviceLayer, x, offsets, perm, y_sorted=None, y_shared=None, ws=None, stream=None):
+def moe_experts_prefill(layer: DeviceLayer, x, offsets, perm, y_sorted=None, y_shared=None, ws=None, stream=None,
+                        half=False):
+    """Grouped-GEMM experts; fp32 rows, or fp16 rows (moe_experts_prefill_f16) when half is true."""
     d = layer.desc
     T = x.shape[0]
     dev = x.device
-    y_sorted = torch.empty((T * d.top_k, d.hidden), dtype=torch.float32, device=dev) if y_sorted is None else y_sorted
+    dt = torch.float16 if half else torch.float32
+    y_sorted = torch.empty((T * d.top_k, d.hidden), dtype=dt, device=dev) if y_sorted is None else y_sorted
     if y_shared is None and d.shared_inter > 0:
-        y_shared = torch.empty((T, d.hidden), dtype=torch.float32, device=dev)
+        y_shared = torch.empty((T, d.hidden), dtype=dt, device=dev)
+    for y in (y_sorted, y_shared):
+        if y is not None and y.dtype != dt:
+            raise TypeError("moe_experts_prefill: output rows must be %s" % dt)
     buf, nb = _ws(d, T, MOE_CALL_EXPERTS_PREFILL, ws)
-    _check(lib().moe_experts_prefill(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(offsets),
-                                     _ptr(perm), _ptr(y_sorted), _ptr(y_shared), _ptr(buf), nb, _stream(stream)),
-           "moe_experts_prefill")
+    fn = lib().moe_experts_prefill_f16 if half else lib().moe_experts_prefill
+    _check(fn(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(offsets), _ptr(perm),
+              _ptr(y_sorted), _ptr(y_shared), _ptr(buf), nb, _stream(stream)),
+           "moe_experts_prefill_f16" if half else "moe_experts_prefill")
     return y_sorted, y_shared
 
 

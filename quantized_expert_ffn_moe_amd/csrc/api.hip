@@ -255,6 +255,21 @@ moe_status moe_experts_prefill(const moe_layer_desc* d, const moe_layer_weights*
                                   carve_prefill_ws(d, T, ws, nullptr).scratch, (hipStream_t)stream);
 }
 
+moe_status moe_experts_prefill_f16(const moe_layer_desc* d, const moe_layer_weights* w, const uint16_t* x,
+                                   int32_t T, const int32_t* offsets, const int32_t* perm, uint16_t* y_sorted,
+                                   uint16_t* y_shared, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(check_desc(d));
+    MOE_TRY(check_T(T));
+    MOE_TRY(check_expert_weights(d, w));
+    if (!x || !aligned16(x) || !offsets || !perm || !y_sorted || !aligned16(y_sorted)) return MOE_ERR_INVALID_ARG;
+    if (d->shared_inter > 0 && (!y_shared || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
+    size_t need = 0;
+    carve_prefill_ws(d, T, nullptr, &need);
+    MOE_TRY(check_ws(ws, ws_bytes, need));
+    return launch_prefill_experts(view(d, w), x, T, offsets, perm, y_sorted, y_shared, true,
+                                  carve_prefill_ws(d, T, ws, nullptr).scratch, (hipStream_t)stream);
+}
+
 moe_status moe_combine(const moe_layer_desc* d, int32_t T, const float* p, const float* y_rows,
                        const int32_t* row_of_pair, const float* y_shared, float* out, void* stream) {
     MOE_TRY(check_desc(d));

@@ -22,13 +22,14 @@ def built():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"moe_route", "moe_permute", "moe_experts_decode", "moe_experts_prefill", "moe_combine", "moe_layer",
-            "moe_workspace_size", "moe_status_string", "moe_abi_version", "moe_kv_encode", "moe_kv_gather"} <= set(names)
+            "moe_workspace_size", "moe_status_string", "moe_abi_version", "moe_kv_encode", "moe_kv_gather",
+            "moe_experts_prefill_f16"} <= set(names)
     L = ctypes.CDLL(moe.library_path)
     for n in names:
         assert hasattr(L, n), n
@@ -102,6 +103,11 @@ def test_host_validation_rejects_before_launch():
     # prefill with a shared expert but no y_shared
     assert _raw("moe_experts_prefill", ref(d.c), ref(w), fake, 8, fake, fake, fake, None, fake, 1 << 40, None) == \
         moe.MOE_ERR_INVALID_ARG
+    assert _raw("moe_experts_prefill_f16", ref(d.c), ref(w), fake, 8, fake, fake, fake, None, fake, 1 << 40, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    # fp16 rows must be 16-byte aligned
+    assert _raw("moe_experts_prefill_f16", ref(d.c), ref(w), fake, 8, fake, fake, fake + 2, fake, fake, 1 << 40,
+                None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_kv_validation_rejects_before_launch():

@@ -269,6 +269,36 @@ def test_experts_prefill_entry(T):
     assert_float_match(Y.cpu().numpy(), ref["Y"], "Y")
 
 
+@pytest.mark.parametrize("fmt,T,H,I,Is", [(synth.Q4, 300, 256, 128, 64), (synth.Q8, 200, 800, 160, 96),
+                                           (synth.Q2, 130, 800, 160, 0)])
+def test_experts_prefill_f16_entry(fmt, T, H, I, Is):
+    """moe_experts_prefill_f16: every fp16 row is the fp32 entry's row rounded to nearest even (same
+    accumulators), and the rows meet the float rule against the oracle."""
+    _need_gpu()
+    spec = small_prefill_spec(fmt, T, E=16, k=4, Is=Is, H=H, I=I)
+    d = synth.make_layer(spec)
+    say("experts_prefill_f16", synth.FMT_NAMES[fmt], "T=%d H=%d I=%d Is=%d" % (T, H, I, Is))
+    O = orc_layer(spec, d)
+    L = dev_layer(spec, d)
+    xd = dev_x(d["x"])
+    logits = torch.empty((T, spec.E), dtype=torch.float32, device="cuda")
+    _, ids, p = moe.moe_route(L, xd, logits=logits)
+    offsets, perm, inv = moe.moe_permute(L, ids)
+    y32, ysh32 = moe.moe_experts_prefill(L, xd, offsets, perm)
+    y16, ysh16 = moe.moe_experts_prefill(L, xd, offsets, perm, half=True)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.float16
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.float16).view(torch.int16))
+    if Is > 0:
+        assert torch.equal(ysh16.view(torch.int16), ysh32.to(torch.float16).view(torch.int16))
+    o_off, o_perm, o_inv = oracle.permute(ids.cpu().numpy(), spec.E)
+    ref = oracle_tokens(O, d["x"], logits.cpu().numpy(), range(T))
+    want_sorted = ref["y_pairs"].reshape(T * spec.k, spec.H)[o_perm]
+    assert_float_match(y16.float().cpu().numpy(), want_sorted, "y_sorted f16")
+    if Is > 0:
+        assert_float_match(ysh16.float().cpu().numpy(), ref["y_shared"], "y_shared f16")
+
+
 def test_decode_and_prefill_agree():
     """The same 4 tokens through the decode entry and the prefill entry both meet the rule."""
     _need_gpu()
