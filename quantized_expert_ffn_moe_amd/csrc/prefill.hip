@@ -56,10 +56,11 @@ struct TileDesc {
 
 // -------------------------------------------------------------------------------- tile list
 // One block of 1024 threads. Thread e < E takes expert e: floor(count / 128) full tiles and, for a
-// remainder, one tile of 32 * ni rows (ni the power of two at or above ceil(rem / 32)). Full tiles
-// come first (expert-major, then the shared group's), remainder tiles after them; block scans
-// place them. Offsets are clamped to [0, T*k] and the list to tiles_max entries, so that
-// inconsistent offsets cannot move any access out of bounds.
+// remainder, one tile of 32 * ni rows (ni the power of two at or above ceil(rem / 32)). The list is
+// expert-major (each expert's tiles side by side, so that they run on one XCD and share its L2;
+// experts of every size end up mixed along the list, which balances the XCDs), the shared group
+// last; a block scan places the experts. Offsets are clamped to [0, T*k] and the list to tiles_max
+// entries, so that inconsistent offsets cannot move any access out of bounds.
 __device__ __forceinline__ void group_rows(const int32_t* offsets, int E, int T, int Tk, int g, int& base,
                                            int& count) {
     if (g == E) { base = 0; count = T; return; }
@@ -72,42 +73,34 @@ __host__ __device__ inline int rem_tile_ni(int rem) {
     return n <= 1 ? 1 : n <= 2 ? 2 : 4;
 }
 
-__device__ __forceinline__ int block_scan_incl(int* part, int v) {
-    const int e = threadIdx.x;
-    part[e] = v;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int t = e >= d ? part[e - d] : 0;
-        __syncthreads();
-        part[e] += t;
-        __syncthreads();
-    }
-    return part[e];
-}
-
 __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict__ offsets, int E, int T, int k,
                                                       int has_shared, int tiles_max, TileDesc* __restrict__ tiles,
                                                       int32_t* __restrict__ ntiles) {
-    __shared__ int pf[1024], pr[1024];
+    __shared__ int part[1024];
     const int e = threadIdx.x;
     int base = 0, n = 0;
     if (e < E) group_rows(offsets, E, T, T * k, e, base, n);
-    const int nf = n / kTM, rem = n % kTM, hr = rem > 0 ? 1 : 0;
-    const int f_incl = block_scan_incl(pf, nf);
-    const int r_incl = block_scan_incl(pr, hr);
-    const int full_routed = pf[1023], rem_routed = pr[1023];
-    const int sf = has_shared ? T / kTM : 0, srem = has_shared ? T % kTM : 0;
-    const int rem0 = full_routed + sf;   // first remainder slot
-    auto put = [&](int slot, TileDesc d) {
-        if (slot < tiles_max) tiles[slot] = d;
-    };
-    for (int i = 0; i < nf; ++i) put(f_incl - nf + i, TileDesc{e, i * kTM, kTM / 32, 0});
-    if (hr) put(rem0 + r_incl - 1, TileDesc{e, nf * kTM, rem_tile_ni(rem), 0});
+    const int nf = n / kTM, rem = n % kTM;
+    const int nt = nf + (rem > 0 ? 1 : 0);
+    part[e] = nt;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+        const int v = e >= d ? part[e - d] : 0;
+        __syncthreads();
+        part[e] += v;
+        __syncthreads();
+    }
+    const int start = part[e] - nt;
+    for (int i = 0; i < nt && start + i < tiles_max; ++i)
+        tiles[start + i] = TileDesc{e, i * kTM, i < nf ? kTM / 32 : rem_tile_ni(rem), 0};
     if (e == 1023) {
-        for (int i = 0; i < sf; ++i) put(full_routed + i, TileDesc{E, i * kTM, kTM / 32, 0});
-        int total = rem0 + rem_routed;
-        if (srem > 0) put(total++, TileDesc{E, sf * kTM, rem_tile_ni(srem), 0});
-        *ntiles = min(total, tiles_max);
+        int total = min(part[1023], tiles_max);
+        if (has_shared) {
+            const int sf = T / kTM, srem = T % kTM;
+            for (int i = 0; i < sf + (srem > 0 ? 1 : 0) && total < tiles_max; ++i)
+                tiles[total++] = TileDesc{E, i * kTM, i < sf ? kTM / 32 : rem_tile_ni(srem), 0};
+        }
+        *ntiles = total;
     }
 }
 
