@@ -143,7 +143,6 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
 
 // -------------------------------------------------------------------------------- dequantisation
 
-constexpr uint32_t kMagic16 = 0x64006400u;   // (1024.0, 1024.0) as fp16 pair
 
 __device__ __forceinline__ uint32_t h2bits(half2v v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ half2v bits2h(uint32_t u) { return __builtin_bit_cast(half2v, u); }
@@ -183,32 +182,53 @@ __device__ __forceinline__ uint32_t dword_of(const BlockCodes& b, int d) {
 
 // Pairs 4 kk .. 4 kk + 3 of a block (K-permuted positions 8 kk .. 8 kk + 7) as level * scale,
 // each rounded once to fp16. Pair p of a block holds elements (j, j + G/2) of its G-group:
-//   Q4: dword d = elements 8d .. 8d+7 (offset binary after the xor), pair 4d + j = nibbles
-//       (j, j + 4). Nibbles at bits 0-3 (j = 0, and j = 2 after a shift by 8) land in the mantissa
-//       of 1024.0 (1024 + n, offset 1032); nibbles at bits 4-7 (j = 1, 3) in that of 64.0, whose
-//       last mantissa bit is worth 1/16 (64 + n, offset 72): one and-or per pair, no shifts.
+//   Q4: dword d = elements 8d .. 8d+7, pair 4d + j = nibbles (j, j + 4), each read as offset
+//       binary n = code + 8 (its top bit flipped). Nibbles at bits 0-3 (j = 0, and j = 2 after a
+//       shift by 8) land in the mantissa of 1024.0 (1024 + n, offset 1032); nibbles at bits 4-7
+//       (j = 1, 3) in that of 64.0, whose last mantissa bit is worth 1/16 (64 + n, offset 72): one
+//       three-input bit operation per pair (mask, flip, exponent), no shifts.
 //   Q8: dword d = elements 4d .. 4d+3, pairs 2d (bytes 0, 2) and 2d + 1 (bytes 1, 3): one byte
 //       permute puts two codes under the exponent byte of 1024.0 (1024 + b, offset 1152).
 //   Q2: dword d = elements 16d .. 16d+15, pair 8d + j = crumbs (j, j + 8) as 2c + 1024, offset
 //       1027 = 1024 + 2 * 1.5, times s / 2.
+// The exponent patterns come in as register values (DequantConsts) rather than literals: an
+// and-or (or a byte permute) can then take its mask as its one literal and run as one instruction.
+struct DequantConsts {
+    uint32_t m1024;   // 0x64006400: (1024.0, 1024.0)
+    uint32_t q4lo;    // 0x64086408: (1024.0, 1024.0) with the sign flips of nibbles 0 and 4
+    uint32_t q4hi;    // 0x54805480: (64.0, 64.0) with the sign flips of nibbles 1 and 5
+    uint32_t b64;     // 0x64646464: four copies of the exponent byte of 1024.0
+};
+
+__device__ __forceinline__ DequantConsts dequant_consts() {
+    DequantConsts c;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(c.m1024));
+    asm volatile("v_mov_b32 %0, 0x64086408" : "=v"(c.q4lo));
+    asm volatile("v_mov_b32 %0, 0x54805480" : "=v"(c.q4hi));
+    asm volatile("v_mov_b32 %0, 0x64646464" : "=v"(c.b64));
+    return c;
+}
+
 template <int FMT, int KK>
-__device__ __forceinline__ half8 dequant8(const BlockCodes& b, half2v sv) {
+__device__ __forceinline__ half8 dequant8(const BlockCodes& b, half2v sv, const DequantConsts& q) {
     uint32_t o[4];
     if constexpr (FMT == MOE_Q4_B32) {
         const half2v off0 = {(_Float16)1032.f, (_Float16)1032.f}, off1 = {(_Float16)72.f, (_Float16)72.f};
-        const uint32_t u = dword_of(b, KK) ^ 0x88888888u, v = u >> 8;
-        o[0] = h2bits((bits2h((u & 0x000F000Fu) | kMagic16) - off0) * sv);
-        o[1] = h2bits((bits2h((u & 0x00F000F0u) | 0x54005400u) - off1) * sv);
-        o[2] = h2bits((bits2h((v & 0x000F000Fu) | kMagic16) - off0) * sv);
-        o[3] = h2bits((bits2h((v & 0x00F000F0u) | 0x54005400u) - off1) * sv);
+        // (u & mask) ^ pattern: the mantissa bits take the nibbles with their top bit flipped (two's
+        // complement -> offset binary), every other bit the exponent pattern
+        const uint32_t u = dword_of(b, KK), v = u >> 8;
+        o[0] = h2bits((bits2h((u & 0x000F000Fu) ^ q.q4lo) - off0) * sv);
+        o[1] = h2bits((bits2h((u & 0x00F000F0u) ^ q.q4hi) - off1) * sv);
+        o[2] = h2bits((bits2h((v & 0x000F000Fu) ^ q.q4lo) - off0) * sv);
+        o[3] = h2bits((bits2h((v & 0x00F000F0u) ^ q.q4hi) - off1) * sv);
     } else if constexpr (FMT == MOE_Q8_B32) {
         const half2v off = {(_Float16)1152.f, (_Float16)1152.f};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t u = dword_of(b, 2 * KK + h) ^ 0x80808080u;
             // bytes {u0, 0x64, u2, 0x64} and {u1, 0x64, u3, 0x64}
-            o[2 * h] = h2bits((bits2h(__builtin_amdgcn_perm(0x64646464u, u, 0x04020400u)) - off) * sv);
-            o[2 * h + 1] = h2bits((bits2h(__builtin_amdgcn_perm(0x64646464u, u, 0x04030401u)) - off) * sv);
+            o[2 * h] = h2bits((bits2h(__builtin_amdgcn_perm(q.b64, u, 0x04020400u)) - off) * sv);
+            o[2 * h + 1] = h2bits((bits2h(__builtin_amdgcn_perm(q.b64, u, 0x04030401u)) - off) * sv);
         }
     } else {
         const half2v off = {(_Float16)1027.f, (_Float16)1027.f};
@@ -219,7 +239,7 @@ __device__ __forceinline__ half8 dequant8(const BlockCodes& b, half2v sv) {
             constexpr int j0 = 4 * (KK % 2);
             const int j = j0 + jj;
             const uint32_t t = j == 0 ? (u << 1) : (u >> (2 * j - 1));
-            o[jj] = h2bits((bits2h((t & 0x00060006u) | kMagic16) - off) * s2);
+            o[jj] = h2bits((bits2h((t & 0x00060006u) | q.m1024) - off) * s2);
         }
     }
     return __builtin_bit_cast(half8, u32x4{o[0], o[1], o[2], o[3]});
@@ -407,6 +427,7 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
         }
     };
 
+    const DequantConsts dq = dequant_consts();
     floatx16 acc[NI][2];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
@@ -443,8 +464,8 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
             half8 (&nxt_a)[NI] = (kk % 2 == 0) ? fb : fa;
             if constexpr (kk < 3) frag(std::integral_constant<int, kk + 1>{}, nxt_a);
             __builtin_amdgcn_sched_barrier(0);
-            const half8 b0 = dequant8<FMT, kk>(cur[0].b, sv0);
-            const half8 b1 = dequant8<FMT, kk>(cur[1].b, sv1);
+            const half8 b0 = dequant8<FMT, kk>(cur[0].b, sv0, dq);
+            const half8 b1 = dequant8<FMT, kk>(cur[1].b, sv1, dq);
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur_a[i], b0, acc[i][0], 0, 0, 0);
