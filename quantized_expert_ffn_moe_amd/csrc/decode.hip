@@ -368,86 +368,86 @@ __global__ __launch_bounds__(1024) void k_dec_gateup(LayerView L, const uint16_t
         for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += blockDim.x) dst[i] = src[i];
     }
 
+    // the rows of the distinct chosen experts (slot order) then the shared expert's, R per wave
+    // and step, the grid striding over them (a grid of at most one block per CU)
     const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave;
-    const int64_t r0 = gw * R;
-    int slot = -1, n0 = 0;
-    const uint8_t *gc = nullptr, *uc = nullptr;
-    const uint16_t *gs = nullptr, *us = nullptr;
+    const int64_t nrouted = (int64_t)P.nU * L.I;
+    const int64_t nreal = nrouted + L.Is;
+    const int64_t wstride = (int64_t)gridDim.x * (blockDim.x / kWave) * R;
     const int64_t rb = row_bytes(FMT, H);
-    if (r0 < (int64_t)npairs * L.I) {
-        const int sl = (int)(r0 / L.I);
-        n0 = (int)(r0 % L.I);
-        if (sl < P.nU) {
-            slot = sl;
+    for (int64_t r0 = gw * R; r0 < nreal; r0 += wstride) {   // uniform per wave
+        int slot, n0;
+        const uint8_t *gc, *uc;
+        const uint16_t *gs, *us;
+        if (r0 < nrouted) {
+            slot = (int)(r0 / L.I);
+            n0 = (int)(r0 % L.I);
             const int64_t row = (int64_t)P.expert[slot] * L.I + n0;
             gc = L.g_codes + row * rb; uc = L.u_codes + row * rb;
             gs = L.g_scales + row * nb; us = L.u_scales + row * nb;
-        }
-    } else {
-        n0 = (int)(r0 - (int64_t)npairs * L.I);
-        if (L.Is > 0 && n0 < L.Is) {
+        } else {
             slot = 64;  // shared
+            n0 = (int)(r0 - nrouted);
             gc = L.sg_codes + (int64_t)n0 * rb; uc = L.su_codes + (int64_t)n0 * rb;
             gs = L.sg_scales + (int64_t)n0 * nb; us = L.su_scales + (int64_t)n0 * nb;
         }
-    }
-    if (slot < 0) return;   // uniform per wave
 
-    const uint32_t mask = slot < 64 ? P.tokmask[slot] : (1u << T) - 1u;
-    float g[R][T], u[R][T];
+        const uint32_t mask = slot < 64 ? P.tokmask[slot] : (1u << T) - 1u;
+        float g[R][T], u[R][T];
 #pragma unroll
-    for (int i = 0; i < R; ++i)
+        for (int i = 0; i < R; ++i)
 #pragma unroll
-        for (int t = 0; t < T; ++t) g[i][t] = u[i][t] = 0.f;
-    for (int b = lane; b < nb; b += kWave) {
-        uint32_t wg[R][8], wu[R][8];
-        uint16_t sgb[R], sub[R];
-        // every load of the step issued before any is used (scales first: the compiler would
-        // otherwise sink them behind the code arithmetic, costing a second round trip)
+            for (int t = 0; t < T; ++t) g[i][t] = u[i][t] = 0.f;
+        for (int b = lane; b < nb; b += kWave) {
+            uint32_t wg[R][8], wu[R][8];
+            uint16_t sgb[R], sub[R];
+            // every load of the step issued before any is used (scales first: the compiler would
+            // otherwise sink them behind the code arithmetic, costing a second round trip)
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            sgb[i] = gs[i * nb + b];
-            sub[i] = us[i * nb + b];
-        }
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            load_codes<FMT>(gc + i * rb + (int64_t)b * block_bytes(FMT), wg[i]);
-            load_codes<FMT>(uc + i * rb + (int64_t)b * block_bytes(FMT), wu[i]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            uint32_t xr[16];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint4 v = xq[((size_t)t * 4 + c) * nb + b];
-                xr[4 * c] = v.x; xr[4 * c + 1] = v.y; xr[4 * c + 2] = v.z; xr[4 * c + 3] = v.w;
+            for (int i = 0; i < R; ++i) {
+                sgb[i] = gs[i * nb + b];
+                sub[i] = us[i * nb + b];
             }
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                uint32_t pg[16], pu[16];
-                code_pairs<FMT>(wg[i], pg);
-                code_pairs<FMT>(wu[i], pu);
-                float dg = 0.f, du = 0.f;
+                load_codes<FMT>(gc + i * rb + (int64_t)b * block_bytes(FMT), wg[i]);
+                load_codes<FMT>(uc + i * rb + (int64_t)b * block_bytes(FMT), wu[i]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) { dg = dot2(pg[j], xr[j], dg); du = dot2(pu[j], xr[j], du); }
-                g[i][t] += f16_to_f32(sgb[i]) * dg;
-                u[i][t] += f16_to_f32(sub[i]) * du;
+            for (int t = 0; t < T; ++t) {
+                uint32_t xr[16];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint4 v = xq[((size_t)t * 4 + c) * nb + b];
+                    xr[4 * c] = v.x; xr[4 * c + 1] = v.y; xr[4 * c + 2] = v.z; xr[4 * c + 3] = v.w;
+                }
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    uint32_t pg[16], pu[16];
+                    code_pairs<FMT>(wg[i], pg);
+                    code_pairs<FMT>(wu[i], pu);
+                    float dg = 0.f, du = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) { dg = dot2(pg[j], xr[j], dg); du = dot2(pu[j], xr[j], du); }
+                    g[i][t] += f16_to_f32(sgb[i]) * dg;
+                    u[i][t] += f16_to_f32(sub[i]) * du;
+                }
             }
         }
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const float gs_ = wave_sum(g[i][t]);
+                const float us_ = wave_sum(u[i][t]);
+                if (lane == 0 && ((mask >> t) & 1u)) {
+                    const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
+                    put_staged<FMT>(reinterpret_cast<_Float16*>(h + (size_t)row * Imax), Imax / 32, n0 + i,
+                                    silu_mul(gs_, us_));
+                }
+            }
     }
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const float gs_ = wave_sum(g[i][t]);
-            const float us_ = wave_sum(u[i][t]);
-            if (lane == 0 && ((mask >> t) & 1u)) {
-                const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
-                put_staged<FMT>(reinterpret_cast<_Float16*>(h + (size_t)row * Imax), Imax / 32, n0 + i,
-                                silu_mul(gs_, us_));
-            }
-        }
 }
 
 // ----------------------------------------------------------------------------------- K3 down
@@ -693,6 +693,19 @@ static bool allow_smem(K kernel, size_t bytes) {
                                (int)bytes) == hipSuccess;
 }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <int FMT, int T, bool ROUTE, int KPL>
 static moe_status launch_gateup(const LayerView& L, const uint16_t* x, const float* logits, int32_t* ids, float* p,
                                 float* h, DecodePlan* plan_g, hipStream_t s) {
@@ -701,10 +714,13 @@ static moe_status launch_gateup(const LayerView& L, const uint16_t* x, const flo
     const size_t sm = gateup_smem_bytes(T, L.H, L.E);
     auto kern = k_dec_gateup<FMT, T, ROUTE, KPL>;
     if (!allow_smem(kern, sm)) return MOE_ERR_UNSUPPORTED;
-    // waves per block chosen so that the blocks spread evenly over the 256 CUs (4..16 waves)
-    const int64_t wpb = std::min<int64_t>(16, std::max<int64_t>(4, (waves1 + 255) / 256));
-    hipLaunchKernelGGL(kern, dim3((unsigned)((waves1 + wpb - 1) / wpb)), dim3((unsigned)(wpb * kWave)), sm, s, L, x,
-                       logits, ids, p, h, plan_g);
+    // waves per block chosen so that the blocks spread evenly over the CUs (4..16 waves), and at
+    // most one block per CU: the waves stride over the rows of the experts actually chosen
+    const int cus = cu_count();
+    const int64_t wpb = std::min<int64_t>(16, std::max<int64_t>(4, (waves1 + cus - 1) / cus));
+    const int64_t blocks = std::min<int64_t>((waves1 + wpb - 1) / wpb, cus);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3((unsigned)(wpb * kWave)), sm, s, L, x, logits, ids, p, h,
+                       plan_g);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
