@@ -24,6 +24,8 @@
 //                    shared expert (combine fused), or written per pair for moe_experts_decode.
 #include <algorithm>
 
+#include <atomic>
+
 #include "kernels.h"
 
 namespace moe {
@@ -693,17 +695,18 @@ static bool allow_smem(K kernel, size_t bytes) {
                                (int)bytes) == hipSuccess;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; callers on several host threads may
+// race to fill an entry, with the same value).
 static int cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 template <int FMT, int T, bool ROUTE, int KPL>

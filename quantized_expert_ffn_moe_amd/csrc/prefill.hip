@@ -8,7 +8,8 @@
 //   - one kernel template, two uses: gate/up (A = x rows gathered through perm; each wave's two
 //     32-row weight tiles are gate and up rows of the same h columns, so SwiGLU pairs them in one
 //     lane; h is written in fp16 through LDS with full-row stores) and down (A = h rows in sorted
-//     order; outputs stored from the accumulators);
+//     order; fp16 outputs leave through LDS as whole-row pieces, fp32 ones straight from the
+//     accumulators);
 //   - a block is 4 waves over a tile of up to 128 rows x 256 weight rows, two blocks per CU so that
 //     one block's prologue, barriers and stores overlap the other's MFMAs; each wave computes all
 //     rows of the tile against its own 64 weight rows with v_mfma_f32_32x32x16_f16 (on this chip
@@ -18,12 +19,12 @@
 //     steps ahead, each 128-byte row segment XOR-swizzled in 16-byte slots so that the fragment
 //     reads of 16 lanes hit distinct banks; one barrier per K step of 64;
 //   - weights never touch LDS: each lane loads the codes and scale of one 32-block of its weight
-//     row (two steps ahead, in named register slots) and dequantises them straight into its MFMA
-//     operand: the code is OR-ed into the mantissa of 1024.0, the offset subtracted (an exact fp16
-//     level) and multiplied by the fp16 scale with packed fp16 arithmetic, i.e. level * scale
-//     rounded once to fp16. The pairs come out in an order that permutes K inside each 4-, 8- or
-//     16-element group; x (converted from bf16) and h are stored with the same permutation so the
-//     dot products are unchanged;
+//     row (two steps ahead, in named register slots, through buffer descriptors) and dequantises
+//     them straight into its MFMA operand: the code is placed in the mantissa of an fp16 power of
+//     two, the offset subtracted (an exact fp16 level) and multiplied by the fp16 scale with packed
+//     fp16 arithmetic, i.e. level * scale rounded once to fp16. The pairs come out in an order that
+//     permutes K inside each 4-, 8- or 16-element group; x (converted from bf16) and h are stored
+//     with the same permutation so the dot products are unchanged;
 //   - blocks are mapped so that consecutive row tiles of one expert (which share a weight panel)
 //     run on the same XCD and reuse it from that XCD's L2.
 #include <utility>
@@ -40,7 +41,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kTM = 128;                   // rows of a full tile
-constexpr int kGW = 4;                     // waves per block (one per SIMD)
+constexpr int kGW = 4;                     // waves per block (two blocks per CU)
 constexpr int kGT = kGW * kWave;           // threads per block
 constexpr int kStages = 3;                 // A stages in LDS
 constexpr int kStageBytes = kTM * 128;     // one K step (64 fp16) of 128 rows
