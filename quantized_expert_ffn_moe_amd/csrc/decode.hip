@@ -81,42 +81,49 @@ __device__ void build_plan_wave(const int32_t* __restrict__ ids, const float* __
 
 // ----------------------------------------------------------------------------------- K1 router
 
+// One block of four waves per expert row: wave w takes the float4 chunks w, w + 4, w + 8, ... of
+// the row (every W_r and x chunk of a lane loaded before any is used), the four partial sums meet
+// in LDS. One block per expert spreads the 2 MB of W_r over as many CUs as there are experts.
 template <int T>
 __global__ __launch_bounds__(256) void k_route_gemv(const float* __restrict__ w_r, const float* __restrict__ bias,
                                                     const uint16_t* __restrict__ x, int H, int E,
                                                     float* __restrict__ logits) {
+    __shared__ float part[4][T];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int e = blockIdx.x * 4 + wave;
-    if (e >= E) return;
-    // all of a lane's W_r and x chunks are loaded before any is used (8 in flight per group)
+    const int e = blockIdx.x;
     const float4* wr = reinterpret_cast<const float4*>(w_r + (size_t)e * H);
     float acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = 0.f;
     const int nch = H / 4;
-    for (int c0 = 0; c0 < nch; c0 += 8 * kWave) {
-        float4 wv[8];
-        uint2 xv[T][8];
+    for (int c0 = 0; c0 < nch; c0 += 2 * 256) {
+        float4 wv[2];
+        uint2 xv[T][2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = c0 + i * kWave + lane;
+        for (int i = 0; i < 2; ++i) {
+            const int c = c0 + i * 256 + threadIdx.x;
             wv[i] = c < nch ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int t = 0; t < T; ++t)
                 xv[t][i] = c < nch ? reinterpret_cast<const uint2*>(x + (size_t)t * H)[c] : make_uint2(0u, 0u);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int t = 0; t < T; ++t)
                 acc[t] += wv[i].x * bf16_lo(xv[t][i].x) + wv[i].y * bf16_hi(xv[t][i].x) +
                           wv[i].z * bf16_lo(xv[t][i].y) + wv[i].w * bf16_hi(xv[t][i].y);
     }
-    const float b = bias ? bias[e] : 0.f;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const float s = wave_sum(acc[t]);
-        if (lane == 0) logits[(size_t)t * E + e] = s + b;
+        if (lane == 0) part[wave][t] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < T) {
+        const int t = threadIdx.x;
+        const float b = bias ? bias[e] : 0.f;
+        logits[(size_t)t * E + e] = ((part[0][t] + part[1][t]) + (part[2][t] + part[3][t])) + b;
     }
 }
 
@@ -656,7 +663,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
 
 moe_status launch_route_gemv(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
                              float* logits, hipStream_t s) {
-    const dim3 grid((E + 3) / 4), block(256);
+    const dim3 grid(E), block(256);
     switch (T) {
         case 1: hipLaunchKernelGGL(k_route_gemv<1>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
         case 2: hipLaunchKernelGGL(k_route_gemv<2>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
