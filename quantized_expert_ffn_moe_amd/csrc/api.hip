@@ -204,10 +204,10 @@ moe_status moe_route(const moe_layer_desc* d, const moe_layer_weights* w, const 
     const RouteWs rw = (!logits || split) ? carve_route(d, T, ws, nullptr) : RouteWs{nullptr, nullptr};
     float* lg = logits ? logits : rw.logits;
     hipStream_t s = (hipStream_t)stream;
-    if (T <= 4)
-        MOE_TRY(launch_route_gemv(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, lg, s));
-    else
-        MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, lg, rw.part, s));
+    if (T > 4)
+        return launch_route_topk(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, d->top_k, lg, ids, p,
+                                 rw.part, s);
+    MOE_TRY(launch_route_gemv(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, lg, s));
     return launch_topk(lg, T, d->num_experts, d->top_k, ids, p, s);
 }
 
@@ -323,8 +323,7 @@ moe_status moe_layer(const moe_layer_desc* d, const moe_layer_weights* w, const 
     // the expert outputs between the down GEMM and the combine are fp16 rows here (half the bytes
     // of the largest stream); the combine sums them in fp32
     const _Float16* ysh = d->shared_inter > 0 ? lw.y_shared : nullptr;
-    MOE_TRY(launch_router(w->w_router, w->router_bias, x, T, L.H, L.E, lg, lw.router_part, s));
-    MOE_TRY(launch_topk(lg, T, L.E, L.k, id, pr, s));
+    MOE_TRY(launch_route_topk(w->w_router, w->router_bias, x, T, L.H, L.E, L.k, lg, id, pr, lw.router_part, s));
     MOE_TRY(launch_permute(id, T, L.k, L.E, lw.offsets, lw.perm, lw.inv, lw.chunks, s));
     MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, true, lw.prefill, s));
     return launch_combine_f16(T, L.k, L.H, pr, lw.y_rows, lw.inv, ysh, out, s);

@@ -159,16 +159,10 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 // k rounds of a DPP wave max of the order-preserving key, ties resolved to the lowest index with
 // ballots; lane j < k ends with the j-th expert and its softmax weight over the chosen k (the
 // first chosen, i.e. largest, logit is subtracted before exp).
+// topk_wave_regs takes the logits already in registers (lv[i] = logit of expert lane + 64 i).
 template <int KPL>
-__device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, int k, int& my_id, float& my_p) {
+__device__ __forceinline__ void topk_wave_regs(const float (&lv)[KPL], int E, int k, int& my_id, float& my_p) {
     const int lane = threadIdx.x % kWave;
-    // all KPL loads issued unconditionally before any is used (the empty asm pins each value, so the
-    // compiler cannot sink a load into the e < E branch and serialise the round trips)
-    float lv[KPL];
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) lv[i] = l[min(lane + kWave * i, E - 1)];
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) asm volatile("" : "+v"(lv[i]));
     uint32_t key[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) key[i] = lane + kWave * i < E ? ordered_key(lv[i]) : 0u;
@@ -196,6 +190,19 @@ __device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, in
     const float s = wave_sum(ex);
     my_id = mine;
     my_p = ex / s;
+}
+
+template <int KPL>
+__device__ __forceinline__ void topk_wave(const float* __restrict__ l, int E, int k, int& my_id, float& my_p) {
+    const int lane = threadIdx.x % kWave;
+    // all KPL loads issued unconditionally before any is used (the empty asm pins each value, so the
+    // compiler cannot sink a load into the e < E branch and serialise the round trips)
+    float lv[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) lv[i] = l[min(lane + kWave * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) asm volatile("" : "+v"(lv[i]));
+    topk_wave_regs<KPL>(lv, E, k, my_id, my_p);
 }
 
 }  // namespace moe

@@ -24,6 +24,9 @@ size_t router_scratch_bytes(int T, int H, int E);
 moe_status launch_router(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
                          float* logits, float* scratch, hipStream_t s);
 moe_status launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* p, hipStream_t s);
+// Router GEMM + top-k; with a split K the reduction and the top-k run as one kernel.
+moe_status launch_route_topk(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E, int k,
+                             float* logits, int32_t* ids, float* p, float* scratch, hipStream_t s);
 
 // permutation: counts/bases scratch of chunks(T) * E ints
 int perm_chunks(int T);

@@ -31,8 +31,8 @@ struct RouterSlot {
 };
 
 // Split K (blockIdx.y = split s of `splits`): with more than one split every block writes fp32 partial
-// sums of its K range to part[s][T][E] and k_router_reduce adds them in split order plus the bias
-// (deterministic); with one split the block writes logits + bias directly.
+// sums of its K range to part[s][T][E] and k_router_reduce (or k_router_reduce_topk) adds them in
+// split order plus the bias (deterministic); with one split the block writes logits + bias directly.
 __global__ __launch_bounds__(256, 2) void k_router_mfma(const float* __restrict__ w_r, const float* __restrict__ bias,
                                                         const uint16_t* __restrict__ x, int T, int H, int E,
                                                         float* __restrict__ logits, int splits,
@@ -169,6 +169,40 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
     }
 }
 
+// Split-K reduction fused with the top-k: one wave per token adds the partial sums of its experts
+// in split order plus the bias (the logits written are the values the top-k sees), then selects.
+template <int KPL>
+__global__ __launch_bounds__(256) void k_router_reduce_topk(const float* __restrict__ part, int splits, int T,
+                                                            int E, int k, const float* __restrict__ bias,
+                                                            float* __restrict__ logits, int32_t* __restrict__ ids,
+                                                            float* __restrict__ p) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    float lv[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) lv[i] = 0.f;
+    const int64_t stride = (int64_t)T * E;
+    for (int sp = 0; sp < splits; ++sp) {
+        const float* ps = part + sp * stride + (int64_t)t * E;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) lv[i] += ps[min(lane + kWave * i, E - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const int e = lane + kWave * i;
+        lv[i] += bias ? bias[min(e, E - 1)] : 0.f;
+        if (e < E) logits[(int64_t)t * E + e] = lv[i];
+    }
+    int id;
+    float pr;
+    topk_wave_regs<KPL>(lv, E, k, id, pr);
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = id;
+        p[(size_t)t * k + lane] = pr;
+    }
+}
+
 // ----------------------------------------------------------------------------- launchers
 
 // Splits of K for the router GEMM: enough blocks to occupy the GPU when T is small, at least four
@@ -200,6 +234,28 @@ moe_status launch_router(const float* w_r, const float* bias, const uint16_t* x,
                            bias, logits);
         MOE_LAUNCH_CHECK();
     }
+    return MOE_OK;
+}
+
+moe_status launch_route_topk(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E, int k,
+                             float* logits, int32_t* ids, float* p, float* scratch, hipStream_t s) {
+    const int sp = router_splits(T, H, E);
+    if (sp == 1) {
+        const moe_status st = launch_router(w_r, bias, x, T, H, E, logits, scratch, s);
+        return st != MOE_OK ? st : launch_topk(logits, T, E, k, ids, p, s);
+    }
+    if (!scratch) return MOE_ERR_WORKSPACE;
+    const int blocks = ((T + kRtM - 1) / kRtM) * ((E + kRtN - 1) / kRtN);
+    const int grid = ((blocks + kRtXcds - 1) / kRtXcds) * kRtXcds;
+    hipLaunchKernelGGL(k_router_mfma, dim3(grid, sp), dim3(256), 0, s, w_r, bias, x, T, H, E, logits, sp, scratch);
+    MOE_LAUNCH_CHECK();
+    const dim3 g2((T + 3) / 4), b2(256);
+    if (E <= 64) hipLaunchKernelGGL(k_router_reduce_topk<1>, g2, b2, 0, s, scratch, sp, T, E, k, bias, logits, ids, p);
+    else if (E <= 128) hipLaunchKernelGGL(k_router_reduce_topk<2>, g2, b2, 0, s, scratch, sp, T, E, k, bias, logits, ids, p);
+    else if (E <= 256) hipLaunchKernelGGL(k_router_reduce_topk<4>, g2, b2, 0, s, scratch, sp, T, E, k, bias, logits, ids, p);
+    else if (E <= 512) hipLaunchKernelGGL(k_router_reduce_topk<8>, g2, b2, 0, s, scratch, sp, T, E, k, bias, logits, ids, p);
+    else hipLaunchKernelGGL(k_router_reduce_topk<16>, g2, b2, 0, s, scratch, sp, T, E, k, bias, logits, ids, p);
+    MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
 
