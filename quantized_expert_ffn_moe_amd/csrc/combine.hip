@@ -6,27 +6,33 @@
 
 namespace moe {
 
-// Rows are fp32 (the C-ABI call) or fp16 (the fused layer's internal rows); the sum is fp32 either way.
+// Rows are fp32 (the C-ABI call) or fp16 (the fused layer's internal rows); the sum is fp32 either
+// way. A thread owns 8 consecutive columns of one token: 32 bytes of an fp32 row or 16 of an fp16 one.
 template <typename RT>
-__device__ __forceinline__ float4 load4(const RT* row, int c);
+__device__ __forceinline__ void load8(const RT* row, int c8, float (&v)[8]);
 template <>
-__device__ __forceinline__ float4 load4<float>(const float* row, int c) {
-    return reinterpret_cast<const float4*>(row)[c];
+__device__ __forceinline__ void load8<float>(const float* row, int c8, float (&v)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(row)[2 * c8];
+    const float4 b = reinterpret_cast<const float4*>(row)[2 * c8 + 1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 template <>
-__device__ __forceinline__ float4 load4<_Float16>(const _Float16* row, int c) {
-    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-    const half4 v = reinterpret_cast<const half4*>(row)[c];
-    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+__device__ __forceinline__ void load8<_Float16>(const _Float16* row, int c8, float (&v)[8]) {
+    typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+    const half8_t h = reinterpret_cast<const half8_t*>(row)[c8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)h[e];
 }
 
+// The k rows of a token are read four at a time with every load of a group in flight before any
+// is used (a dropped pair reads row 0 and adds nothing); the sum stays in slot order.
 template <typename RT>
 __global__ __launch_bounds__(256) void k_combine(int T, int k, int H, const float* __restrict__ p,
                                                  const RT* __restrict__ y_rows,
                                                  const int32_t* __restrict__ row_of_pair,
                                                  const RT* __restrict__ y_shared, float* __restrict__ out) {
     const int t = blockIdx.y;
-    const int c = blockIdx.x * blockDim.x + threadIdx.x;  // float4 column
+    const int c8 = blockIdx.x * blockDim.x + threadIdx.x;  // group of 8 columns
     __shared__ float ps[16];
     __shared__ int rows[16];
     if (threadIdx.x < k) {
@@ -35,24 +41,41 @@ __global__ __launch_bounds__(256) void k_combine(int T, int k, int H, const floa
         rows[threadIdx.x] = row_of_pair ? row_of_pair[q] : q;
     }
     __syncthreads();
-    if (c >= H / 4) return;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        if ((unsigned)rows[j] >= (unsigned)(T * k)) continue;  // dropped pair
-        const float4 v = load4<RT>(y_rows + (size_t)rows[j] * H, c);
-        const float pj = ps[j];
-        acc.x += pj * v.x; acc.y += pj * v.y; acc.z += pj * v.z; acc.w += pj * v.w;
+    if (c8 >= H / 8) return;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += 4) {
+        float v[4][8];
+        bool ok[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int r = j0 + jj < k ? rows[j0 + jj] : -1;
+            ok[jj] = (unsigned)r < (unsigned)(T * k);
+            load8<RT>(y_rows + (size_t)(ok[jj] ? r : 0) * H, c8, v[jj]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            if (!ok[jj]) continue;
+            const float pj = ps[j0 + jj];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += pj * v[jj][e];
+        }
     }
     if (y_shared) {
-        const float4 v = load4<RT>(y_shared + (size_t)t * H, c);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        float v[8];
+        load8<RT>(y_shared + (size_t)t * H, c8, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += v[e];
     }
-    reinterpret_cast<float4*>(out + (size_t)t * H)[c] = acc;
+    float4* o = reinterpret_cast<float4*>(out + (size_t)t * H) + 2 * c8;
+    o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 moe_status launch_combine(int T, int k, int H, const float* p, const float* y_rows, const int32_t* row_of_pair,
                           const float* y_shared, float* out, hipStream_t s) {
-    const int cols = H / 4;
+    const int cols = H / 8;
     dim3 grid((cols + 255) / 256, T);
     hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, s, T, k, H, p, y_rows, row_of_pair, y_shared, out);
     MOE_LAUNCH_CHECK();
@@ -61,7 +84,7 @@ moe_status launch_combine(int T, int k, int H, const float* p, const float* y_ro
 
 moe_status launch_combine_f16(int T, int k, int H, const float* p, const _Float16* y_rows,
                               const int32_t* row_of_pair, const _Float16* y_shared, float* out, hipStream_t s) {
-    const int cols = H / 4;
+    const int cols = H / 8;
     dim3 grid((cols + 255) / 256, T);
     hipLaunchKernelGGL(k_combine<_Float16>, grid, dim3(256), 0, s, T, k, H, p, y_rows, row_of_pair, y_shared, out);
     MOE_LAUNCH_CHECK();
