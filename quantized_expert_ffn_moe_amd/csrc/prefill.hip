@@ -60,8 +60,9 @@ struct TileDesc {
 // remainder, one tile of 32 * ni rows (ni the power of two at or above ceil(rem / 32)). The list is
 // expert-major (each expert's tiles side by side, so that they run on one XCD and share its L2;
 // experts of every size end up mixed along the list, which balances the XCDs), the shared group
-// last; a block scan places the experts. Offsets are clamped to [0, T*k] and the list to tiles_max
-// entries, so that inconsistent offsets cannot move any access out of bounds.
+// last; a block scan places the experts and all threads write the list. Offsets are clamped to
+// [0, T*k] and the list to tiles_max entries, so that inconsistent offsets cannot move any access
+// out of bounds.
 __device__ __forceinline__ void group_rows(const int32_t* offsets, int E, int T, int Tk, int g, int& base,
                                            int& count) {
     if (g == E) { base = 0; count = T; return; }
@@ -77,12 +78,14 @@ __host__ __device__ inline int rem_tile_ni(int rem) {
 __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict__ offsets, int E, int T, int k,
                                                       int has_shared, int tiles_max, TileDesc* __restrict__ tiles,
                                                       int32_t* __restrict__ ntiles) {
-    __shared__ int part[1024];
+    __shared__ int part[1024];   // inclusive prefix of the tile counts, then tile rows of each group
+    __shared__ int cnt[1025];    // rows of each group (the shared group last)
     const int e = threadIdx.x;
     int base = 0, n = 0;
     if (e < E) group_rows(offsets, E, T, T * k, e, base, n);
-    const int nf = n / kTM, rem = n % kTM;
-    const int nt = nf + (rem > 0 ? 1 : 0);
+    cnt[e] = n;
+    if (e == 0) cnt[1024] = has_shared ? T : 0;
+    const int nt = (n + kTM - 1) / kTM;
     part[e] = nt;
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {
@@ -91,18 +94,30 @@ __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict_
         part[e] += v;
         __syncthreads();
     }
-    const int start = part[e] - nt;
-    for (int i = 0; i < nt && start + i < tiles_max; ++i)
-        tiles[start + i] = TileDesc{e, i * kTM, i < nf ? kTM / 32 : rem_tile_ni(rem), 0};
-    if (e == 1023) {
-        int total = min(part[1023], tiles_max);
-        if (has_shared) {
-            const int sf = T / kTM, srem = T % kTM;
-            for (int i = 0; i < sf + (srem > 0 ? 1 : 0) && total < tiles_max; ++i)
-                tiles[total++] = TileDesc{E, i * kTM, i < sf ? kTM / 32 : rem_tile_ni(srem), 0};
+    const int routed = part[1023];
+    const int total = min(routed + (cnt[1024] + kTM - 1) / kTM, tiles_max);
+    // every thread writes tiles: slot i of the routed list belongs to the first group whose
+    // inclusive prefix exceeds i (binary search), the rest to the shared group
+    for (int i = e; i < total; i += 1024) {
+        int g, first;
+        if (i < routed) {
+            int lo = 0, hi = 1023;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (part[mid] > i) hi = mid;
+                else lo = mid + 1;
+            }
+            g = lo;
+            first = lo > 0 ? part[lo - 1] : 0;
+        } else {
+            g = 1024;
+            first = routed;
         }
-        *ntiles = total;
+        const int j = i - first, rows = cnt[g];
+        const int nf = rows / kTM;
+        tiles[i] = TileDesc{g == 1024 ? E : g, j * kTM, j < nf ? kTM / 32 : rem_tile_ni(rows % kTM), 0};
     }
+    if (e == 0) *ntiles = total;
 }
 
 int max_tiles(int T, int k, int E) { return (T * k) / kTM + T / kTM + E + 2; }
