@@ -39,8 +39,8 @@ __global__ __launch_bounds__(64) void k_perm_hist(const int32_t* __restrict__ id
 
 // One block of 1024 threads: thread i owns the contiguous segment [i * per, (i + 1) * per) of the
 // n = E * nchunks counts (per a multiple of 16), sums it, a block scan of the 1024 sums gives each
-// segment's start, and a second pass writes the exclusive prefix in place. Both passes move 16
-// counts per step with four independent 16-byte accesses.
+// segment's start, and a second pass writes the exclusive prefix in place. Counts move 16 per step
+// with four independent 16-byte accesses; segments of up to 32 are read once and kept in registers.
 __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts, int nchunks, int E,
                                                     int32_t* __restrict__ offsets) {
     __shared__ int32_t part[1024];
@@ -60,12 +60,28 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts
             for (int j = 0; j < 16; ++j) v[j] = i + j < hi ? counts[i + j] : 0;
         }
     };
+    // up to 32 counts per thread stay in registers between the two passes (one read of the counts)
+    const bool held = per <= 32;
+    int h0[16], h1[16];
     int sum = 0;
-    for (int i = lo; i < hi; i += 16) {
-        int v[16];
-        load16(i, v);
+    if (held) {
+        if (lo < hi) load16(lo, h0);
+        else
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sum += v[j];
+            for (int j = 0; j < 16; ++j) h0[j] = 0;
+        if (lo + 16 < hi) load16(lo + 16, h1);
+        else
+#pragma unroll
+            for (int j = 0; j < 16; ++j) h1[j] = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sum += h0[j] + h1[j];
+    } else {
+        for (int i = lo; i < hi; i += 16) {
+            int v[16];
+            load16(i, v);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sum += v[j];
+        }
     }
     part[tid] = sum;
     __syncthreads();
@@ -79,7 +95,12 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts
     int e = lo / nchunks, c = lo - e * nchunks;
     for (int i = lo; i < hi; i += 16) {
         int v[16], o[16];
-        load16(i, v);
+        if (held) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = i == lo ? h0[j] : h1[j];
+        } else {
+            load16(i, v);
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             o[j] = run;
