@@ -47,6 +47,9 @@ constexpr int kStages = 3;                 // A stages in LDS
 constexpr int kStageBytes = kTM * 128;     // one K step (64 fp16) of 128 rows
 constexpr int kHS = 128 + 8;               // fp16 per row of the staged h tile (padded)
 constexpr int kXcds = 8;
+// Word 3 of a raw buffer descriptor (no stride, no swizzle) with the 32-bit data format; loads past
+// num_records bytes return zero.
+constexpr int kRawBufferWord3 = 0x00020000;
 
 struct TileDesc {
     int group;  // expert id, or E for the shared expert
@@ -426,9 +429,9 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
             const int cofs = 2 * t * BB, sofs = 4 * t;
             const int bvo = bvo0 + j * bdv, svo = svo0 + j * sdv;
             const __amdgpu_buffer_rsrc_t rc =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(bmat[j] + cofs), (short)0, (int)(bbytes - cofs), 0x00020000);
+                __builtin_amdgcn_make_buffer_rsrc((void*)(bmat[j] + cofs), (short)0, (int)(bbytes - cofs), kRawBufferWord3);
             const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(smat[j] + sofs), (short)0, (int)(sbytes - sofs), 0x00020000);
+                __builtin_amdgcn_make_buffer_rsrc((void*)(smat[j] + sofs), (short)0, (int)(sbytes - sofs), kRawBufferWord3);
             if constexpr (FMT == MOE_Q8_B32) {
                 sl[j].b.c0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, bvo, 0, 0));
                 sl[j].b.c1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, bvo + 16, 0, 0));
