@@ -28,6 +28,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* ---------------------------------------------------------------- random streams */
@@ -241,15 +242,16 @@ int synth_expert_stack(int fmt, uint64_t key, int32_t E, int32_t N, int32_t K, d
     if (nthreads < 1) nthreads = 1;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : rc)
     for (int32_t e = 0; e < E; ++e) {
-        float row[8192];
+        float* row = (float*)malloc(sizeof(float) * (size_t)K);
+        if (!row) { rc |= 1; continue; }
         normal_stream ns;
         ns_init(&ns, synth_key(key, (uint64_t)e, 0x5EED, 0, 0));
         for (int32_t n = 0; n < N; ++n) {
-            if (K > 8192) { rc |= 1; break; }
             for (int32_t k = 0; k < K; ++k) row[k] = (float)(sigma * ns_next(&ns));
             rc |= synth_quantize_rows(fmt, row, 1, K, codes + e * per_codes + (int64_t)n * K * bits / 8,
                                       scales + e * per_scales + (int64_t)n * (K / 32)) != 0;
         }
+        free(row);
     }
     return rc ? -1 : 0;
 }

@@ -240,6 +240,23 @@ def test_layer_prefill_ragged_shapes(fmt):
     assert_float_match(Y, ref["Y"], "Y")
 
 
+@pytest.mark.parametrize("T,k,Is", [(1, 2, 4096), (5, 1, 0)])
+def test_layer_max_shapes(T, k, Is):
+    """The largest hidden and intermediate sizes the library accepts (H = 16384, I = Is = 4096, int8
+    codes): the decode kernels (T = 1, with the shared expert) and the grouped GEMMs (T = 5), whose
+    32-bit lane offsets and 64 MB weight matrices sit at their limits."""
+    _need_gpu()
+    spec = synth.LayerSpec("max", T=T, H=16384, E=2, k=k, I=4096, Is=Is, fmt=synth.Q8, zipf=False,
+                           cfg_id=95)
+    d = synth.make_layer(spec)
+    say("max shapes", "T=%d k=%d Is=%d" % (T, k, Is))
+    O = orc_layer(spec, d)
+    g_logits, g_ids, g_p, Y = run_layer(spec, d)
+    check_routing(O, d["x"], g_logits, g_ids, g_p)
+    ref = oracle_tokens(O, d["x"], g_logits, range(T))
+    assert_float_match(Y, ref["Y"], "Y")
+
+
 @pytest.mark.parametrize("T", [1, 4, 65])
 def test_experts_prefill_entry(T):
     """moe_permute + moe_experts_prefill as separate calls: permutation bit-exact, y_sorted rows."""
