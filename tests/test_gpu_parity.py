@@ -452,6 +452,22 @@ def test_k_equals_E_and_no_shared():
     assert_float_match(Y, ref["Y"], "Y")
 
 
+@pytest.mark.parametrize("T", [4, 100, 400])
+def test_layer_max_experts(T):
+    """The largest expert count and top-k (E = 1024, k = 16, with a shared expert): 64 routed pairs in
+    the decode plan (T = 4); in the prefill path the top-k over 16 logits per lane, the one-block
+    permutation (T = 100) and the three-kernel one (T = 400), the tile list with a group per thread."""
+    _need_gpu()
+    spec = synth.LayerSpec("maxE", T=T, H=256, E=1024, k=16, I=64, Is=64, fmt=synth.Q4, zipf=True, cfg_id=96)
+    d = synth.make_layer(spec)
+    say("max experts", "T=%d" % T)
+    O = orc_layer(spec, d)
+    g_logits, g_ids, g_p, Y = run_layer(spec, d)
+    check_routing(O, d["x"], g_logits, g_ids, g_p)
+    ref = oracle_tokens(O, d["x"], g_logits, range(T))
+    assert_float_match(Y, ref["Y"], "Y")
+
+
 def test_determinism():
     """Two calls give identical bits (atomic-free combine, stable permutation)."""
     _need_gpu()
