@@ -43,9 +43,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kTM = 128;                   // rows of a full tile
 constexpr int kGW = 4;                     // waves per block (two blocks per CU)
 constexpr int kGT = kGW * kWave;           // threads per block
-constexpr int kStages = 3;                 // A stages in LDS
+constexpr int kStages = 4;                 // A stages in LDS (a ring of four, loads two steps ahead)
 constexpr int kStageBytes = kTM * 128;     // one K step (64 fp16) of 128 rows
 constexpr int kHS = 128 + 8;               // fp16 per row of the staged h tile (padded)
+constexpr int kScaleBytes = 2 * kGW * 1024; // two groups of 4 K steps of scales, 1 KB per wave each
 constexpr int kXcds = 8;
 // Word 3 of a raw buffer descriptor (no stride, no swizzle) with the 32-bit data format; loads past
 // num_records bytes return zero.
@@ -296,8 +297,9 @@ template <int VM> __device__ __forceinline__ void step_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// One tile of 32 * NI rows against the block's 256 weight rows (gate/up: 128 h columns).
-template <int FMT, bool GATEUP, typename YT, int NI>
+// One tile of 32 * NI rows against the block's 256 weight rows (gate/up: 128 h columns). SD: the
+// scales come as groups of four K steps straight into LDS (the scale rows are 16-byte aligned).
+template <int FMT, bool GATEUP, typename YT, int NI, bool SD>
 __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileDesc& td, int ntile,
                                           const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
                                           const _Float16* __restrict__ asrc, _Float16* __restrict__ h16,
@@ -305,7 +307,8 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     constexpr int G = perm_group<FMT>();
     constexpr int BB = FMT == MOE_Q8_B32 ? 32 : FMT == MOE_Q4_B32 ? 16 : 8;   // bytes per block
     constexpr int QW = NI;                         // 1 KB (8-row) direct loads per wave and step
-    constexpr int BATCH = QW + 2 * code_loads<FMT>() + 2;   // vector-memory instructions per step
+    // vector-memory instructions per step (with SD, one more in every fourth step's batch)
+    constexpr int BATCH = QW + 2 * code_loads<FMT>() + (SD ? 0 : 2);
 
     const bool shared = td.group == L.E;
     const int H = L.H, Imax = L.Imax();
@@ -399,13 +402,22 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     // lane offsets of block g of row wrow (tile 0; tile 1 adds its row difference)
     const int bvo0 = (int)(wrow[0] * rb) + g * BB, svo0 = (wrow[0] * nb + g) * 2;
     const int bdv = (int)((wrow[1] - wrow[0]) * rb), sdv = (wrow[1] - wrow[0]) * nb * 2;
+    // SD: lane l of wave w loads 16 bytes (the 8 scales of 4 K steps) of row wrow[l / 32] of tile
+    // l / 32 for rows 32 w + l % 32; they land at byte 16 l of the wave's 1 KB of the group's buffer
+    const char* sgsrc = nullptr;
+    if constexpr (SD) {
+        const int j = lane / 32;
+        sgsrc = reinterpret_cast<const char*>(smat[j]) + (int64_t)wrow[j] * nb * 2;
+    }
+    uint8_t* sbuf = smem + kStages * kStageBytes;
 
-    BSlot slot0[2], slot1[2], slot2[2];
+    BSlot slot0[2], slot1[2], slot2[2], slot3[2];   // steps s, s + 1, s + 2 live at a time
     auto slot = [&](auto sc) __attribute__((always_inline)) -> BSlot(&)[2] {
         constexpr int v = decltype(sc)::value;
         if constexpr (v == 0) return slot0;
         else if constexpr (v == 1) return slot1;
-        else return slot2;
+        else if constexpr (v == 2) return slot2;
+        else return slot3;
     };
     // A source of load u at step t: its row + min(128 t + 2 ach, 2 (K - 8)) bytes
     const char* abase[QW];
@@ -417,12 +429,18 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     // lane offsets stay fixed; a block past the end of the matrix reads as zero (bounds-checked).
     // A chunk past K (the second half of the last step when K % 64 == 32) reloads the row's last
     // chunk instead (its weights are zero, see below).
-    auto issue = [&](BSlot (&sl)[2], int t, int stage) __attribute__((always_inline)) {
+    auto issue = [&](BSlot (&sl)[2], int t, int stage, auto group_start) __attribute__((always_inline)) {
         t = min(t, nsteps - 1);
         uint8_t* st = smem + stage * kStageBytes + wave * 1024;
 #pragma unroll
         for (int u = 0; u < QW; ++u)
             __builtin_amdgcn_global_load_lds(abase[u] + min(128 * t + 2 * ach[u], klim), (lds_void*)(st + u * kGW * 1024),
+                                             16, 0, 0);
+        // the scales of steps t .. t + 3 (blocks 2 t .. 2 t + 7), issued by the steps that start a group
+        // of four (known at compile time; a clamped step past the end rewrites the last group with the
+        // same bytes)
+        if constexpr (SD && decltype(group_start)::value)
+            __builtin_amdgcn_global_load_lds(sgsrc + 4 * (t & ~3), (lds_void*)(sbuf + ((t >> 2) & 1) * (kGW * 1024) + wave * 1024),
                                              16, 0, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -442,7 +460,7 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
                 sl[j].b.c0.x = v.x;
                 sl[j].b.c0.y = v.y;
             }
-            sl[j].sc = __builtin_amdgcn_raw_buffer_load_b16(rs, svo, 0, 0);
+            if constexpr (!SD) sl[j].sc = __builtin_amdgcn_raw_buffer_load_b16(rs, svo, 0, 0);
         }
     };
 
@@ -456,16 +474,28 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // step s: refill the slots and stage of step s + 2, dequantise this lane's blocks of step s
-    // and run its MFMAs against stage s % 3, then wait for the loads of step s + 1 (everything but
+    // and run its MFMAs against stage s % 4, then wait for the loads of step s + 1 (everything but
     // the last BATCH vector-memory instructions) and meet the other waves. The barrier is written
     // out so that no memory fence makes it wait for the loads still in flight.
     auto kstep = [&](int s, auto sc) __attribute__((always_inline)) {
-        constexpr int SL = decltype(sc)::value;
-        issue(slot(std::integral_constant<int, (SL + 2) % 3>{}), s + 2, (SL + 2) % 3);
+        constexpr int SL = decltype(sc)::value;   // = s % 4
+        constexpr bool kGroup = SD && (SL + 2) % 4 == 0;
+        issue(slot(std::integral_constant<int, (SL + 2) % 4>{}), s + 2, (SL + 2) % 4,
+              std::integral_constant<bool, kGroup>{});
         const BSlot(&cur)[2] = slot(sc);
         const bool blive = 2 * s + g < nb;     // a block past K contributes zero
-        const _Float16 s0 = blive ? __builtin_bit_cast(_Float16, (uint16_t)cur[0].sc) : (_Float16)0.f;
-        const _Float16 s1 = blive ? __builtin_bit_cast(_Float16, (uint16_t)cur[1].sc) : (_Float16)0.f;
+        uint16_t sc0, sc1;
+        if constexpr (SD) {
+            // group s / 4 in buffer (s / 4) % 2; element 2 (s % 4) + g of tile j's 16 bytes
+            const uint16_t* sb = reinterpret_cast<const uint16_t*>(sbuf + ((s >> 2) & 1) * (kGW * 1024) + wave * 1024);
+            sc0 = sb[frow * 8 + 2 * (s & 3) + g];
+            sc1 = sb[(32 + frow) * 8 + 2 * (s & 3) + g];
+        } else {
+            sc0 = (uint16_t)cur[0].sc;
+            sc1 = (uint16_t)cur[1].sc;
+        }
+        const _Float16 s0 = blive ? __builtin_bit_cast(_Float16, sc0) : (_Float16)0.f;
+        const _Float16 s1 = blive ? __builtin_bit_cast(_Float16, sc1) : (_Float16)0.f;
         const half2v sv0 = {s0, s0}, sv1 = {s1, s1};
         const uint8_t* st = smem + SL * kStageBytes;
         // A fragments of sub-step kk + 1 are read while the MFMAs of kk run (two named sets, so
@@ -491,20 +521,22 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
                 acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur_a[i], b1, acc[i][1], 0, 0, 0);
             }
         });
-        step_barrier<BATCH>();
+        step_barrier<BATCH + (kGroup ? 1 : 0)>();
     };
 
-    issue(slot0, 0, 0);
-    issue(slot1, 1, 1);
+    issue(slot0, 0, 0, std::integral_constant<bool, SD>{});
+    issue(slot1, 1, 1, std::integral_constant<bool, false>{});
     step_barrier<BATCH>();
     int s = 0;
-    for (; s + 3 <= nsteps; s += 3) {
+    for (; s + 4 <= nsteps; s += 4) {
         kstep(s, std::integral_constant<int, 0>{});
         kstep(s + 1, std::integral_constant<int, 1>{});
         kstep(s + 2, std::integral_constant<int, 2>{});
+        kstep(s + 3, std::integral_constant<int, 3>{});
     }
     if (s < nsteps) kstep(s, std::integral_constant<int, 0>{});
     if (s + 1 < nsteps) kstep(s + 1, std::integral_constant<int, 1>{});
+    if (s + 2 < nsteps) kstep(s + 2, std::integral_constant<int, 2>{});
     // every direct load has landed and every wave is done with the stages: LDS is free
     step_barrier<0>();
 
@@ -587,7 +619,7 @@ __global__ __launch_bounds__(kGT, 2) void k_grouped_gemm(LayerView L, int T, con
                                                          const int32_t* __restrict__ perm,
                                                          const _Float16* __restrict__ asrc, _Float16* __restrict__ h16,
                                                          YT* __restrict__ y_sorted, YT* __restrict__ y_shared) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes + kScaleBytes];
     // XCD-aware work index: block b runs on XCD b % 8, and consecutive work items go to the same
     // XCD. Work items are ordered tile-major: the weight-row tiles of one row tile (same A rows)
     // run side by side, and so do the row tiles of one expert (same weights). The grid is sized for
@@ -602,11 +634,17 @@ __global__ __launch_bounds__(kGT, 2) void k_grouped_gemm(LayerView L, int T, con
     if (w >= total) return;
     const int tile = w / n_ntile, ntile = w % n_ntile;
     const TileDesc td = tiles[tile];
+    // scale rows are 16-byte aligned when the scale count per row is a multiple of 8
+    const int K = GATEUP ? L.H : (td.group == L.E ? L.Is : L.I);
+    const bool sd = (K / 32) % 8 == 0;
+#define MOE_GEMM_TILE(NI_, SD_) \
+    gemm_tile<FMT, GATEUP, YT, NI_, SD_>(L, T, td, ntile, offsets, perm, asrc, h16, y_sorted, y_shared, smem)
     switch (td.ni) {
-        case 4: gemm_tile<FMT, GATEUP, YT, 4>(L, T, td, ntile, offsets, perm, asrc, h16, y_sorted, y_shared, smem); break;
-        case 2: gemm_tile<FMT, GATEUP, YT, 2>(L, T, td, ntile, offsets, perm, asrc, h16, y_sorted, y_shared, smem); break;
-        default: gemm_tile<FMT, GATEUP, YT, 1>(L, T, td, ntile, offsets, perm, asrc, h16, y_sorted, y_shared, smem); break;
+        case 4: if (sd) MOE_GEMM_TILE(4, true); else MOE_GEMM_TILE(4, false); break;
+        case 2: if (sd) MOE_GEMM_TILE(2, true); else MOE_GEMM_TILE(2, false); break;
+        default: if (sd) MOE_GEMM_TILE(1, true); else MOE_GEMM_TILE(1, false); break;
     }
+#undef MOE_GEMM_TILE
 }
 
 // -------------------------------------------------------------------------------- launch
