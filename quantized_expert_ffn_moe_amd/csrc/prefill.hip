@@ -15,11 +15,11 @@
 //     rows of the tile against its own 64 weight rows with v_mfma_f32_32x32x16_f16 (on this chip
 //     the 32 x 32 form sustains a far higher rate than 16 x 16 x 32): every A fragment read from
 //     LDS feeds 2 MFMAs and every dequantised weight fragment up to 4;
-//   - A goes global -> LDS directly (16 bytes per lane, no registers), in a three-stage ring two K
+//   - A goes global -> LDS directly (16 bytes per lane, no registers), in a four-stage ring three K
 //     steps ahead, each 128-byte row segment XOR-swizzled in 16-byte slots so that the fragment
 //     reads of 16 lanes hit distinct banks; one barrier per K step of 64;
 //   - weights never touch LDS: each lane loads the codes and scale of one 32-block of its weight
-//     row (two steps ahead, in named register slots, through buffer descriptors) and dequantises
+//     row (three steps ahead, in named register slots, through buffer descriptors) and dequantises
 //     them straight into its MFMA operand: the code is placed in the mantissa of an fp16 power of
 //     two, the offset subtracted (an exact fp16 level) and multiplied by the fp16 scale with packed
 //     fp16 arithmetic, i.e. level * scale rounded once to fp16. The pairs come out in an order that
@@ -43,7 +43,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kTM = 128;                   // rows of a full tile
 constexpr int kGW = 4;                     // waves per block (two blocks per CU)
 constexpr int kGT = kGW * kWave;           // threads per block
-constexpr int kStages = 4;                 // A stages in LDS (a ring of four, loads two steps ahead)
+constexpr int kStages = 4;                 // A stages in LDS (a ring of four, loads three steps ahead)
 constexpr int kStageBytes = kTM * 128;     // one K step (64 fp16) of 128 rows
 constexpr int kHS = 128 + 8;               // fp16 per row of the staged h tile (padded)
 constexpr int kScaleBytes = 2 * kGW * 1024; // two groups of 4 K steps of scales, 1 KB per wave each
@@ -411,7 +411,7 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     }
     uint8_t* sbuf = smem + kStages * kStageBytes;
 
-    BSlot slot0[2], slot1[2], slot2[2], slot3[2];   // steps s, s + 1, s + 2 live at a time
+    BSlot slot0[2], slot1[2], slot2[2], slot3[2];   // steps s .. s + 3 live at a time
     auto slot = [&](auto sc) __attribute__((always_inline)) -> BSlot(&)[2] {
         constexpr int v = decltype(sc)::value;
         if constexpr (v == 0) return slot0;
@@ -473,60 +473,105 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // step s: refill the slots and stage of step s + 2, dequantise this lane's blocks of step s
-    // and run its MFMAs against stage s % 4, then wait for the loads of step s + 1 (everything but
-    // the last BATCH vector-memory instructions) and meet the other waves. The barrier is written
-    // out so that no memory fence makes it wait for the loads still in flight.
-    auto kstep = [&](int s, auto sc) __attribute__((always_inline)) {
-        constexpr int SL = decltype(sc)::value;   // = s % 4
-        constexpr bool kGroup = SD && (SL + 2) % 4 == 0;
-        issue(slot(std::integral_constant<int, (SL + 2) % 4>{}), s + 2, (SL + 2) % 4,
-              std::integral_constant<bool, kGroup>{});
-        const BSlot(&cur)[2] = slot(sc);
-        const bool blive = 2 * s + g < nb;     // a block past K contributes zero
+    // Scales of step t as an fp16 pair per weight tile (zero for a block past K, which then
+    // contributes nothing): from the LDS group buffer (t / 4) % 2, element 2 (t % 4) + g of tile
+    // j's 16 bytes, or from the B slot itself.
+    auto scales = [&](int t, const BSlot (&sl)[2], half2v& v0, half2v& v1) __attribute__((always_inline)) {
+        const bool blive = 2 * t + g < nb;
         uint16_t sc0, sc1;
         if constexpr (SD) {
-            // group s / 4 in buffer (s / 4) % 2; element 2 (s % 4) + g of tile j's 16 bytes
-            const uint16_t* sb = reinterpret_cast<const uint16_t*>(sbuf + ((s >> 2) & 1) * (kGW * 1024) + wave * 1024);
-            sc0 = sb[frow * 8 + 2 * (s & 3) + g];
-            sc1 = sb[(32 + frow) * 8 + 2 * (s & 3) + g];
+            const uint16_t* sb = reinterpret_cast<const uint16_t*>(sbuf + ((t >> 2) & 1) * (kGW * 1024) + wave * 1024);
+            sc0 = sb[frow * 8 + 2 * (t & 3) + g];
+            sc1 = sb[(32 + frow) * 8 + 2 * (t & 3) + g];
         } else {
-            sc0 = (uint16_t)cur[0].sc;
-            sc1 = (uint16_t)cur[1].sc;
+            sc0 = (uint16_t)sl[0].sc;
+            sc1 = (uint16_t)sl[1].sc;
         }
         const _Float16 s0 = blive ? __builtin_bit_cast(_Float16, sc0) : (_Float16)0.f;
         const _Float16 s1 = blive ? __builtin_bit_cast(_Float16, sc1) : (_Float16)0.f;
-        const half2v sv0 = {s0, s0}, sv1 = {s1, s1};
-        const uint8_t* st = smem + SL * kStageBytes;
-        // A fragments of sub-step kk + 1 are read while the MFMAs of kk run (two named sets, so
-        // that nothing is indexed at run time); the scheduling fences keep that order.
-        half8 fa[NI], fb[NI];
-        auto frag = [&](auto kc, half8 (&f)[NI]) __attribute__((always_inline)) {
-            constexpr int kk = decltype(kc)::value;
+        v0 = half2v{s0, s0};
+        v1 = half2v{s1, s1};
+    };
+    auto frag = [&](const uint8_t* st, auto kc, half8 (&f)[NI]) __attribute__((always_inline)) {
+        constexpr int kk = decltype(kc)::value;
 #pragma unroll
-            for (int i = 0; i < NI; ++i) f[i] = *reinterpret_cast<const half8*>(st + aoff[kk] + i * 4096);
-        };
-        frag(std::integral_constant<int, 0>{}, fa);
+        for (int i = 0; i < NI; ++i) f[i] = *reinterpret_cast<const half8*>(st + aoff[kk] + i * 4096);
+    };
+    auto deq = [&](const BSlot (&sl)[2], auto kc, half2v v0, half2v v1, half8 (&b)[2]) __attribute__((always_inline)) {
+        constexpr int kk = decltype(kc)::value;
+        b[0] = dequant8<FMT, kk>(sl[0].b, v0, dq);
+        b[1] = dequant8<FMT, kk>(sl[1].b, v1, dq);
+    };
+    // A fragments and dequantised weights of the next sub-step are prepared while the MFMAs of the
+    // current one run (two named sets of each, so that nothing is indexed at run time); scheduling
+    // groups interleave each MFMA with a share of that preparation, so that a wave keeps issuing
+    // MFMAs back to back. The operands of sub-step 0 of a step are prepared during sub-step 3 of
+    // the step before, so no step starts with an exposed LDS read or dequantisation.
+    half8 fa[NI], fb[NI];
+    half8 ba[2], bb[2];
+    half2v svc0, svc1;   // scales of the current step
+
+    // Step s. Sub-steps 0-2 run on operands prepared one sub-step ahead. Before sub-step 3 the wave
+    // waits for the loads of step s + 1 (everything but those of steps s + 2 and s + 3) and for
+    // its LDS reads, then meets the other waves: stage s % 4 and the B slot of step s are then
+    // free, and step s + 4 is loaded into them while sub-step 3 runs and step s + 1's first
+    // operands are prepared. The barrier is written out so that no memory fence makes it wait for
+    // the loads still in flight.
+    auto kstep = [&](int s, auto sc) __attribute__((always_inline)) {
+        constexpr int SL = decltype(sc)::value;   // = s % 4
+        constexpr int SN = (SL + 1) % 4;
+        constexpr bool kIssueGroup = SD && SL == 0;                  // step s + 4 starts a scale group
+        constexpr int kInFlightGroups = (SD && (SL == 1 || SL == 2)) ? 1 : 0;   // s + 2 or s + 3 does
+        const BSlot(&cur)[2] = slot(sc);
+        const BSlot(&nxt)[2] = slot(std::integral_constant<int, SN>{});
+        const uint8_t* st = smem + SL * kStageBytes;
+        const uint8_t* stn = smem + SN * kStageBytes;
+        half2v svn0, svn1;
         static_for<4>([&](auto kc) {
             constexpr int kk = decltype(kc)::value;
             half8 (&cur_a)[NI] = (kk % 2 == 0) ? fa : fb;
             half8 (&nxt_a)[NI] = (kk % 2 == 0) ? fb : fa;
-            if constexpr (kk < 3) frag(std::integral_constant<int, kk + 1>{}, nxt_a);
+            half8 (&cur_b)[2] = (kk % 2 == 0) ? ba : bb;
+            half8 (&nxt_b)[2] = (kk % 2 == 0) ? bb : ba;
             __builtin_amdgcn_sched_barrier(0);
-            const half8 b0 = dequant8<FMT, kk>(cur[0].b, sv0, dq);
-            const half8 b1 = dequant8<FMT, kk>(cur[1].b, sv1, dq);
+            if constexpr (kk < 3) {
+                frag(st, std::integral_constant<int, kk + 1>{}, nxt_a);
+                deq(cur, std::integral_constant<int, kk + 1>{}, svc0, svc1, nxt_b);
+            } else {
+                step_barrier<2 * BATCH + kInFlightGroups>();
+                issue(slot(sc), s + 4, SL, std::integral_constant<bool, kIssueGroup>{});
+                scales(s + 1, nxt, svn0, svn1);
+                frag(stn, std::integral_constant<int, 0>{}, nxt_a);
+                deq(nxt, std::integral_constant<int, 0>{}, svn0, svn1, nxt_b);
+            }
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur_a[i], b0, acc[i][0], 0, 0, 0);
-                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur_a[i], b1, acc[i][1], 0, 0, 0);
+                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur_a[i], cur_b[0], acc[i][0], 0, 0, 0);
+                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur_a[i], cur_b[1], acc[i][1], 0, 0, 0);
             }
+            // 2 NI MFMAs; about 26 VALU and NI LDS reads of the next sub-step between them
+            constexpr int kV = (28 + 2 * NI - 1) / (2 * NI);
+            static_for<2 * NI>([&](auto mc) {
+                constexpr int m = decltype(mc)::value;
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+                if constexpr (m % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);    // VALU
+            });
         });
-        step_barrier<BATCH + (kGroup ? 1 : 0)>();
+        __builtin_amdgcn_sched_barrier(0);
+        svc0 = svn0;
+        svc1 = svn1;
     };
 
+    // prologue: steps 0-3 in flight, then step 0's first operands
     issue(slot0, 0, 0, std::integral_constant<bool, SD>{});
     issue(slot1, 1, 1, std::integral_constant<bool, false>{});
-    step_barrier<BATCH>();
+    issue(slot2, 2, 2, std::integral_constant<bool, false>{});
+    issue(slot3, 3, 3, std::integral_constant<bool, false>{});
+    step_barrier<3 * BATCH>();
+    scales(0, slot0, svc0, svc1);
+    frag(smem, std::integral_constant<int, 0>{}, fa);
+    deq(slot0, std::integral_constant<int, 0>{}, svc0, svc1, ba);
     int s = 0;
     for (; s + 4 <= nsteps; s += 4) {
         kstep(s, std::integral_constant<int, 0>{});
