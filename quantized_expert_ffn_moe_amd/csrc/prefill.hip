@@ -549,12 +549,13 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
                 acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur_a[i], cur_b[0], acc[i][0], 0, 0, 0);
                 acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur_a[i], cur_b[1], acc[i][1], 0, 0, 0);
             }
-            // 2 NI MFMAs; about 26 VALU and NI LDS reads of the next sub-step between them
+            // 2 NI MFMAs; the NI LDS reads of the next sub-step behind the first NI of them (their
+            // latency then hides behind the rest), about 26 VALU spread over all of them
             constexpr int kV = (28 + 2 * NI - 1) / (2 * NI);
             static_for<2 * NI>([&](auto mc) {
                 constexpr int m = decltype(mc)::value;
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
-                if constexpr (m % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                if constexpr (m < NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
                 __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);    // VALU
             });
         });
