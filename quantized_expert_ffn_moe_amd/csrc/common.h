@@ -30,6 +30,14 @@ __device__ __forceinline__ uint32_t ordered_key(float v) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
+// SiLU(g) * u from the hardware exp2 and reciprocal (each within about 1 ulp of fp32), for results
+// that are rounded to fp16 right away: g * u / (1 + 2^(-g log2 e)). Large negative g gives an
+// infinite exponential and a zero reciprocal, i.e. the limit 0.
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+    return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // ------------------------------------------------------------------------------------- reductions
 
 template <int kWidth>

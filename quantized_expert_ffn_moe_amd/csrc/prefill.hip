@@ -597,7 +597,7 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
-                hs[row * kHS + pc] = (_Float16)silu_mul(acc[i][0][r], acc[i][1][r]);
+                hs[row * kHS + pc] = (_Float16)silu_mul_fast(acc[i][0][r], acc[i][1][r]);
             }
         __syncthreads();
 #pragma unroll
