@@ -285,11 +285,18 @@ __device__ __forceinline__ void bf16x32_to_f32(const uint4 (&raw)[4], float (&v)
 
 // ----------------------------------------------------------------------------------- K2 gate/up
 
-constexpr int kGateUpRows = 2;    // gate/up rows per K2 wave
+// Gate/up rows per K2 wave and waves per K2 block: 2 rows and up to 16 waves (128 VGPRs); for three
+// or four tokens 3 rows and up to 12 waves (168 VGPRs, so that the 8-bit codes of 3 rows and 4
+// tokens' sums stay in registers), i.e. 9216 rows per pass over 256 CUs: the union of the chosen
+// experts (about 16 + the shared one, 8704 rows) then takes one pass instead of two.
+__host__ __device__ constexpr int gateup_rows(int T) { return T >= 3 ? 3 : 2; }
+__host__ __device__ constexpr int gateup_max_waves(int T) { return T >= 3 ? 12 : 16; }
 constexpr int kDownRows = 1;      // output rows per K3 wave
 constexpr int kDownWaves = 8;     // waves per K3 block (two per SIMD hide each other's latency)
 constexpr int kDownThreads = kDownWaves * kWave;
-constexpr int kDownJ = 4;         // down items per row whose loads a K3 lane issues together
+// Down items per row whose loads a K3 lane issues together: 4, and 5 for three or four tokens
+// (16 + 1 experts x 16 blocks = 272 items per row then take one batch of loads, not two).
+__host__ __device__ constexpr int down_batch(int T) { return T >= 3 ? 5 : 4; }
 
 // LDS of k_dec_gateup: plan | first[E] | ids_s[64] | p_s[64] | xq[T][4][nb] uint4
 __host__ __device__ inline size_t lds_head(int E) {
@@ -302,11 +309,11 @@ static size_t gateup_smem_bytes(int T, int H, int E) { return lds_head(E) + (siz
 // use, h = silu(g) * u written for each token that chose the expert, already in the staged fp16
 // hi/lo layout the down kernel reads. Block 0 publishes ids, p and the plan (plan_g).
 template <int FMT, int T, bool ROUTE, int KPL>
-__global__ __launch_bounds__(1024) void k_dec_gateup(LayerView L, const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(LayerView L, const uint16_t* __restrict__ x,
                                                     const float* __restrict__ logits, int32_t* __restrict__ ids,
                                                     float* __restrict__ p, float* __restrict__ h,
                                                     DecodePlan* __restrict__ plan_g) {
-    constexpr int R = kGateUpRows;
+    constexpr int R = gateup_rows(T);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     DecodePlan& P = *reinterpret_cast<DecodePlan*>(smem);
     int* first = reinterpret_cast<int*>(smem + align_up(sizeof(DecodePlan), 16));
@@ -377,29 +384,38 @@ __global__ __launch_bounds__(1024) void k_dec_gateup(LayerView L, const uint16_t
         for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += blockDim.x) dst[i] = src[i];
     }
 
-    // the rows of the distinct chosen experts (slot order) then the shared expert's, R per wave
-    // and step, the grid striding over them (a grid of at most one block per CU)
+    // tasks of R consecutive rows of one expert (the last task of an expert may hold fewer): those
+    // of the distinct chosen experts (slot order) then the shared expert's, one task per wave and
+    // step, the grid striding over them (a grid of at most one block per CU)
     const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave;
-    const int64_t nrouted = (int64_t)P.nU * L.I;
-    const int64_t nreal = nrouted + L.Is;
-    const int64_t wstride = (int64_t)gridDim.x * (blockDim.x / kWave) * R;
+    const int tpeI = (L.I + R - 1) / R, tpeS = (L.Is + R - 1) / R;
+    const int64_t nrouted = (int64_t)P.nU * tpeI;
+    const int64_t ntasks = nrouted + tpeS;
+    const int64_t tstride = (int64_t)gridDim.x * (blockDim.x / kWave);
     const int64_t rb = row_bytes(FMT, H);
-    for (int64_t r0 = gw * R; r0 < nreal; r0 += wstride) {   // uniform per wave
-        int slot, n0;
+    for (int64_t tk = gw; tk < ntasks; tk += tstride) {   // uniform per wave
+        int slot, n0, nv;
         const uint8_t *gc, *uc;
         const uint16_t *gs, *us;
-        if (r0 < nrouted) {
-            slot = (int)(r0 / L.I);
-            n0 = (int)(r0 % L.I);
+        if (tk < nrouted) {
+            slot = (int)(tk / tpeI);
+            n0 = (int)(tk % tpeI) * R;
+            nv = min(R, L.I - n0);
             const int64_t row = (int64_t)P.expert[slot] * L.I + n0;
             gc = L.g_codes + row * rb; uc = L.u_codes + row * rb;
             gs = L.g_scales + row * nb; us = L.u_scales + row * nb;
         } else {
             slot = 64;  // shared
-            n0 = (int)(r0 - nrouted);
+            n0 = (int)(tk - nrouted) * R;
+            nv = min(R, L.Is - n0);
             gc = L.sg_codes + (int64_t)n0 * rb; uc = L.su_codes + (int64_t)n0 * rb;
             gs = L.sg_scales + (int64_t)n0 * nb; us = L.su_scales + (int64_t)n0 * nb;
         }
+        // row i of the task, clamped to its last valid row (loads stay in the expert's matrix;
+        // the results of clamped rows are not stored)
+        int ro[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) ro[i] = min(i, nv - 1);
 
         const uint32_t mask = slot < 64 ? P.tokmask[slot] : (1u << T) - 1u;
         float g[R][T], u[R][T];
@@ -414,34 +430,40 @@ __global__ __launch_bounds__(1024) void k_dec_gateup(LayerView L, const uint16_t
             // otherwise sink them behind the code arithmetic, costing a second round trip)
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                sgb[i] = gs[i * nb + b];
-                sub[i] = us[i * nb + b];
+                sgb[i] = gs[ro[i] * nb + b];
+                sub[i] = us[ro[i] * nb + b];
             }
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                load_codes<FMT>(gc + i * rb + (int64_t)b * block_bytes(FMT), wg[i]);
-                load_codes<FMT>(uc + i * rb + (int64_t)b * block_bytes(FMT), wu[i]);
+                load_codes<FMT>(gc + ro[i] * rb + (int64_t)b * block_bytes(FMT), wg[i]);
+                load_codes<FMT>(uc + ro[i] * rb + (int64_t)b * block_bytes(FMT), wu[i]);
             }
             __builtin_amdgcn_sched_barrier(0);
+            // matrix- and row-outer: each row's codes become fp16 pairs once, and the staged x of
+            // every token is read from LDS per row (few registers live at a time, so nothing spills
+            // at 4 tokens)
+            auto rowdot = [&](const uint32_t (&w)[8], uint16_t sc, float (&acc)[T]) __attribute__((always_inline)) {
+                uint32_t pw[16];
+                code_pairs<FMT>(w, pw);
+                const float sf = f16_to_f32(sc);
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                uint32_t xr[16];
+                for (int t = 0; t < T; ++t) {
+                    uint32_t xr[16];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint4 v = xq[((size_t)t * 4 + c) * nb + b];
-                    xr[4 * c] = v.x; xr[4 * c + 1] = v.y; xr[4 * c + 2] = v.z; xr[4 * c + 3] = v.w;
+                    for (int c = 0; c < 4; ++c) {
+                        const uint4 v = xq[((size_t)t * 4 + c) * nb + b];
+                        xr[4 * c] = v.x; xr[4 * c + 1] = v.y; xr[4 * c + 2] = v.z; xr[4 * c + 3] = v.w;
+                    }
+                    float d = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) d = dot2(pw[j], xr[j], d);
+                    acc[t] += sf * d;
                 }
+            };
 #pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    uint32_t pg[16], pu[16];
-                    code_pairs<FMT>(wg[i], pg);
-                    code_pairs<FMT>(wu[i], pu);
-                    float dg = 0.f, du = 0.f;
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) { dg = dot2(pg[j], xr[j], dg); du = dot2(pu[j], xr[j], du); }
-                    g[i][t] += f16_to_f32(sgb[i]) * dg;
-                    u[i][t] += f16_to_f32(sub[i]) * du;
-                }
+            for (int i = 0; i < R; ++i) {
+                rowdot(wg[i], sgb[i], g[i]);
+                rowdot(wu[i], sub[i], u[i]);
             }
         }
 #pragma unroll
@@ -450,7 +472,7 @@ __global__ __launch_bounds__(1024) void k_dec_gateup(LayerView L, const uint16_t
             for (int t = 0; t < T; ++t) {
                 const float gs_ = wave_sum(g[i][t]);
                 const float us_ = wave_sum(u[i][t]);
-                if (lane == 0 && ((mask >> t) & 1u)) {
+                if (lane == 0 && i < nv && ((mask >> t) & 1u)) {
                     const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
                     put_staged<FMT>(reinterpret_cast<_Float16*>(h + (size_t)row * Imax), Imax / 32, n0 + i,
                                     silu_mul(gs_, us_));
@@ -478,7 +500,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
                                                   const float* __restrict__ h, float* __restrict__ out,
                                                   float* __restrict__ y_pairs, float* __restrict__ y_shared,
                                                   int items_max) {
-    constexpr int RPW = kDownRows, MAXJ = kDownJ;
+    constexpr int RPW = kDownRows, MAXJ = down_batch(T);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     DecodePlan& P = *reinterpret_cast<DecodePlan*>(smem);
     uint4* hq = reinterpret_cast<uint4*>(smem + lds_head(L.E));
@@ -719,15 +741,15 @@ static int cu_count() {
 template <int FMT, int T, bool ROUTE, int KPL>
 static moe_status launch_gateup(const LayerView& L, const uint16_t* x, const float* logits, int32_t* ids, float* p,
                                 float* h, DecodePlan* plan_g, hipStream_t s) {
-    const int64_t rows1 = (int64_t)T * L.k * L.I + L.Is;
-    const int64_t waves1 = (rows1 + kGateUpRows - 1) / kGateUpRows;
+    constexpr int R = gateup_rows(T);
+    const int64_t waves1 = (int64_t)T * L.k * ((L.I + R - 1) / R) + (L.Is + R - 1) / R;   // tasks, at most
     const size_t sm = gateup_smem_bytes(T, L.H, L.E);
     auto kern = k_dec_gateup<FMT, T, ROUTE, KPL>;
     if (!allow_smem(kern, sm)) return MOE_ERR_UNSUPPORTED;
     // waves per block chosen so that the blocks spread evenly over the CUs (4..16 waves), and at
     // most one block per CU: the waves stride over the rows of the experts actually chosen
     const int cus = cu_count();
-    const int64_t wpb = std::min<int64_t>(16, std::max<int64_t>(4, (waves1 + cus - 1) / cus));
+    const int64_t wpb = std::min<int64_t>(gateup_max_waves(T), std::max<int64_t>(4, (waves1 + cus - 1) / cus));
     const int64_t blocks = std::min<int64_t>((waves1 + wpb - 1) / wpb, cus);
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3((unsigned)(wpb * kWave)), sm, s, L, x, logits, ids, p, h,
                        plan_g);
