@@ -376,7 +376,7 @@ def main():
     else:
         value, ms, roof, cfg = decode_workload(args.workload, args.steps, args.warmup, graph=not args.eager)
         metric = "MoE-layer tokens/s (decode, %% HBM peak on expert-weight bytes)"
-        secondary = None if args.no_prefill else prefill_workload(max(3, args.steps // 4), 2)
+        secondary = None if args.no_prefill else prefill_workload(max(10, args.steps), 3)
     line = {"metric": metric.replace("%%", "%"), "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "f16" if args.workload == "prefill8k" else "f32",
