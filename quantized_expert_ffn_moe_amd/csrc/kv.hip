@@ -6,11 +6,11 @@
 // section "KV transfer and next update"). Both kernels are HBM-bound streams:
 //   k_kv_encode  one thread per 32-value block: 64 bytes of bf16 in, max |v| in fp32,
 //                s = fp16(max / 127) saturating at 65504, codes rne(v / s) (fp32 division, correctly
-//                rounded) clamped to +-127, 32 bytes
-//                of codes and 2 bytes of scale out;
-//   k_kv_gather  one thread per (output row, block): the row index, 32 bytes of codes and the
-//                scale in, 128 bytes of exact fp32 values out; consecutive threads cover
-//                consecutive blocks of a row, so reads and writes are contiguous per row.
+//                rounded) clamped to +-127, 32 bytes of codes and 2 bytes of scale out;
+//   k_kv_gather  nb = D / 32 threads per output row, each taking 8 chunks of 4 values strided by
+//                nb chunks: all 8 code words and scales of a thread are in flight together, and
+//                at each of the 8 steps the row's threads read contiguous code bytes and write
+//                contiguous 16-byte pieces of exact fp32 values.
 #include "kernels.h"
 
 namespace moe {
@@ -62,24 +62,34 @@ __global__ __launch_bounds__(256) void k_kv_gather(const int8_t* __restrict__ co
     const int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (it >= nitems) return;
     const int64_t j = it / nb;
-    const int b = (int)(it - j * nb);
+    const int l = (int)(it - j * nb);
     const int32_t r = idx[j];
-    kv_f32x4* dst = reinterpret_cast<kv_f32x4*>(out + it * 32);
+    const int D = 32 * nb;
+    float* dst = out + j * D;
+    // lane l of the row's nb lanes takes the 4-value chunks l, l + nb, ..., l + 7 nb: for each of
+    // its 8 steps the row's lanes read 4 nb contiguous code bytes and write 16 nb contiguous bytes
     if ((uint32_t)r >= (uint32_t)n_rows) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) dst[q] = kv_f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 8; ++q) *reinterpret_cast<kv_f32x4*>(dst + 4 * (l + nb * q)) = kv_f32x4{0.f, 0.f, 0.f, 0.f};
         return;
     }
-    const int64_t blk = (int64_t)r * nb + b;
-    const kv_u32x4* src = reinterpret_cast<const kv_u32x4*>(codes + blk * 32);
-    const kv_u32x4 c0 = src[0], c1 = src[1];
-    const float s = f16_to_f32(scales[blk]);
-    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const int8_t* crow = codes + (int64_t)r * D;
+    const uint16_t* srow = scales + (int64_t)r * nb;
+    uint32_t w[8];
+    uint16_t sc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int e0 = 4 * (l + nb * q);
+        w[q] = *reinterpret_cast<const uint32_t*>(crow + e0);
+        sc[q] = srow[e0 / 32];
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const uint32_t u = w[q];
-        dst[q] = kv_f32x4{(float)(int8_t)(u & 0xFFu) * s, (float)(int8_t)((u >> 8) & 0xFFu) * s,
-                          (float)(int8_t)((u >> 16) & 0xFFu) * s, (float)(int8_t)(u >> 24) * s};
+        const float s = f16_to_f32(sc[q]);
+        *reinterpret_cast<kv_f32x4*>(dst + 4 * (l + nb * q)) =
+            kv_f32x4{(float)(int8_t)(u & 0xFFu) * s, (float)(int8_t)((u >> 8) & 0xFFu) * s,
+                     (float)(int8_t)((u >> 16) & 0xFFu) * s, (float)(int8_t)(u >> 24) * s};
     }
 }
 
