@@ -7,21 +7,26 @@
 namespace moe {
 
 // Rows are fp32 (the C-ABI call) or fp16 (the fused layer's internal rows); the sum is fp32 either
-// way. A thread owns 8 consecutive columns of one token: 32 bytes of an fp32 row or 16 of an fp16 one.
+// way. Thread c of a token owns the 4 columns 4c .. 4c + 3 and the 4 columns H/2 + 4c ..: each of
+// its loads and stores is then contiguous over the lanes of a wave (16 or 8 bytes a lane).
 template <typename RT>
-__device__ __forceinline__ void load8(const RT* row, int c8, float (&v)[8]);
+__device__ __forceinline__ void load8(const RT* row, int c, int half, float (&v)[8]);
 template <>
-__device__ __forceinline__ void load8<float>(const float* row, int c8, float (&v)[8]) {
-    const float4 a = reinterpret_cast<const float4*>(row)[2 * c8];
-    const float4 b = reinterpret_cast<const float4*>(row)[2 * c8 + 1];
+__device__ __forceinline__ void load8<float>(const float* row, int c, int half, float (&v)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(row)[c];
+    const float4 b = reinterpret_cast<const float4*>(row + half)[c];
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 template <>
-__device__ __forceinline__ void load8<_Float16>(const _Float16* row, int c8, float (&v)[8]) {
-    typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-    const half8_t h = reinterpret_cast<const half8_t*>(row)[c8];
+__device__ __forceinline__ void load8<_Float16>(const _Float16* row, int c, int half, float (&v)[8]) {
+    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+    const half4_t a = reinterpret_cast<const half4_t*>(row)[c];
+    const half4_t b = reinterpret_cast<const half4_t*>(row + half)[c];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)h[e];
+    for (int e = 0; e < 4; ++e) {
+        v[e] = (float)a[e];
+        v[4 + e] = (float)b[e];
+    }
 }
 
 // The k rows of a token are read four at a time with every load of a group in flight before any
@@ -32,7 +37,8 @@ __global__ __launch_bounds__(256) void k_combine(int T, int k, int H, const floa
                                                  const int32_t* __restrict__ row_of_pair,
                                                  const RT* __restrict__ y_shared, float* __restrict__ out) {
     const int t = blockIdx.y;
-    const int c8 = blockIdx.x * blockDim.x + threadIdx.x;  // group of 8 columns
+    const int c8 = blockIdx.x * blockDim.x + threadIdx.x;  // columns 4 c8 .. and H/2 + 4 c8 ..
+    const int half = H / 2;
     __shared__ float ps[16];
     __shared__ int rows[16];
     if (threadIdx.x < k) {
@@ -52,7 +58,7 @@ __global__ __launch_bounds__(256) void k_combine(int T, int k, int H, const floa
         for (int jj = 0; jj < 4; ++jj) {
             const int r = j0 + jj < k ? rows[j0 + jj] : -1;
             ok[jj] = (unsigned)r < (unsigned)(T * k);
-            load8<RT>(y_rows + (size_t)(ok[jj] ? r : 0) * H, c8, v[jj]);
+            load8<RT>(y_rows + (size_t)(ok[jj] ? r : 0) * H, c8, half, v[jj]);
         }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -64,13 +70,12 @@ __global__ __launch_bounds__(256) void k_combine(int T, int k, int H, const floa
     }
     if (y_shared) {
         float v[8];
-        load8<RT>(y_shared + (size_t)t * H, c8, v);
+        load8<RT>(y_shared + (size_t)t * H, c8, half, v);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += v[e];
     }
-    float4* o = reinterpret_cast<float4*>(out + (size_t)t * H) + 2 * c8;
-    o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    reinterpret_cast<float4*>(out + (size_t)t * H)[c8] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    reinterpret_cast<float4*>(out + (size_t)t * H + half)[c8] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 moe_status launch_combine(int T, int k, int H, const float* p, const float* y_rows, const int32_t* row_of_pair,

@@ -139,26 +139,35 @@ __host__ __device__ inline int kperm(int e, int G) {
 }
 
 // -------------------------------------------------------------------------------- x to fp16
-// x (bf16) -> fp16, 16 elements per thread, stored with the format's K permutation.
-template <int G>
-__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, int64_t n16, _Float16* __restrict__ x16) {
+// x (bf16) -> fp16, stored with the format's K permutation: VPT = 8 elements per thread when the
+// permutation groups hold at most 8 (one 16-byte load and store per thread, contiguous over a
+// wave), else 16.
+template <int G, int VPT>
+__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, int64_t nv, _Float16* __restrict__ x16) {
+    static_assert(VPT % G == 0, "a thread holds whole permutation groups");
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n16) return;
-    const uint4* src = reinterpret_cast<const uint4*>(x) + 2 * i;
-    const uint4 a = src[0], b = src[1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    _Float16 o[16];
+    if (i >= nv) return;
+    const uint4* src = reinterpret_cast<const uint4*>(x) + (VPT / 8) * i;
+    uint32_t w[VPT / 2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int h = 0; h < VPT / 8; ++h) {
+        const uint4 a = src[h];
+        w[4 * h] = a.x; w[4 * h + 1] = a.y; w[4 * h + 2] = a.z; w[4 * h + 3] = a.w;
+    }
+    _Float16 o[VPT];
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) {
         const float v = (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
         o[kperm(e, G)] = (_Float16)v;
     }
-    half8* dst = reinterpret_cast<half8*>(x16) + 2 * i;
-    half8 lo, hi;
+    half8* dst = reinterpret_cast<half8*>(x16) + (VPT / 8) * i;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { lo[e] = o[e]; hi[e] = o[8 + e]; }
-    dst[0] = lo;
-    dst[1] = hi;
+    for (int h = 0; h < VPT / 8; ++h) {
+        half8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = o[8 * h + e];
+        dst[h] = v;
+    }
 }
 
 // -------------------------------------------------------------------------------- dequantisation
@@ -724,8 +733,9 @@ static moe_status launch_prefill_f(const LayerView& L, const uint16_t* x, int T,
                                    const int32_t* perm, void* y_sorted, void* y_shared, bool y16,
                                    const PrefillScratch& s, hipStream_t st) {
     constexpr int G = perm_group<FMT>();
-    const int64_t n16 = (int64_t)T * L.H / 16;
-    hipLaunchKernelGGL(k_x_to_f16<G>, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st, x, n16, s.x16);
+    constexpr int VPT = G <= 8 ? 8 : 16;
+    const int64_t nv = (int64_t)T * L.H / VPT;
+    hipLaunchKernelGGL((k_x_to_f16<G, VPT>), dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, st, x, nv, s.x16);
     MOE_LAUNCH_CHECK();
     const int mt = max_tiles(T, L.k, L.E);
     const int nt1 = (L.Imax() + 127) / 128;
