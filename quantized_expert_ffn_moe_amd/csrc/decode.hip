@@ -16,8 +16,9 @@
 //                    laid out to match the packed codes; then gate/up rows streamed with every
 //                    load of a wave issued up front: codes become fp16 by OR-ing them into the
 //                    mantissa of 1024.0 and multiply into x with v_dot2_f32_f16 (fp32
-//                    accumulation); the constant 1024 (and the code offset) is removed once per
-//                    block with a precomputed sum over x. Block 0 publishes ids and p.
+//                    accumulation); for one or two tokens the constant 1024 (and the code
+//                    offset) is removed once per block with a sum over the staged x, for three or
+//                    four by a packed subtract per code pair. Block 0 publishes ids and p.
 //   k_dec_down       output rows m: every chosen expert's down row m times its h (LDS as fp16
 //                    hi/lo pairs, laid out so that lanes reading consecutive 32-blocks hit
 //                    consecutive banks), weighted by the routing probability and summed with the
@@ -160,48 +161,63 @@ constexpr uint32_t kMagic = 0x64006400u;  // (1024.0, 1024.0) as fp16 pair
 
 // Subtract the same constant K from both fp16 halves; exact when K and the results are integers
 // below 2048 (all values here are).
-template <int K>
+template <int K, bool SUB = true>
 __device__ __forceinline__ uint32_t sub_k(uint32_t pr) {
+    if constexpr (!SUB) return pr;
     half2_t v = __builtin_bit_cast(half2_t, pr);
     v -= half2_t{(_Float16)(float)K, (_Float16)(float)K};
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// The constant sub_k takes off code pair p of a block (p = 0 .. 15, in code_pairs' order).
+template <int FMT>
+__device__ __forceinline__ float pair_offset(int p) {
+    if constexpr (FMT == MOE_Q4_B32) return (p & 1) ? 1152.f : 1032.f;
+    else if constexpr (FMT == MOE_Q8_B32) return 1152.f;
+    else {
+        const int j = p & 7;
+        return j == 0 ? 1027.f : j == 1 ? 1030.f : j == 2 ? 1048.f : j == 3 ? 1120.f : j == 4 ? 1408.f
+             : j == 5 ? 1027.f : j == 6 ? 1036.f : 1072.f;
+    }
+}
+
 // The 16 fp16 pairs of one 32-element block, each half = f * level exactly: the stored code (offset
 // to be unsigned) is OR-ed into the mantissa of 1024.0 at f times its unit, then 1024 + f * offset
-// is subtracted (Q4: offset 8, Q8: offset 128, Q2: offset 1.5, the level being c - 1.5).
-template <int FMT>
+// is subtracted (Q4: offset 8, Q8: offset 128, Q2: offset 1.5, the level being c - 1.5). With
+// SUB = false the subtraction is left out: each half is pair_offset(p) + f * level, and the caller
+// removes pair_offset(p) times the pair's activations once per block.
+template <int FMT, bool SUB = true>
 __device__ __forceinline__ void code_pairs(const uint32_t* w, uint32_t (&pr)[16]) {
     if constexpr (FMT == MOE_Q4_B32) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const uint32_t u = w[d] ^ 0x88888888u;
             const uint32_t v = u >> 8;
-            pr[4 * d + 0] = sub_k<1032>((u & 0x000F000Fu) | kMagic);
-            pr[4 * d + 1] = sub_k<1152>((u & 0x00F000F0u) | kMagic);
-            pr[4 * d + 2] = sub_k<1032>((v & 0x000F000Fu) | kMagic);
-            pr[4 * d + 3] = sub_k<1152>((v & 0x00F000F0u) | kMagic);
+            pr[4 * d + 0] = sub_k<1032, SUB>((u & 0x000F000Fu) | kMagic);
+            pr[4 * d + 1] = sub_k<1152, SUB>((u & 0x00F000F0u) | kMagic);
+            pr[4 * d + 2] = sub_k<1032, SUB>((v & 0x000F000Fu) | kMagic);
+            pr[4 * d + 3] = sub_k<1152, SUB>((v & 0x00F000F0u) | kMagic);
         }
     } else if constexpr (FMT == MOE_Q8_B32) {
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
             const uint32_t u = w[d] ^ 0x80808080u;
-            pr[2 * d + 0] = sub_k<1152>((u & 0x00FF00FFu) | kMagic);
-            pr[2 * d + 1] = sub_k<1152>(((u >> 8) & 0x00FF00FFu) | kMagic);
+            pr[2 * d + 0] = sub_k<1152, SUB>((u & 0x00FF00FFu) | kMagic);
+            pr[2 * d + 1] = sub_k<1152, SUB>(((u >> 8) & 0x00FF00FFu) | kMagic);
         }
     } else {
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
             const uint32_t u = w[d];
             const uint32_t v = u >> 9;   // elements 5..7 (and 13..15) at bits 1, 3, 5 (17, 19, 21)
-            pr[8 * d + 0] = sub_k<1027>(((u << 1) & 0x00060006u) | kMagic);
-            pr[8 * d + 1] = sub_k<1030>((u & 0x000C000Cu) | kMagic);
-            pr[8 * d + 2] = sub_k<1048>((u & 0x00300030u) | kMagic);
-            pr[8 * d + 3] = sub_k<1120>((u & 0x00C000C0u) | kMagic);
-            pr[8 * d + 4] = sub_k<1408>((u & 0x03000300u) | kMagic);
-            pr[8 * d + 5] = sub_k<1027>((v & 0x00060006u) | kMagic);
-            pr[8 * d + 6] = sub_k<1036>((v & 0x00180018u) | kMagic);
-            pr[8 * d + 7] = sub_k<1072>((v & 0x00600060u) | kMagic);
+            pr[8 * d + 0] = sub_k<1027, SUB>(((u << 1) & 0x00060006u) | kMagic);
+            pr[8 * d + 1] = sub_k<1030, SUB>((u & 0x000C000Cu) | kMagic);
+            pr[8 * d + 2] = sub_k<1048, SUB>((u & 0x00300030u) | kMagic);
+            pr[8 * d + 3] = sub_k<1120, SUB>((u & 0x00C000C0u) | kMagic);
+            pr[8 * d + 4] = sub_k<1408, SUB>((u & 0x03000300u) | kMagic);
+            pr[8 * d + 5] = sub_k<1027, SUB>((v & 0x00060006u) | kMagic);
+            pr[8 * d + 6] = sub_k<1036, SUB>((v & 0x00180018u) | kMagic);
+            pr[8 * d + 7] = sub_k<1072, SUB>((v & 0x00600060u) | kMagic);
         }
     }
 }
@@ -256,6 +272,24 @@ __device__ __forceinline__ void stage_pairs(const float (&v)[32], uint4* dst, si
     }
 }
 
+// sum over the block's code pairs p of pair_offset(p) times the two staged fp16 activations of pair
+// p (rounded exactly as stage_pairs<FMT, 1> rounds them): what the dot products of pairs left
+// without their offset (code_pairs<FMT, false>) carry in excess, in a fixed order
+template <int FMT>
+__device__ __forceinline__ float stage_corr(const float (&v)[32]) {
+    using F = Fmt<FMT>;
+    float c = 0.f;
+#pragma unroll
+    for (int d = 0; d < F::ND; ++d)
+#pragma unroll
+        for (int j = 0; j < F::NP; ++j) {
+            const float sc = F::xs(j);
+            const float a = (float)(_Float16)(v[F::e0(d, j)] * sc), b = (float)(_Float16)(v[F::e1(d, j)] * sc);
+            c += pair_offset<FMT>(d * F::NP + j) * (a + b);
+        }
+    return c;
+}
+
 // One activation h[row][n] written straight into the staged layout that stage_pairs<FMT, 2> builds
 // for a whole 32-block: row = [8][nbm] uint4 (pairs 0..15 as fp16 hi, then as fp16 lo), pair p of
 // block b at uint4 (p / 4) * nbm + b, component p % 4, half 0 for e0 and 1 for e1.
@@ -302,7 +336,7 @@ __host__ __device__ constexpr int down_batch(int T) { return T >= 3 ? 5 : 4; }
 __host__ __device__ inline size_t lds_head(int E) {
     return align_up(sizeof(DecodePlan), 16) + align_up((size_t)E * 4, 16) + 2 * 64 * 4;
 }
-static size_t gateup_smem_bytes(int T, int H, int E) { return lds_head(E) + (size_t)T * (H / 32) * 64; }
+static size_t gateup_smem_bytes(int T, int H, int E) { return lds_head(E) + (size_t)T * (H / 32) * (64 + 4); }
 
 // Per block: top-k of every token (given logits) or the given ids, the union of the chosen experts,
 // x as fp16 pairs; per wave: R consecutive rows of one expert's gate and up, all loads issued before
@@ -320,6 +354,11 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
     int* ids_s = reinterpret_cast<int*>(smem + align_up(sizeof(DecodePlan), 16) + align_up((size_t)L.E * 4, 16));
     float* p_s = reinterpret_cast<float*>(ids_s + 64);
     uint4* xq = reinterpret_cast<uint4*>(smem + lds_head(L.E));
+    float* xc = reinterpret_cast<float*>(xq + (size_t)T * 4 * (L.H / 32));   // [T][nb] pair-offset sums
+    // one or two tokens: code pairs keep their offsets and each block's dot product drops the
+    // pair-offset sum xc of its activations (one instruction per pair less); three or four tokens
+    // subtract per pair (the extra LDS read per token and block costs them more than it saves)
+    constexpr bool kSubPairs = T >= 3;   // code_pairs subtracts the offsets itself
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int H = L.H, nb = H / 32;
     const int Imax = L.Imax();
@@ -364,6 +403,7 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
             float v[32];
             bf16x32_to_f32(xraw[s], v);
             stage_pairs<FMT, 1>(v, xq + (size_t)(tb / nb) * 4 * nb + tb % nb, nb);
+            if constexpr (!kSubPairs) xc[tb] = stage_corr<FMT>(v);
         }
     }
     for (int tb = threadIdx.x + kMaxStage * blockDim.x; tb < T * nb; tb += blockDim.x) {
@@ -374,6 +414,7 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
         float v[32];
         bf16x32_to_f32(raw, v);
         stage_pairs<FMT, 1>(v, xq + (size_t)(tb / nb) * 4 * nb + tb % nb, nb);
+        if constexpr (!kSubPairs) xc[tb] = stage_corr<FMT>(v);
     }
     if constexpr (ROUTE) __syncthreads();   // every token's choices in ids_s
     if (wave == 0) build_plan_wave(ids_src, ROUTE ? p_s : nullptr, T, L.k, L.E, P, first);
@@ -444,7 +485,7 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
             // at 4 tokens)
             auto rowdot = [&](const uint32_t (&w)[8], uint16_t sc, float (&acc)[T]) __attribute__((always_inline)) {
                 uint32_t pw[16];
-                code_pairs<FMT>(w, pw);
+                code_pairs<FMT, kSubPairs>(w, pw);
                 const float sf = f16_to_f32(sc);
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
@@ -457,7 +498,8 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
                     float d = 0.f;
 #pragma unroll
                     for (int j = 0; j < 16; ++j) d = dot2(pw[j], xr[j], d);
-                    acc[t] += sf * d;
+                    if constexpr (kSubPairs) acc[t] += sf * d;
+                    else acc[t] += sf * (d - xc[t * nb + b]);
                 }
             };
 #pragma unroll
