@@ -78,7 +78,7 @@ struct PermWs { int32_t* chunks; };
 PermWs carve_perm(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
     Carve c(base);
     PermWs r;
-    r.chunks = c.take<int32_t>((size_t)perm_chunks(T) * d->num_experts);
+    r.chunks = c.take<int32_t>(perm_scratch_ints(T, d->num_experts));
     if (bytes) *bytes = c.bytes();
     return r;
 }
@@ -127,7 +127,7 @@ LayerWs carve_layer(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
         r.offsets = c.take<int32_t>((size_t)d->num_experts + 1);
         r.perm = c.take<int32_t>(P);
         r.inv = c.take<int32_t>(P);
-        r.chunks = c.take<int32_t>((size_t)perm_chunks(T) * d->num_experts);
+        r.chunks = c.take<int32_t>(perm_scratch_ints(T, d->num_experts));
         r.prefill = c.take<char>(prefill_scratch_bytes(shape_view(d), T));
         const size_t pb = router_scratch_bytes(T, d->hidden, d->num_experts);
         r.router_part = pb ? c.take<float>(pb / sizeof(float)) : nullptr;

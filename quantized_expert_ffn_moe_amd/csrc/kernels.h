@@ -28,8 +28,9 @@ moe_status launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 moe_status launch_route_topk(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E, int k,
                              float* logits, int32_t* ids, float* p, float* scratch, hipStream_t s);
 
-// permutation: counts/bases scratch of chunks(T) * E ints
+// permutation: scratch of perm_scratch_ints(T, E) ints (per-chunk counts, then per-expert totals)
 int perm_chunks(int T);
+size_t perm_scratch_ints(int T, int E);
 moe_status launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* perm, int32_t* inv,
                           int32_t* chunk_scratch, hipStream_t s);
 

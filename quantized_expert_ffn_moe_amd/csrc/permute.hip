@@ -5,8 +5,9 @@
 // contiguous. Deterministic and atomic-free on the order:
 //   1. per chunk of 64 tokens, per-expert counts (LDS histogram; counts do not depend on order),
 //      stored expert-major: counts[e][c];
-//   2. one block turns counts[e][c] into its exclusive prefix sum in that (expert, chunk) order,
-//      which is at once offsets[e] (the value at c = 0) and each chunk's first slot base[e][c];
+//   2. one wave per expert turns its counts[e][c] into their exclusive prefix (the chunk's base
+//      inside the expert) and writes the expert's total; the offsets are the exclusive prefix of
+//      the totals, which every step-3 block derives itself (block 0 writes them out);
 //   3. per chunk, a pair's rank inside its expert is the number of earlier tokens of the chunk
 //      that chose the same expert: a 64-bit LDS mask of tokens per expert, popcount below the lane.
 // Token t's k choices are distinct (top-k output), so each token adds at most one pair per expert.
@@ -19,6 +20,7 @@ namespace moe {
 constexpr int kChunk = 64;
 
 int perm_chunks(int T) { return (T + kChunk - 1) / kChunk; }
+size_t perm_scratch_ints(int T, int E) { return (size_t)(perm_chunks(T) + 1) * E; }
 
 __global__ __launch_bounds__(64) void k_perm_hist(const int32_t* __restrict__ ids, int T, int k, int E,
                                                   int32_t* __restrict__ counts) {
@@ -37,97 +39,67 @@ __global__ __launch_bounds__(64) void k_perm_hist(const int32_t* __restrict__ id
     for (int e = lane; e < E; e += kWave) counts[(size_t)e * nc + c] = cnt[e];
 }
 
-// One block of 1024 threads: thread i owns the contiguous segment [i * per, (i + 1) * per) of the
-// n = E * nchunks counts (per a multiple of 16), sums it, a block scan of the 1024 sums gives each
-// segment's start, and a second pass writes the exclusive prefix in place. Counts move 16 per step
-// with four independent 16-byte accesses; segments of up to 32 are read once and kept in registers.
-__global__ __launch_bounds__(1024) void k_perm_scan(int32_t* __restrict__ counts, int nchunks, int E,
-                                                    int32_t* __restrict__ offsets) {
-    __shared__ int32_t part[1024];
-    const int tid = threadIdx.x;
-    const int n = E * nchunks;
-    const int per = ((n + 1023) / 1024 + 15) & ~15;
-    const int lo = min(tid * per, n), hi = min(lo + per, n);
-    auto load16 = [&](int i, int (&v)[16]) {
-        if (i + 16 <= hi) {
+// Exclusive prefix of a wave's per-lane values (every lane also gets the total).
+__device__ __forceinline__ int wave_excl_scan(int v, int& total) {
+    const int lane = threadIdx.x % kWave;
+    int incl = v;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int4 w = reinterpret_cast<const int4*>(counts + i)[q];
-                v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] = i + j < hi ? counts[i + j] : 0;
-        }
-    };
-    // up to 32 counts per thread stay in registers between the two passes (one read of the counts)
-    const bool held = per <= 32;
-    int h0[16], h1[16];
-    int sum = 0;
-    if (held) {
-        if (lo < hi) load16(lo, h0);
-        else
-#pragma unroll
-            for (int j = 0; j < 16; ++j) h0[j] = 0;
-        if (lo + 16 < hi) load16(lo + 16, h1);
-        else
-#pragma unroll
-            for (int j = 0; j < 16; ++j) h1[j] = 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sum += h0[j] + h1[j];
-    } else {
-        for (int i = lo; i < hi; i += 16) {
-            int v[16];
-            load16(i, v);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) sum += v[j];
-        }
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int u = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += u;
     }
-    part[tid] = sum;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int v = tid >= d ? part[tid - d] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    int run = part[tid] - sum;
-    int e = lo / nchunks, c = lo - e * nchunks;
-    for (int i = lo; i < hi; i += 16) {
-        int v[16], o[16];
-        if (held) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] = i == lo ? h0[j] : h1[j];
-        } else {
-            load16(i, v);
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            o[j] = run;
-            if (c == 0 && i + j < hi) offsets[e] = run;
-            run += v[j];
-            if (++c == nchunks) { c = 0; ++e; }
-        }
-        if (i + 16 <= hi) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                reinterpret_cast<int4*>(counts + i)[q] = make_int4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if (i + j < hi) counts[i + j] = o[j];
-        }
-    }
-    if (tid == 1023) offsets[E] = run;   // = total when every id is in range
+    total = __shfl(incl, kWave - 1, kWave);
+    return incl - v;
 }
 
+// One wave per expert: the counts of its chunks (contiguous, expert-major) become their exclusive
+// prefix in place, and the expert's total goes to totals[e].
+__global__ __launch_bounds__(64) void k_perm_scan_expert(int32_t* __restrict__ counts, int nchunks,
+                                                         int32_t* __restrict__ totals) {
+    const int e = blockIdx.x, lane = threadIdx.x;
+    int32_t* row = counts + (size_t)e * nchunks;
+    const int per = (nchunks + kWave - 1) / kWave;
+    const int lo = min(lane * per, nchunks), hi = min(lo + per, nchunks);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += row[i];
+    int total;
+    int run = wave_excl_scan(sum, total);
+    for (int i = lo; i < hi; ++i) {
+        const int v = row[i];
+        row[i] = run;
+        run += v;
+    }
+    if (lane == 0) totals[e] = total;
+}
+
+// Per chunk: the experts' offsets are the exclusive prefix of their totals (every block derives
+// them from the E totals itself; block 0 also writes them out), a pair's slot is its expert's
+// offset + the chunk's base inside the expert + its rank among the chunk's tokens of that expert.
 __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                     const int32_t* __restrict__ base, int32_t* __restrict__ perm,
+                                                     const int32_t* __restrict__ base,
+                                                     const int32_t* __restrict__ totals,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                      int32_t* __restrict__ inv) {
     extern __shared__ unsigned long long tokmask[];
+    int32_t* offs = reinterpret_cast<int32_t*>(tokmask + E);   // [E + 1]
     const int c = blockIdx.x, lane = threadIdx.x;
     for (int e = lane; e < E; e += kWave) tokmask[e] = 0ull;
+    {
+        const int per = (E + kWave - 1) / kWave;
+        const int lo = min(lane * per, E), hi = min(lo + per, E);
+        int sum = 0;
+        for (int i = lo; i < hi; ++i) sum += totals[i];
+        int total;
+        int run = wave_excl_scan(sum, total);
+        for (int i = lo; i < hi; ++i) {
+            offs[i] = run;
+            run += totals[i];
+        }
+        if (lane == 0) offs[E] = total;   // = kept pairs
+    }
     __syncthreads();
+    if (c == 0)
+        for (int e = lane; e <= E; e += kWave) offsets[e] = offs[e];
     const int t = c * kChunk + lane;
     if (t < T)
         for (int j = 0; j < k; ++j) {
@@ -144,7 +116,7 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
                 inv[q] = -1;
                 continue;
             }
-            const int pos = base[(size_t)e * gridDim.x + c] + __popcll(tokmask[e] & below);
+            const int pos = offs[e] + base[(size_t)e * gridDim.x + c] + __popcll(tokmask[e] & below);
             perm[pos] = q;
             inv[q] = pos;
         }
@@ -235,12 +207,13 @@ moe_status launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
         return MOE_OK;
     }
     const int nc = perm_chunks(T);
+    int32_t* totals = scratch + (size_t)nc * E;
     hipLaunchKernelGGL(k_perm_hist, dim3(nc), dim3(64), E * sizeof(int32_t), s, ids, T, k, E, scratch);
     MOE_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, scratch, nc, E, offsets);
+    hipLaunchKernelGGL(k_perm_scan_expert, dim3(E), dim3(64), 0, s, scratch, nc, totals);
     MOE_LAUNCH_CHECK();
-    hipLaunchKernelGGL(k_perm_scatter, dim3(nc), dim3(64), E * sizeof(unsigned long long), s, ids, T, k, E,
-                       scratch, perm, inv);
+    hipLaunchKernelGGL(k_perm_scatter, dim3(nc), dim3(64), E * sizeof(unsigned long long) + (E + 1) * sizeof(int32_t),
+                       s, ids, T, k, E, scratch, totals, offsets, perm, inv);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
