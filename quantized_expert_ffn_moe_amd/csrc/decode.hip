@@ -364,13 +364,20 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
     const int Imax = L.Imax();
     const int npairs = T * L.k;
 
-    // x chunks are loaded first (they do not depend on the routing)
-    constexpr int kMaxStage = 1;   // T * H / 32 <= 256 is staged from registers; the rest in a loop
+    // x is staged by the waves after the first T (the top-k waves; without routing, after wave 0,
+    // which builds the plan), so that the staging runs beside the top-k and the plan rather than
+    // after them; a block too small for that stages with all its threads. Its chunks are loaded
+    // first (they do not depend on the routing).
+    constexpr int kBusyWaves = ROUTE ? T : 1;
+    const int sb = (int)blockDim.x > kWave * kBusyWaves ? kWave * kBusyWaves : 0;
+    const int sn = (int)blockDim.x - sb;       // staging threads
+    const int sti = (int)threadIdx.x - sb;     // this thread's staging index (< 0: none)
+    constexpr int kMaxStage = 1;   // the first sn chunks are staged from registers, the rest in a loop
     uint4 xraw[kMaxStage][4];
 #pragma unroll
     for (int s = 0; s < kMaxStage; ++s) {
-        const int tb = threadIdx.x + s * blockDim.x;
-        if (tb < T * nb) {
+        const int tb = sti + s * sn;
+        if (sti >= 0 && tb < T * nb) {
             const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(tb / nb) * H + (size_t)(tb % nb) * 32);
 #pragma unroll
             for (int c = 0; c < 4; ++c) xraw[s][c] = xr[c];
@@ -395,18 +402,18 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
         ids_src = ids_s;
     }
 
-    // x staging (the waves without a top-k start at once)
+    // x staging
 #pragma unroll
     for (int s = 0; s < kMaxStage; ++s) {
-        const int tb = threadIdx.x + s * blockDim.x;
-        if (tb < T * nb) {
+        const int tb = sti + s * sn;
+        if (sti >= 0 && tb < T * nb) {
             float v[32];
             bf16x32_to_f32(xraw[s], v);
             stage_pairs<FMT, 1>(v, xq + (size_t)(tb / nb) * 4 * nb + tb % nb, nb);
             if constexpr (!kSubPairs) xc[tb] = stage_corr<FMT>(v);
         }
     }
-    for (int tb = threadIdx.x + kMaxStage * blockDim.x; tb < T * nb; tb += blockDim.x) {
+    for (int tb = sti + kMaxStage * sn; sti >= 0 && tb < T * nb; tb += sn) {
         uint4 raw[4];
         const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(tb / nb) * H + (size_t)(tb % nb) * 32);
 #pragma unroll
