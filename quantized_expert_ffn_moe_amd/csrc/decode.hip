@@ -423,8 +423,13 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
         stage_pairs<FMT, 1>(v, xq + (size_t)(tb / nb) * 4 * nb + tb % nb, nb);
         if constexpr (!kSubPairs) xc[tb] = stage_corr<FMT>(v);
     }
-    if constexpr (ROUTE) __syncthreads();   // every token's choices in ids_s
-    if (wave == 0) build_plan_wave(ids_src, ROUTE ? p_s : nullptr, T, L.k, L.E, P, first);
+    // every token's choices in ids_s before the plan: with one token the wave that chose them is
+    // the wave that builds the plan, so its own LDS writes only need to be complete
+    if constexpr (ROUTE && T > 1) __syncthreads();
+    if (wave == 0) {
+        if constexpr (ROUTE && T == 1) wave_lds_sync();
+        build_plan_wave(ids_src, ROUTE ? p_s : nullptr, T, L.k, L.E, P, first);
+    }
     __syncthreads();                        // the plan and the staged x
     if (blockIdx.x == 0) {
         const uint32_t* src = reinterpret_cast<const uint32_t*>(&P);
