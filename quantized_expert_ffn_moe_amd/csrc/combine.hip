@@ -41,8 +41,8 @@ __global__ __launch_bounds__(256) void k_combine(int T, int k, int H, const floa
     const int half = H / 2;
     __shared__ float ps[16];
     __shared__ int rows[16];
-    if (threadIdx.x < k) {
-        const int q = t * k + threadIdx.x;
+    if ((int)threadIdx.x < k) {
+        const int q = t * k + (int)threadIdx.x;
         ps[threadIdx.x] = p[q];
         rows[threadIdx.x] = row_of_pair ? row_of_pair[q] : q;
     }
