@@ -60,7 +60,7 @@ struct TileDesc {
 };
 
 // -------------------------------------------------------------------------------- tile list
-// One block of 1024 threads. Thread e < E takes expert e: floor(count / 128) full tiles and, for a
+// Each expert takes floor(count / 128) full tiles and, for a
 // remainder, one tile of 32 * ni rows (ni the power of two at or above ceil(rem / 32)). The list is
 // expert-major (each expert's tiles side by side, so that they run on one XCD and share its L2;
 // experts of every size end up mixed along the list, which balances the XCDs), the shared group
@@ -79,30 +79,49 @@ __host__ __device__ inline int rem_tile_ni(int rem) {
     return n <= 1 ? 1 : n <= 2 ? 2 : 4;
 }
 
-__global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict__ offsets, int E, int T, int k,
-                                                      int has_shared, int tiles_max, TileDesc* __restrict__ tiles,
-                                                      int32_t* __restrict__ ntiles) {
-    __shared__ int part[1024];   // inclusive prefix of the tile counts, then tile rows of each group
+// Built by one block of 256 threads (block 0 of k_x_to_f16): thread i takes experts
+// 4 i .. 4 i + 3 (E <= 1024).
+constexpr int kTileThreads = 256;
+__device__ __forceinline__ void build_tiles_block(const int32_t* __restrict__ offsets, int E, int T, int k,
+                                                  int has_shared, int tiles_max, TileDesc* __restrict__ tiles,
+                                                  int32_t* __restrict__ ntiles) {
+    __shared__ int part[1024];   // inclusive prefix of the tile counts of experts 0 .. e
     __shared__ int cnt[1025];    // rows of each group (the shared group last)
-    const int e = threadIdx.x;
-    int base = 0, n = 0;
-    if (e < E) group_rows(offsets, E, T, T * k, e, base, n);
-    cnt[e] = n;
-    if (e == 0) cnt[1024] = has_shared ? T : 0;
-    const int nt = (n + kTM - 1) / kTM;
-    part[e] = nt;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int v = e >= d ? part[e - d] : 0;
-        __syncthreads();
-        part[e] += v;
-        __syncthreads();
+    __shared__ int wsum[kTileThreads / kWave];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    int nt4[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = 4 * tid + q;
+        int base = 0, n = 0;
+        if (e < E) group_rows(offsets, E, T, T * k, e, base, n);
+        cnt[e] = n;
+        nt4[q] = (n + kTM - 1) / kTM;
+        sum += nt4[q];
     }
+    if (tid == 0) cnt[1024] = has_shared ? T : 0;
+    // block exclusive scan of the per-thread tile counts: wave scans, then the wave totals
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int u = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += u;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        run += nt4[q];
+        part[4 * tid + q] = run;
+    }
+    __syncthreads();
     const int routed = part[1023];
     const int total = min(routed + (cnt[1024] + kTM - 1) / kTM, tiles_max);
     // every thread writes tiles: slot i of the routed list belongs to the first group whose
     // inclusive prefix exceeds i (binary search), the rest to the shared group
-    for (int i = e; i < total; i += 1024) {
+    for (int i = tid; i < total; i += kTileThreads) {
         int g, first;
         if (i < routed) {
             int lo = 0, hi = 1023;
@@ -121,7 +140,7 @@ __global__ __launch_bounds__(1024) void k_build_tiles(const int32_t* __restrict_
         const int nf = rows / kTM;
         tiles[i] = TileDesc{g == 1024 ? E : g, j * kTM, j < nf ? kTM / 32 : rem_tile_ni(rows % kTM), 0};
     }
-    if (e == 0) *ntiles = total;
+    if (tid == 0) *ntiles = total;
 }
 
 int max_tiles(int T, int k, int E) { return (T * k) / kTM + T / kTM + E + 2; }
@@ -142,10 +161,19 @@ __host__ __device__ inline int kperm(int e, int G) {
 // x (bf16) -> fp16, stored with the format's K permutation: VPT = 8 elements per thread when the
 // permutation groups hold at most 8 (one 16-byte load and store per thread, contiguous over a
 // wave), else 16.
+// Block 0 builds the tile list instead (the two do not depend on each other; the first block is
+// dispatched first, so the longer tile build overlaps the conversion).
 template <int G, int VPT>
-__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, int64_t nv, _Float16* __restrict__ x16) {
+__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, int64_t nv, _Float16* __restrict__ x16,
+                                                  const int32_t* __restrict__ offsets, int E, int T, int k,
+                                                  int has_shared, int tiles_max, TileDesc* __restrict__ tiles,
+                                                  int32_t* __restrict__ ntiles) {
     static_assert(VPT % G == 0, "a thread holds whole permutation groups");
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (blockIdx.x == 0) {
+        build_tiles_block(offsets, E, T, k, has_shared, tiles_max, tiles, ntiles);
+        return;
+    }
+    const int64_t i = (int64_t)(blockIdx.x - 1) * 256 + threadIdx.x;
     if (i >= nv) return;
     const uint4* src = reinterpret_cast<const uint4*>(x) + (VPT / 8) * i;
     uint32_t w[VPT / 2];
@@ -735,7 +763,8 @@ static moe_status launch_prefill_f(const LayerView& L, const uint16_t* x, int T,
     constexpr int G = perm_group<FMT>();
     constexpr int VPT = G <= 8 ? 8 : 16;
     const int64_t nv = (int64_t)T * L.H / VPT;
-    hipLaunchKernelGGL((k_x_to_f16<G, VPT>), dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, st, x, nv, s.x16);
+    hipLaunchKernelGGL((k_x_to_f16<G, VPT>), dim3((unsigned)((nv + 255) / 256 + 1)), dim3(kTileThreads), 0, st, x, nv,
+                       s.x16, offsets, L.E, T, L.k, L.Is > 0 ? 1 : 0, max_tiles(T, L.k, L.E), s.tiles, s.ntiles);
     MOE_LAUNCH_CHECK();
     const int mt = max_tiles(T, L.k, L.E);
     const int nt1 = (L.Imax() + 127) / 128;
@@ -761,9 +790,6 @@ moe_status launch_prefill_experts(const LayerView& L, const uint16_t* x, int T, 
                                   const int32_t* perm, void* y_sorted, void* y_shared, bool y16, void* scratch,
                                   hipStream_t st) {
     const PrefillScratch s = carve_prefill(L, T, scratch, nullptr);
-    hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(1024), 0, st, offsets, L.E, T, L.k, L.Is > 0 ? 1 : 0,
-                       max_tiles(T, L.k, L.E), s.tiles, s.ntiles);
-    MOE_LAUNCH_CHECK();
     switch (L.fmt) {
         case MOE_Q8_B32: return launch_prefill_f<MOE_Q8_B32>(L, x, T, offsets, perm, y_sorted, y_shared, y16, s, st);
         case MOE_Q4_B32: return launch_prefill_f<MOE_Q4_B32>(L, x, T, offsets, perm, y_sorted, y_shared, y16, s, st);
