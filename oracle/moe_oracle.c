@@ -364,9 +364,11 @@ void orc_kv_encode(const uint16_t* src, int32_t rows, int32_t D, int8_t* codes, 
             float sf = (float)orc_f16(sb);
             scales[(int64_t)r * (D / 32) + b] = sb;
             for (int i = 0; i < 32; ++i) {
+                /* a NaN value gets code 0 (it took no part in the maximum above either) */
+                const float xv = (float)orc_bf16(v[i]);
                 int c = 0;
-                if (sf != 0.0f) {
-                    float t = rintf((float)orc_bf16(v[i]) / sf);
+                if (sf != 0.0f && !isnan(xv)) {
+                    float t = rintf(xv / sf);
                     c = t > 127.0f ? 127 : t < -127.0f ? -127 : (int)t;
                 }
                 codes[(int64_t)r * D + 32 * b + i] = (int8_t)c;

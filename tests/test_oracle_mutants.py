@@ -33,7 +33,8 @@ MUTANTS = {
     "combine_alone_row_map": ("int64_t r = row_of_pair ? row_of_pair[q] : q;", "int64_t r = q;"),
     "kv_scale_divisor": ("float q = m / 127.0f;", "float q = m / 128.0f;"),
     "kv_scale_overflow": ("if (sb == 0x7C00u) sb = 0x7BFFu;", ";"),
-    "kv_ties_away": ("float t = rintf((float)orc_bf16(v[i]) / sf);", "float t = roundf((float)orc_bf16(v[i]) / sf);"),
+    "kv_ties_away": ("float t = rintf(xv / sf);", "float t = roundf(xv / sf);"),
+    "kv_nan_in_max": ("if (a > m) m = a;", "if (!(a <= m)) m = a;"),
     "kv_f16_truncation": ("double m = nearbyint(a / step);", "double m = floor(a / step);"),
     "kv_gather_block_index": ("orc_f16(scales[(int64_t)r * (D / 32) + d / 32])", "orc_f16(scales[(int64_t)r * (D / 32) + d % (D / 32)])"),
     "up_uses_gate": ("u += weight(fmt, u_codes, u_scales, H, n, kappa) * x[kappa];",

@@ -444,7 +444,24 @@ def pin_kv_scale_saturates():
     assert abs(v[2] - 3 * 65504.0) < 0.5 * 65504.0   # the truncated bf16 input still rounds to code 3
 
 
-KV_PINS = [("kv_scale_saturates", pin_kv_scale_saturates), ("kv_f16_rounding", pin_kv_f16_rounding), ("kv_worked_example", pin_kv_worked_example),
+def pin_kv_nan_inputs():
+    """Reading of the codec for NaN inputs (the pages say nothing of them): a NaN takes no part in
+    its block's maximum and gets code 0; a block of NaNs only gets scale 0. Hand-computed block:
+    [NaN, 127, -63.5, -NaN, 0 ...] -> max 127, scale fp16(127 / 127) = 1.0 (0x3C00), codes
+    [0, 127, -64 (a tie, to even), 0, 0 ...]."""
+    vals = np.zeros((2, 32), np.float32)
+    vals[0, 1:3] = [127.0, -63.5]
+    src = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    src[0, 0] = 0x7FC0            # quiet NaN
+    src[0, 3] = 0xFFC1            # negative NaN with a payload
+    src[1, :] = 0x7F81            # a whole block of NaNs
+    codes, scales = oracle.kv_encode(src)
+    assert int(scales[0, 0]) == 0x3C00 and int(scales[1, 0]) == 0
+    assert codes[0, :4].tolist() == [0, 127, -64, 0]
+    assert np.all(codes[0, 4:] == 0) and np.all(codes[1] == 0)
+
+
+KV_PINS = [("kv_nan_inputs", pin_kv_nan_inputs), ("kv_scale_saturates", pin_kv_scale_saturates), ("kv_f16_rounding", pin_kv_f16_rounding), ("kv_worked_example", pin_kv_worked_example),
            ("kv_round_trip", pin_kv_round_trip), ("kv_symmetry", pin_kv_symmetry), ("kv_gather", pin_kv_gather),
            ("kv_ties_to_even", pin_kv_ties_to_even)]
 
