@@ -36,8 +36,17 @@
  *     waits on another block of its own grid; every cross-block dependency is a kernel boundary,
  *     so calls may be captured in a HIP graph. Expert ids read from memory are range-checked
  *     before they address weights.
- *   - Preconditions that are not checked: router logits are finite (no NaN); ids passed in are in
- *     [0, E) and distinct within a token; buffers hold the documented number of elements.
+ *   - Preconditions that are not checked: x is finite with |x| < 2^60 and the router logits are
+ *     finite (no NaN); ids passed in are in [0, E) and distinct within a token; buffers hold the
+ *     documented number of elements.
+ *   - Activation range: the expert paths multiply 16-bit operands (fp16) on the dot-product units
+ *     and the matrix cores. Each token's activations are taken at an exact power-of-two scale
+ *     2^e_t, chosen from the token's largest |x| so that it lands in [2, 4) (e_t clamped to
+ *     [-60, 60]); the SwiGLU activation h is kept at the scale 2^(2 e_t) (silu(g) * u is bounded
+ *     by |g| |u|, so it grows like x^2) and the expert outputs are multiplied by 2^(-2 e_t) in fp32.
+ *     Activations of any size therefore keep fp16's relative precision; 16-bit intermediates that
+ *     still leave the fp16 range (weights large enough that |h| 2^(2 e_t) exceeds 65504) saturate at
+ *     +-65504 rather than becoming inf.
  *
  * Data layout (row-major, innermost index contiguous)
  *   x            bf16 bits  [T][H]
@@ -120,7 +129,10 @@ typedef struct {
 } moe_layer_weights;
 
 /*
- * Router and top-k selection.
+ * Router and top-k selection (the router scores every expert and only a few run per token: 648news
+ * 10-cyber-on-strata-moe-local-inference, section "tiered VRAM/RAM inference"; the router is
+ * resident and finishes early: 648news 07-nano-cuda-moe-qwen38-release, section "asynchronous
+ * CPU/GPU compute").
  *   logits[t][e] = sum_h x[t][h] * w_router[e][h] + bias[e]   (fp32 accumulation)
  *   ids[t][j]    = the j-th expert in the order (logit descending, expert index ascending),
  *                  -0.0 and +0.0 being equal
@@ -133,6 +145,9 @@ moe_status moe_route(const moe_layer_desc* desc, const moe_layer_weights* w, con
                      float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Grouping of the (token, expert) pairs by expert, so that each chosen expert's weights serve all
+ * of its tokens at once (the grouped expert kernels of prompt processing: 648news
+ * 07-nano-cuda-moe-qwen38-release, section "speed comparison and accuracy check").
  * Stable counting sort of the pairs q = t*k + j by expert ids[q] (integer, deterministic):
  *   offsets[e] = number of pairs with expert < e (offsets[E] = T*k);
  *   pos(q) = offsets[ids[q]] + number of earlier pairs q' < q with the same expert;
@@ -144,24 +159,36 @@ moe_status moe_permute(const moe_layer_desc* desc, const int32_t* ids, int32_t T
                        int32_t* inv, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Expert FFNs for a decode step of 1 <= T <= 4 tokens (T > 4 returns MOE_ERR_UNSUPPORTED).
- * Each distinct chosen expert's weights are read once for all tokens that chose it.
+ * Expert FFNs for a decode step of 1 <= T <= 4 tokens: the selected experts run on the GPU and a
+ * token costs the bytes of the experts it reads (648news 07-nano-cuda-moe-qwen38-release, section
+ * "asynchronous CPU/GPU compute"; 648news 10-cyber-on-strata-moe-local-inference, section "bitwise
+ * validation and speed bottleneck"). Each distinct chosen expert's weights are read once for all
+ * tokens that chose it.
  *   y_pairs[q]  = D_e (silu(G_e x_t) * (U_e x_t)), e = ids[q], for every pair q = t*k + j
  *   y_shared[t] = the shared expert on x_t (required iff Is > 0, else ignored)
- * Math in fp32; dequantised weights are exact. Workspace: MOE_CALL_EXPERTS_DECODE.
+ * Dequantised weights are exact fp16 values; the dot products accumulate in fp32 over fp16
+ * operands: x rounded once to fp16 (at its token scale, see "Activation range"), h as an fp16
+ * hi + lo pair (about 22 bits). Workspace: MOE_CALL_EXPERTS_DECODE.
+ * The kernels keep every chosen pair's SwiGLU activations in LDS (160 KB per workgroup):
+ * 4 (T k + T) max(I, Is) bytes plus the routing plan and about 4 E bytes must fit; a shape beyond
+ * that (or T > 4) returns MOE_ERR_UNSUPPORTED before anything is enqueued, and so does
+ * moe_workspace_size(MOE_CALL_EXPERTS_DECODE).
  */
 moe_status moe_experts_decode(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x,
                               int32_t T, const int32_t* ids, float* y_pairs, float* y_shared, void* ws,
                               size_t ws_bytes, void* stream);
 
 /*
- * Expert FFNs for a prefill chunk (any T >= 1): a grouped GEMM over expert-sorted row tiles
+ * Expert FFNs for a prefill chunk (any T >= 1; prompts run in 8K-token chunks through GEMMs and
+ * grouped expert kernels: 648news 07-nano-cuda-moe-qwen38-release, section "speed comparison and
+ * accuracy check"): a grouped GEMM over expert-sorted row tiles
  * (rows in perm order, groups from offsets, as moe_permute returns them), with the shared
  * expert as one more group of all T tokens. Offsets are clamped to [0, T*k] and perm entries
  * outside [0, T*k) read token 0, so inconsistent inputs give wrong rows but no stray access.
  *   y_sorted[i] = expert FFN of pair perm[i] (sorted order), y_shared[t] as above.
- * Operands are fp16 on the matrix cores (x converted from bf16, weights dequantised once to fp16,
- * the SwiGLU activation h kept in fp16) with fp32 accumulation and fp32 outputs.
+ * Operands are fp16 on the matrix cores (x converted from bf16 at its token scale, weights
+ * dequantised once to fp16, the SwiGLU activation h kept in fp16 at the token scale squared; see
+ * "Activation range") with fp32 accumulation and fp32 outputs at the true scale.
  * Workspace: MOE_CALL_EXPERTS_PREFILL.
  */
 moe_status moe_experts_prefill(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x,
@@ -169,17 +196,20 @@ moe_status moe_experts_prefill(const moe_layer_desc* desc, const moe_layer_weigh
                                float* y_shared, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * moe_experts_prefill with the output rows in fp16 (IEEE binary16 bits, round to nearest even
- * from the fp32 accumulators): the form the fused layer keeps between its down GEMM and its
- * combine (half the bytes of the largest stream of the layer). Same kernels, same workspace
- * (MOE_CALL_EXPERTS_PREFILL); y_sorted and y_shared must be 16-byte aligned.
+ * moe_experts_prefill with the output rows in fp16 (IEEE binary16 bits, the fp32 row rounded to
+ * nearest even, saturating at +-65504): the precision the fused layer keeps between its down GEMM
+ * and its combine (half the bytes of the largest stream of the layer; inside the layer the rows
+ * stay at the token scale, so they never saturate for ordinary weights). Same kernels, same
+ * workspace (MOE_CALL_EXPERTS_PREFILL); y_sorted and y_shared must be 16-byte aligned.
  */
 moe_status moe_experts_prefill_f16(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x,
                                    int32_t T, const int32_t* offsets, const int32_t* perm, uint16_t* y_sorted,
                                    uint16_t* y_shared, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Weighted combine, atomic-free and deterministic:
+ * Weighted combine plus the always-used shared expert (resident beside the router: 648news
+ * 07-nano-cuda-moe-qwen38-release, section "asynchronous CPU/GPU compute"), atomic-free and
+ * deterministic:
  *   out[t] = sum_{j=0}^{k-1} p[t][j] * y_rows[r(t,j)] + y_shared[t]     (slot order, then shared)
  * with r(t,j) = row_of_pair[t*k+j] (e.g. inv from moe_permute) or t*k+j when row_of_pair is NULL;
  * a row outside [0, T*k) (a dropped pair) contributes nothing. y_shared may be NULL (no shared
@@ -189,10 +219,12 @@ moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const float* p, co
                        const int32_t* row_of_pair, const float* y_shared, float* out, void* stream);
 
 /*
- * The whole layer: route, permute, experts, combine. T <= 4 takes the decode path (three launches:
- * router GEMV; top-k + gate/up; down with the combine fused), larger T the prefill path (router GEMM,
- * top-k, permutation, grouped GEMMs, combine). out [T][H] fp32. logits/ids/p are optional outputs
- * (NULL = kept in the workspace). Workspace: MOE_CALL_LAYER.
+ * The whole layer: route, permute, experts, combine (the five steps above in one call). T <= 4
+ * takes the decode path (three launches: router GEMV; top-k + gate/up; down with the combine
+ * fused) when its LDS fits the shape (see moe_experts_decode), else, like larger T, the prefill
+ * path (router GEMM, top-k, permutation, grouped GEMMs, combine); moe_workspace_size sizes the
+ * path that is taken. out [T][H] fp32. logits/ids/p are optional outputs (NULL = kept in the
+ * workspace). Workspace: MOE_CALL_LAYER.
  */
 moe_status moe_layer(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x, int32_t T,
                      float* out, float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes,
@@ -203,8 +235,8 @@ moe_status moe_layer(const moe_layer_desc* desc, const moe_layer_weights* w, con
  * 07-nano-cuda-moe-qwen38-release, section "memory hierarchy spanning VRAM and RAM": the KV cache is
  * int8 with one scale per 32 values, and an indexer selects 2048 positions per query). Per block of
  * 32 values of a row, in fp32: m = max |v|, s = fp16(m / 127) rounded to nearest even and
- * saturating at 65504, code = rne(v / s) clamped to [-127, 127], or 0 when s is 0 (codes of NaN
- * inputs are unspecified).
+ * saturating at 65504, code = rne(v / s) clamped to [-127, 127], or 0 when s is 0. A NaN value takes
+ * no part in m and gets code 0.
  *   src bf16 [rows][D] -> codes int8 [rows][D], scales fp16 bits [rows][D/32]
  * D a multiple of 32, 32 <= D <= 65536; rows >= 0 (0 enqueues nothing). src and codes 16-byte
  * aligned, scales 2-byte aligned. No workspace.

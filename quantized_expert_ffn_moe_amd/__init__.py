@@ -128,6 +128,16 @@ def _stream(stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+def _keep(stream, *tensors):
+    """Tensors the binding allocated on torch's current stream but handed to work queued on another
+    stream: tell the caching allocator so their memory is not reused before that work is done."""
+    if stream is None or not isinstance(stream, torch.cuda.Stream) or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.device.type == "cuda":
+            t.record_stream(stream)
+
+
 class LayerDesc:
     def __init__(self, hidden: int, inter: int, num_experts: int, top_k: int, shared_inter: int, fmt: int):
         self.hidden, self.inter, self.num_experts = hidden, inter, num_experts
@@ -171,7 +181,9 @@ class DeviceLayer:
 
 
 class Workspace:
-    """A growable device byte buffer handed to the library (the library itself allocates nothing)."""
+    """A growable device byte buffer handed to the library (the library itself allocates nothing).
+    When it grows, the old buffer is released to torch's caching allocator; calls queued on a
+    stream other than torch's current one keep the buffer they used alive through record_stream."""
 
     def __init__(self, device="cuda"):
         self.device = device
@@ -216,6 +228,7 @@ def moe_route(layer: DeviceLayer, x, logits=None, ids=None, p=None, ws=None, str
     buf, nb = _ws(d, T, MOE_CALL_ROUTE, ws)
     _check(lib().moe_route(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(logits), _ptr(ids),
                            _ptr(p), _ptr(buf), nb, _stream(stream)), "moe_route")
+    _keep(stream, buf, ids, p)
     return logits, ids, p
 
 
@@ -229,6 +242,7 @@ def moe_permute(layer: DeviceLayer, ids, offsets=None, perm=None, inv=None, ws=N
     buf, nb = _ws(d, T, MOE_CALL_PERMUTE, ws)
     _check(lib().moe_permute(ctypes.byref(d.c), _ptr(ids), T, _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(buf), nb,
                              _stream(stream)), "moe_permute")
+    _keep(stream, buf, offsets, perm, inv)
     return offsets, perm, inv
 
 
@@ -243,6 +257,7 @@ def moe_experts_decode(layer: DeviceLayer, x, ids, y_pairs=None, y_shared=None, 
     _check(lib().moe_experts_decode(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(ids),
                                     _ptr(y_pairs), _ptr(y_shared), _ptr(buf), nb, _stream(stream)),
            "moe_experts_decode")
+    _keep(stream, buf, y_pairs, y_shared)
     return y_pairs, y_shared
 
 
@@ -264,6 +279,7 @@ def moe_experts_prefill(layer: DeviceLayer, x, offsets, perm, y_sorted=None, y_s
     _check(fn(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(offsets), _ptr(perm),
               _ptr(y_sorted), _ptr(y_shared), _ptr(buf), nb, _stream(stream)),
            "moe_experts_prefill_f16" if half else "moe_experts_prefill")
+    _keep(stream, buf, y_sorted, y_shared)
     return y_sorted, y_shared
 
 
@@ -273,6 +289,7 @@ def moe_combine(layer_or_desc, p, y_rows, row_of_pair=None, y_shared=None, out=N
     out = torch.empty((T, d.hidden), dtype=torch.float32, device=p.device) if out is None else out
     _check(lib().moe_combine(ctypes.byref(d.c), T, _ptr(p), _ptr(y_rows), _ptr(row_of_pair), _ptr(y_shared),
                              _ptr(out), _stream(stream)), "moe_combine")
+    _keep(stream, out)
     return out
 
 
@@ -283,6 +300,7 @@ def moe_layer(layer: DeviceLayer, x, out=None, logits=None, ids=None, p=None, ws
     buf, nb = _ws(d, T, MOE_CALL_LAYER, ws)
     _check(lib().moe_layer(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(out), _ptr(logits),
                            _ptr(ids), _ptr(p), _ptr(buf), nb, _stream(stream)), "moe_layer")
+    _keep(stream, buf, out)
     return out
 
 
@@ -295,6 +313,7 @@ def moe_kv_encode(src, codes=None, scales=None, stream=None):
     codes = torch.empty((rows, D), dtype=torch.int8, device=dev) if codes is None else codes
     scales = torch.empty((rows, D // 32), dtype=torch.int16, device=dev) if scales is None else scales
     _check(lib().moe_kv_encode(_ptr(bits), rows, D, _ptr(codes), _ptr(scales), _stream(stream)), "moe_kv_encode")
+    _keep(stream, codes, scales)
     return codes, scales
 
 
@@ -305,4 +324,5 @@ def moe_kv_gather(codes, scales, idx, out=None, stream=None):
     out = torch.empty((n_idx, D), dtype=torch.float32, device=codes.device) if out is None else out
     _check(lib().moe_kv_gather(_ptr(codes), _ptr(scales), n_rows, D, _ptr(idx), n_idx, _ptr(out), _stream(stream)),
            "moe_kv_gather")
+    _keep(stream, out)
     return out

@@ -101,6 +101,10 @@ PrefillWs carve_prefill_ws(const moe_layer_desc* d, int T, void* base, size_t* b
     return r;
 }
 
+// moe_layer's regime: the decode kernels for 1 <= T <= 4 when they fit the shape (their LDS holds
+// every chosen pair's activations), the grouped-GEMM path otherwise.
+bool layer_uses_decode(const moe_layer_desc* d, int T) { return T <= 4 && decode_fits(shape_view(d), T, true); }
+
 struct LayerWs {
     float* logits;
     int32_t* ids;
@@ -119,7 +123,7 @@ LayerWs carve_layer(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
     r.logits = c.take<float>((size_t)T * d->num_experts);
     r.ids = c.take<int32_t>(P);
     r.p = c.take<float>(P);
-    if (T <= 4) {
+    if (layer_uses_decode(d, T)) {
         r.h = c.take<float>(decode_scratch_floats(shape_view(d), T));
     } else {
         r.y_rows = c.take<_Float16>(P * d->hidden);
@@ -174,7 +178,7 @@ moe_status moe_workspace_size(const moe_layer_desc* d, int32_t T, moe_call call,
         case MOE_CALL_ROUTE: carve_route(d, T, nullptr, &b); break;
         case MOE_CALL_PERMUTE: carve_perm(d, T, nullptr, &b); break;
         case MOE_CALL_EXPERTS_DECODE:
-            if (T > 4) return MOE_ERR_UNSUPPORTED;
+            if (T > 4 || !decode_fits(shape_view(d), T, false)) return MOE_ERR_UNSUPPORTED;
             carve_decode(d, T, nullptr, &b);
             break;
         case MOE_CALL_EXPERTS_PREFILL:
@@ -228,7 +232,7 @@ moe_status moe_experts_decode(const moe_layer_desc* d, const moe_layer_weights* 
                               void* stream) {
     MOE_TRY(check_desc(d));
     MOE_TRY(check_T(T));
-    if (T > 4) return MOE_ERR_UNSUPPORTED;
+    if (T > 4 || !decode_fits(shape_view(d), T, false)) return MOE_ERR_UNSUPPORTED;
     MOE_TRY(check_expert_weights(d, w));
     if (!x || !aligned16(x) || !ids || !y_pairs || !aligned16(y_pairs)) return MOE_ERR_INVALID_ARG;
     if (d->shared_inter > 0 && (!y_shared || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;
@@ -251,7 +255,7 @@ moe_status moe_experts_prefill(const moe_layer_desc* d, const moe_layer_weights*
     size_t need = 0;
     carve_prefill_ws(d, T, nullptr, &need);
     MOE_TRY(check_ws(ws, ws_bytes, need));
-    return launch_prefill_experts(view(d, w), x, T, offsets, perm, y_sorted, y_shared, false,
+    return launch_prefill_experts(view(d, w), x, T, offsets, perm, y_sorted, y_shared, PrefillOut::kF32,
                                   carve_prefill_ws(d, T, ws, nullptr).scratch, (hipStream_t)stream);
 }
 
@@ -266,7 +270,7 @@ moe_status moe_experts_prefill_f16(const moe_layer_desc* d, const moe_layer_weig
     size_t need = 0;
     carve_prefill_ws(d, T, nullptr, &need);
     MOE_TRY(check_ws(ws, ws_bytes, need));
-    return launch_prefill_experts(view(d, w), x, T, offsets, perm, y_sorted, y_shared, true,
+    return launch_prefill_experts(view(d, w), x, T, offsets, perm, y_sorted, y_shared, PrefillOut::kF16,
                                   carve_prefill_ws(d, T, ws, nullptr).scratch, (hipStream_t)stream);
 }
 
@@ -316,17 +320,19 @@ moe_status moe_layer(const moe_layer_desc* d, const moe_layer_weights* w, const 
     float* pr = p ? p : lw.p;
     const LayerView L = view(d, w);
     hipStream_t s = (hipStream_t)stream;
-    if (T <= 4) {
+    if (layer_uses_decode(d, T)) {
         MOE_TRY(launch_route_gemv(w->w_router, w->router_bias, x, T, L.H, L.E, lg, s));
         return launch_decode_experts(L, x, T, lg, id, pr, lw.h, out, nullptr, nullptr, s);
     }
     // the expert outputs between the down GEMM and the combine are fp16 rows here (half the bytes
-    // of the largest stream); the combine sums them in fp32
+    // of the largest stream), at each token's activation scale; the combine sums and unscales them
+    // in fp32
     const _Float16* ysh = d->shared_inter > 0 ? lw.y_shared : nullptr;
     MOE_TRY(launch_route_topk(w->w_router, w->router_bias, x, T, L.H, L.E, L.k, lg, id, pr, lw.router_part, s));
     MOE_TRY(launch_permute(id, T, L.k, L.E, lw.offsets, lw.perm, lw.inv, lw.chunks, s));
-    MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, true, lw.prefill, s));
-    return launch_combine_f16(T, L.k, L.H, pr, lw.y_rows, lw.inv, ysh, out, s);
+    MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, PrefillOut::kF16Scaled,
+                                   lw.prefill, s));
+    return launch_combine_f16(T, L.k, L.H, pr, lw.y_rows, lw.inv, ysh, prefill_token_exps(L, T, lw.prefill), out, s);
 }
 
 }  // extern "C"

@@ -30,12 +30,15 @@ __device__ __forceinline__ void load8<_Float16>(const _Float16* row, int c, int 
 }
 
 // The k rows of a token are read four at a time with every load of a group in flight before any
-// is used (a dropped pair reads row 0 and adds nothing); the sum stays in slot order.
+// is used (a dropped pair reads row 0 and adds nothing); the sum stays in slot order. With texp,
+// the rows of token t are at the scale 2^(2 texp[t]) of its activations and the sum is multiplied
+// by 2^(-2 texp[t]) (exact in fp32).
 template <typename RT>
 __global__ __launch_bounds__(256) void k_combine(int T, int k, int H, const float* __restrict__ p,
                                                  const RT* __restrict__ y_rows,
                                                  const int32_t* __restrict__ row_of_pair,
-                                                 const RT* __restrict__ y_shared, float* __restrict__ out) {
+                                                 const RT* __restrict__ y_shared, const int32_t* __restrict__ texp,
+                                                 float* __restrict__ out) {
     const int t = blockIdx.y;
     const int c8 = blockIdx.x * blockDim.x + threadIdx.x;  // columns 4 c8 .. and H/2 + 4 c8 ..
     const int half = H / 2;
@@ -74,6 +77,11 @@ __global__ __launch_bounds__(256) void k_combine(int T, int k, int H, const floa
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += v[e];
     }
+    if (texp) {
+        const float sc = pow2f(-2 * texp[t]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= sc;
+    }
     reinterpret_cast<float4*>(out + (size_t)t * H)[c8] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     reinterpret_cast<float4*>(out + (size_t)t * H + half)[c8] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
@@ -82,16 +90,19 @@ moe_status launch_combine(int T, int k, int H, const float* p, const float* y_ro
                           const float* y_shared, float* out, hipStream_t s) {
     const int cols = H / 8;
     dim3 grid((cols + 255) / 256, T);
-    hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, s, T, k, H, p, y_rows, row_of_pair, y_shared, out);
+    hipLaunchKernelGGL(k_combine<float>, grid, dim3(256), 0, s, T, k, H, p, y_rows, row_of_pair, y_shared,
+                       (const int32_t*)nullptr, out);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
 
 moe_status launch_combine_f16(int T, int k, int H, const float* p, const _Float16* y_rows,
-                              const int32_t* row_of_pair, const _Float16* y_shared, float* out, hipStream_t s) {
+                              const int32_t* row_of_pair, const _Float16* y_shared, const int32_t* texp, float* out,
+                              hipStream_t s) {
     const int cols = H / 8;
     dim3 grid((cols + 255) / 256, T);
-    hipLaunchKernelGGL(k_combine<_Float16>, grid, dim3(256), 0, s, T, k, H, p, y_rows, row_of_pair, y_shared, out);
+    hipLaunchKernelGGL(k_combine<_Float16>, grid, dim3(256), 0, s, T, k, H, p, y_rows, row_of_pair, y_shared, texp,
+                       out);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -28,14 +28,62 @@ __device__ __forceinline__ uint32_t ordered_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ------------------------------------------------------------------------------------- activation range
+// The 16-bit operands (x and the SwiGLU activation h in fp16 on the dot-product and matrix-core
+// paths) are kept inside the fp16 range whatever the scale of a token: each token t gets an exact
+// power of two sigma_t = 2^e_t chosen from its largest |x| so that max |x_t| * sigma_t lies in
+// [2, 4), with e_t clamped to [-kExpClamp, kExpClamp] so that sigma_t^2 and its inverse are normal
+// fp32 numbers. x is staged as x * sigma_t; gate and up then come out as g * sigma_t and
+// u * sigma_t, the activation is kept as h * sigma_t^2 (silu(g) * u is bounded by |g| |u|, so it
+// scales like x^2 in both the small and the large regime), and the expert outputs, linear in h,
+// are multiplied by sigma_t^-2 in fp32. For activations of ordinary size (max |x| in [2, 4))
+// sigma_t = 1 and nothing changes.
+constexpr int kExpClamp = 60;
+
+// e_t from the largest |x| of the token given as bf16 magnitude bits (sign cleared): with the
+// biased exponent b of that value, 2^(b - 127) <= max < 2^(b - 126), and e = 128 - b puts the scaled
+// maximum in [2, 4). An all-zero (or subnormal-only) token takes the upper clamp.
+__host__ __device__ inline int token_exp_from_bits(uint32_t max_abs_bf16_bits) {
+    const int b = (int)((max_abs_bf16_bits >> 7) & 0xFFu);
+    int e = 128 - b;
+    e = e < -kExpClamp ? -kExpClamp : e;
+    e = e > kExpClamp ? kExpClamp : e;
+    return e;
+}
+
+// 2^e as an fp32 (e inside the normal range)
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
+// largest bf16 magnitude (bits, sign cleared) among the 8 values of a uint4
+__device__ __forceinline__ uint32_t bf16_absmax_bits(uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t m = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m = max(m, w[i] & 0x7FFFu);
+        m = max(m, (w[i] >> 16) & 0x7FFFu);
+    }
+    return m;
+}
+
+// Largest finite fp16; 16-bit activations and outputs saturate there instead of becoming inf.
+constexpr float kF16Max = 65504.0f;
+__device__ __forceinline__ float sat_f16(float v) { return __builtin_amdgcn_fmed3f(v, -kF16Max, kF16Max); }
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-// SiLU(g) * u from the hardware exp2 and reciprocal (each within about 1 ulp of fp32), for results
-// that are rounded to fp16 right away: g * u / (1 + 2^(-g log2 e)). Large negative g gives an
-// infinite exponential and a zero reciprocal, i.e. the limit 0.
-__device__ __forceinline__ float silu_mul_fast(float g, float u) {
-    const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
-    return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+// The SwiGLU activation of scaled accumulators: with gs = g * sigma and us = u * sigma (inv_sigma =
+// 1 / sigma), silu(g) * u * sigma^2 = gs * us / (1 + exp(-gs * inv_sigma)).
+__device__ __forceinline__ float silu_mul_scaled(float gs, float us, float inv_sigma) {
+    return gs * us / (1.0f + expf(-gs * inv_sigma));
+}
+
+// The same from the hardware exp2 and reciprocal (each within about 1 ulp of fp32), for results
+// that are rounded to fp16 right away. Large negative g gives an infinite exponential and a zero
+// reciprocal, i.e. the limit 0.
+__device__ __forceinline__ float silu_mul_scaled_fast(float gs, float us, float inv_sigma) {
+    const float e = __builtin_amdgcn_exp2f(gs * (inv_sigma * -1.4426950408889634f));
+    return gs * us * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // ------------------------------------------------------------------------------------- reductions

@@ -42,6 +42,7 @@ struct DecodePlan {
     uint32_t tokmask[64];    // slot -> bitmask of the tokens that chose it
     int pair_of[64][4];      // slot, token -> pair q = t*k + j, or -1
     float pw[64][4];         // slot, token -> routing probability of that pair (0 if none)
+    int xexp[4];             // token -> e_t of its activation scale 2^e_t (token_exp_from_bits)
 };
 
 // Built by one wave (lane q = pair q = t*k + j; T*k <= 64), LDS only, no block barrier: the caller
@@ -301,7 +302,7 @@ __device__ __forceinline__ void put_staged(_Float16* row, int nbm, int n, float 
     const int d = e / GS, r = e % GS;
     const int j = r % F::NP, half = r / F::NP;
     const int pidx = d * F::NP + j;
-    const float a = v * F::xs(j);
+    const float a = sat_f16(v) * F::xs(j);
     const _Float16 hi = (_Float16)a;
     const _Float16 lo = (_Float16)(a - (float)hi);
     row[((size_t)(pidx / 4) * nbm + b) * 8 + 2 * (pidx % 4) + half] = hi;
@@ -365,24 +366,23 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
     const int npairs = T * L.k;
 
     // x is staged by the waves after the first T (the top-k waves; without routing, after wave 0,
-    // which builds the plan), so that the staging runs beside the top-k and the plan rather than
-    // after them; a block too small for that stages with all its threads. Its chunks are loaded
-    // first (they do not depend on the routing).
+    // which builds the plan), one wave per token, so that the staging runs beside the top-k and the
+    // plan rather than after them; a block too small for that stages with all its waves after their
+    // other work. A token's largest |x| is one wave reduction; its scale 2^e_t (see common.h) is
+    // applied before the fp16 rounding. The first chunk of each staging wave's first token is loaded
+    // before the top-k (it does not depend on the routing).
     constexpr int kBusyWaves = ROUTE ? T : 1;
-    const int sb = (int)blockDim.x > kWave * kBusyWaves ? kWave * kBusyWaves : 0;
-    const int sn = (int)blockDim.x - sb;       // staging threads
-    const int sti = (int)threadIdx.x - sb;     // this thread's staging index (< 0: none)
-    constexpr int kMaxStage = 1;   // the first sn chunks are staged from registers, the rest in a loop
-    uint4 xraw[kMaxStage][4];
+    const int nwaves = (int)blockDim.x / kWave;
+    const bool spare = nwaves > kBusyWaves;
+    const int sw = spare ? wave - kBusyWaves : wave;   // staging wave index (< 0: none)
+    const int nsw = spare ? nwaves - kBusyWaves : nwaves;
+    auto load_chunk = [&](int t, int c, uint4 (&r)[4]) __attribute__((always_inline)) {
+        const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)t * H + (size_t)c * 32);
 #pragma unroll
-    for (int s = 0; s < kMaxStage; ++s) {
-        const int tb = sti + s * sn;
-        if (sti >= 0 && tb < T * nb) {
-            const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(tb / nb) * H + (size_t)(tb % nb) * 32);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) xraw[s][c] = xr[c];
-        }
-    }
+        for (int i = 0; i < 4; ++i) r[i] = xr[i];
+    };
+    uint4 xpre[4];
+    if (sw >= 0) load_chunk(min(sw, T - 1), min(lane, nb - 1), xpre);
     const int32_t* ids_src = ids;
     if constexpr (ROUTE) {
         // top-k of every token from the router logits (wave t: token t), recomputed by every block
@@ -402,26 +402,44 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
         ids_src = ids_s;
     }
 
-    // x staging
+    // x staging: max |x| of the token (chunks beyond the first 64 are read twice, from L2), then
+    // x * 2^e_t as fp16 pairs (and their offset sums)
+    for (int t = sw; sw >= 0 && t < T; t += nsw) {   // uniform per wave
+        uint4 keep[4];
+        if (t == sw) {
 #pragma unroll
-    for (int s = 0; s < kMaxStage; ++s) {
-        const int tb = sti + s * sn;
-        if (sti >= 0 && tb < T * nb) {
-            float v[32];
-            bf16x32_to_f32(xraw[s], v);
-            stage_pairs<FMT, 1>(v, xq + (size_t)(tb / nb) * 4 * nb + tb % nb, nb);
-            if constexpr (!kSubPairs) xc[tb] = stage_corr<FMT>(v);
+            for (int i = 0; i < 4; ++i) keep[i] = xpre[i];
+        } else {
+            load_chunk(t, min(lane, nb - 1), keep);
         }
-    }
-    for (int tb = sti + kMaxStage * sn; sti >= 0 && tb < T * nb; tb += sn) {
-        uint4 raw[4];
-        const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(tb / nb) * H + (size_t)(tb % nb) * 32);
+        uint32_t m = 0u;
+        if (lane < nb) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) raw[c] = xr[c];
-        float v[32];
-        bf16x32_to_f32(raw, v);
-        stage_pairs<FMT, 1>(v, xq + (size_t)(tb / nb) * 4 * nb + tb % nb, nb);
-        if constexpr (!kSubPairs) xc[tb] = stage_corr<FMT>(v);
+            for (int i = 0; i < 4; ++i) m = max(m, bf16_absmax_bits(keep[i]));
+        }
+        for (int c = lane + kWave; c < nb; c += kWave) {
+            uint4 r[4];
+            load_chunk(t, c, r);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = max(m, bf16_absmax_bits(r[i]));
+        }
+        const int e = token_exp_from_bits(wave_max_u32(m));
+        if (lane == 0) P.xexp[t] = e;
+        const float sc = pow2f(e);
+        auto stage = [&](const uint4 (&r)[4], int c) __attribute__((always_inline)) {
+            float v[32];
+            bf16x32_to_f32(r, v);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) v[i] *= sc;
+            stage_pairs<FMT, 1>(v, xq + (size_t)t * 4 * nb + c, nb);
+            if constexpr (!kSubPairs) xc[t * nb + c] = stage_corr<FMT>(v);
+        };
+        if (lane < nb) stage(keep, lane);
+        for (int c = lane + kWave; c < nb; c += kWave) {
+            uint4 r[4];
+            load_chunk(t, c, r);
+            stage(r, c);
+        }
     }
     // every token's choices in ids_s before the plan: with one token the wave that chose them is
     // the wave that builds the plan, so its own LDS writes only need to be complete
@@ -529,7 +547,7 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
                 if (lane == 0 && i < nv && ((mask >> t) & 1u)) {
                     const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
                     put_staged<FMT>(reinterpret_cast<_Float16*>(h + (size_t)row * Imax), Imax / 32, n0 + i,
-                                    silu_mul(gs_, us_));
+                                    silu_mul_scaled(gs_, us_, pow2f(-P.xexp[t])));
                 }
             }
     }
@@ -538,10 +556,11 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
 // ----------------------------------------------------------------------------------- K3 down
 
 // LDS of k_dec_down: plan | first[E] | ids/p [64] | hq[rows][8][nbm] uint4 (fp16 hi/lo pairs;
-// lanes reading consecutive 32-blocks hit consecutive banks) | partials [4][RPW][T][items]
-static size_t down_smem_bytes(int T, int k, int E, int Imax, int items_max, bool combine) {
+// lanes reading consecutive 32-blocks hit consecutive banks) | partials [waves][RPW][T][items_cap]
+// (per-pair outputs only)
+static size_t down_smem_bytes(int T, int k, int E, int Imax, int items_cap, bool combine) {
     size_t b = lds_head(E) + (size_t)(T * k + T) * (Imax / 32) * 128;
-    if (!combine) b += (size_t)kDownWaves * kDownRows * T * items_max * 4;
+    if (!combine) b += (size_t)kDownWaves * kDownRows * T * items_cap * 4;
     return b;
 }
 
@@ -549,11 +568,15 @@ static size_t down_smem_bytes(int T, int k, int E, int Imax, int items_max, bool
 // issues the loads of up to MAXJ items of every row before using any of them. The plan and h (fp16
 // hi + lo pairs, about 22 bits, already in the LDS layout) come from the gate/up kernel and are
 // copied into LDS first, so the dot products run on v_dot2_f32_f16 with fp32 accumulation.
+// Per-pair outputs (no combine) keep each item's partial sum in LDS until its slot is complete; the
+// slots are taken in chunks of spc (items_cap partials per wave, row and token), the shared
+// expert's blocks last, so that any shape fits: each chunk is reduced in block order before the
+// next one reuses the partials.
 template <int FMT, int T, bool COMBINE>
 __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const DecodePlan* __restrict__ plan_g,
                                                   const float* __restrict__ h, float* __restrict__ out,
                                                   float* __restrict__ y_pairs, float* __restrict__ y_shared,
-                                                  int items_max) {
+                                                  int items_cap, int spc) {
     constexpr int RPW = kDownRows, MAXJ = down_batch(T);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     DecodePlan& P = *reinterpret_cast<DecodePlan*>(smem);
@@ -594,11 +617,11 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
     const int H = L.H;
     const int nbI = L.I / 32, nbS = L.Is / 32;
     const int nU = P.nU;
-    const int items = nU * nbI + nbS;
-    const int nit = (items + kWave - 1) / kWave;
     const int64_t rbI = row_bytes(FMT, L.I), rbS = row_bytes(FMT, L.Is);
     const int m0 = (blockIdx.x * kDownWaves + wave) * RPW;
-    float* mypart = part + (size_t)wave * RPW * T * items_max;
+    float* mypart = part + (size_t)wave * RPW * T * items_cap;
+    const int nrc = COMBINE ? 1 : (nU + spc - 1) / spc;   // chunks of routed slots
+    const int nch = COMBINE ? 1 : nrc + (nbS > 0 ? 1 : 0);
 
     float acc[RPW][T];
 #pragma unroll
@@ -606,6 +629,13 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
 #pragma unroll
         for (int t = 0; t < T; ++t) acc[r][t] = 0.f;
 
+    bool h_in = false;   // h staged into LDS (by the first batch of loads; uniform over the block)
+    for (int ch = 0; ch < nch; ++ch) {
+        int it0, it1;    // items [it0, it1) of this chunk
+        if (COMBINE) { it0 = 0; it1 = nU * nbI + nbS; }
+        else if (ch < nrc) { it0 = ch * spc * nbI; it1 = min((ch + 1) * spc, nU) * nbI; }
+        else { it0 = nU * nbI; it1 = it0 + nbS; }
+        const int nit = (it1 - it0 + kWave - 1) / kWave;
     for (int j0 = 0; j0 < nit; j0 += MAXJ) {
         uint32_t w[RPW][MAXJ][8];
         uint16_t sdb[RPW][MAXJ];
@@ -617,8 +647,8 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
         // unused), so that every load below is unconditional and all of them stay in flight together
 #pragma unroll
         for (int jj = 0; jj < MAXJ; ++jj) {
-            const int it = lane + kWave * (j0 + jj);
-            const bool iv = it < items;
+            const int it = it0 + lane + kWave * (j0 + jj);
+            const bool iv = it < it1;
             int slot = 64, b = 0;
             if (iv) {
                 if (it < nU * nbI) { slot = it / nbI; b = it - slot * nbI; }
@@ -653,7 +683,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
 #pragma unroll
             for (int r = 0; r < RPW; ++r) load_codes<FMT>(dcp[r][jj], w[r][jj]);
         __builtin_amdgcn_sched_barrier(0);
-        if (j0 == 0) {
+        if (!h_in) {
             // h into LDS behind the first weight loads
             u32x4_t* hq4 = reinterpret_cast<u32x4_t*>(hq);
 #pragma unroll
@@ -663,11 +693,12 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
             }
             for (int i = (int)threadIdx.x + kDownThreads * kHBatch; i < n4; i += kDownThreads) hq[i] = hs[i];
             __syncthreads();
+            h_in = true;
         }
 #pragma unroll
         for (int jj = 0; jj < MAXJ; ++jj) {
             const int slot = slot_[jj], b = b_[jj];
-            const int it = lane + kWave * (j0 + jj);
+            const int it = it0 + lane + kWave * (j0 + jj);
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
                 if (!ok[r][jj]) continue;
@@ -694,10 +725,42 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
                         const float wgt = slot < 64 ? P.pw[slot][t] : 1.f;
                         acc[r][t] += wgt * sd * d;
                     } else {
-                        mypart[((size_t)r * T + t) * items_max + it] = sd * d;
+                        mypart[((size_t)r * T + t) * items_cap + (it - it0)] = sd * d;
                     }
                 }
             }
+        }
+    }
+        if constexpr (!COMBINE) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // lane -> (row, slot of the chunk, token): the slot's block partials summed in order
+            const bool routed = ch < nrc;
+            const int s0 = routed ? ch * spc : nU;
+            const int ns = routed ? min(spc, nU - s0) : 1;
+            for (int st = lane; st < RPW * ns * T; st += kWave) {
+                const int r = st / (ns * T), rem = st % (ns * T);
+                const int sl = rem / T, t = rem % T;
+                const int m = m0 + r;
+                if (m >= H) continue;
+                const float* pr = mypart + ((size_t)r * T + t) * items_cap;
+                const float sc = pow2f(-2 * P.xexp[t]);
+                if (routed) {
+                    const int q = P.pair_of[s0 + sl][t];
+                    if (q < 0) continue;
+                    float sum = 0.f;
+                    for (int b = 0; b < nbI; ++b) sum += pr[sl * nbI + b];
+                    y_pairs[(size_t)q * H + m] = sum * sc;
+                } else {
+                    float sum = 0.f;
+                    for (int b = 0; b < nbS; ++b) sum += pr[b];
+                    y_shared[(size_t)t * H + m] = sum * sc;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
 
@@ -707,31 +770,8 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 const float sm = wave_sum(acc[r][t]);
-                if (lane == 0 && m0 + r < H) out[(size_t)t * H + m0 + r] = sm;
+                if (lane == 0 && m0 + r < H) out[(size_t)t * H + m0 + r] = sm * pow2f(-2 * P.xexp[t]);
             }
-    } else {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // lane -> (row, slot, token): the slot's block partials summed in order
-        for (int st = lane; st < RPW * (nU + 1) * T; st += kWave) {
-            const int r = st / ((nU + 1) * T), rem = st % ((nU + 1) * T);
-            const int slot = rem / T, t = rem % T;
-            const int m = m0 + r;
-            if (m >= H) continue;
-            const float* pr = mypart + ((size_t)r * T + t) * items_max;
-            if (slot < nU) {
-                const int q = P.pair_of[slot][t];
-                if (q < 0) continue;
-                float sum = 0.f;
-                for (int b = 0; b < nbI; ++b) sum += pr[slot * nbI + b];
-                y_pairs[(size_t)q * H + m] = sum;
-            } else if (nbS > 0) {
-                float sum = 0.f;
-                for (int b = 0; b < nbS; ++b) sum += pr[nU * nbI + b];
-                y_shared[(size_t)t * H + m] = sum;
-            }
-        }
     }
 }
 
@@ -758,21 +798,50 @@ size_t decode_scratch_floats(const LayerView& L, int T) {
     return h_floats(L, T) + align_up(sizeof(DecodePlan), 256) / 4;
 }
 
-static int down_items_max(const LayerView& L, int T) {
+constexpr size_t kMaxLds = 160 * 1024;   // LDS of a gfx950 workgroup
+
+// LDS plan of the down kernel: for per-pair outputs, partials of items_cap items per wave, row and
+// token (all slots at once when they fit, else chunks of spc whole slots).
+struct DownFit {
+    bool ok;
+    int items_cap, spc;
+    size_t smem;
+};
+static DownFit down_fit(const LayerView& L, int T, bool combine) {
+    DownFit f{false, 0, 1, 0};
+    const size_t base = down_smem_bytes(T, L.k, L.E, L.Imax(), 0, true);
+    if (combine) {
+        f.smem = base;
+        f.ok = base <= kMaxLds;
+        return f;
+    }
+    const int nbI = L.I / 32, nbS = L.Is / 32;
     const int slots = min(T * L.k, L.E);
-    return slots * (L.I / 32) + L.Is / 32;
+    const int need = slots * nbI + nbS;               // every slot and the shared expert at once
+    const size_t per_item = (size_t)kDownWaves * kDownRows * T * 4;
+    const int avail = base < kMaxLds ? (int)((kMaxLds - base) / per_item) : 0;
+    if (avail >= need) {
+        f.items_cap = need;
+        f.spc = slots;
+        f.ok = true;
+    } else {
+        f.spc = avail / nbI;
+        f.items_cap = max(f.spc * nbI, nbS);
+        f.ok = f.spc >= 1 && f.items_cap <= avail;
+    }
+    f.smem = down_smem_bytes(T, L.k, L.E, L.Imax(), f.items_cap, false);
+    f.ok = f.ok && f.smem <= kMaxLds;
+    return f;
 }
 
-size_t decode_smem_bytes(const LayerView& L, int T, bool combine) {
-    const size_t a = gateup_smem_bytes(T, L.H, L.E);
-    const size_t b = down_smem_bytes(T, L.k, L.E, L.Imax(), down_items_max(L, T), combine);
-    return a > b ? a : b;
+bool decode_fits(const LayerView& L, int T, bool combine) {
+    return T >= 1 && T <= 4 && gateup_smem_bytes(T, L.H, L.E) <= kMaxLds && down_fit(L, T, combine).ok;
 }
 
-// Kernels asking for more than 64 KB of dynamic LDS must say so (gfx950 has 160 KB per CU).
+// Kernels asking for more than 64 KB of dynamic LDS must say so (gfx950 has 160 KB per workgroup).
 template <typename K>
 static bool allow_smem(K kernel, size_t bytes) {
-    if (bytes > 160 * 1024) return false;
+    if (bytes > kMaxLds) return false;
     if (bytes <= 65536) return true;
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)bytes) == hipSuccess;
@@ -815,6 +884,12 @@ template <int FMT, int T>
 static moe_status launch_experts_t(const LayerView& L, const uint16_t* x, const float* logits, int32_t* ids, float* p,
                                    float* h, float* out, float* y_pairs, float* y_shared, hipStream_t s) {
     DecodePlan* plan_g = reinterpret_cast<DecodePlan*>(h + h_floats(L, T));
+    // both kernels' LDS is settled before anything is enqueued
+    const bool combine = out != nullptr;
+    const DownFit fit = down_fit(L, T, combine);
+    if (!fit.ok) return MOE_ERR_UNSUPPORTED;
+    if (combine ? !allow_smem(k_dec_down<FMT, T, true>, fit.smem) : !allow_smem(k_dec_down<FMT, T, false>, fit.smem))
+        return MOE_ERR_UNSUPPORTED;
     moe_status st;
     if (!logits) st = launch_gateup<FMT, T, false, 1>(L, x, nullptr, ids, nullptr, h, plan_g, s);
     else if (L.E <= 64) st = launch_gateup<FMT, T, true, 1>(L, x, logits, ids, p, h, plan_g, s);
@@ -823,19 +898,13 @@ static moe_status launch_experts_t(const LayerView& L, const uint16_t* x, const 
     else if (L.E <= 512) st = launch_gateup<FMT, T, true, 8>(L, x, logits, ids, p, h, plan_g, s);
     else st = launch_gateup<FMT, T, true, 16>(L, x, logits, ids, p, h, plan_g, s);
     if (st != MOE_OK) return st;
-    const int items_max = down_items_max(L, T);
     const int blocks = (L.H + kDownWaves * kDownRows - 1) / (kDownWaves * kDownRows);
-    const bool combine = out != nullptr;
-    const size_t sm = down_smem_bytes(T, L.k, L.E, L.Imax(), items_max, combine);
-    if (combine) {
-        if (!allow_smem(k_dec_down<FMT, T, true>, sm)) return MOE_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL((k_dec_down<FMT, T, true>), dim3(blocks), dim3(kDownThreads), sm, s, L, plan_g, h, out, nullptr,
-                           nullptr, items_max);
-    } else {
-        if (!allow_smem(k_dec_down<FMT, T, false>, sm)) return MOE_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL((k_dec_down<FMT, T, false>), dim3(blocks), dim3(kDownThreads), sm, s, L, plan_g, h, nullptr,
-                           y_pairs, y_shared, items_max);
-    }
+    if (combine)
+        hipLaunchKernelGGL((k_dec_down<FMT, T, true>), dim3(blocks), dim3(kDownThreads), fit.smem, s, L, plan_g, h, out,
+                           nullptr, nullptr, 0, 1);
+    else
+        hipLaunchKernelGGL((k_dec_down<FMT, T, false>), dim3(blocks), dim3(kDownThreads), fit.smem, s, L, plan_g, h,
+                           nullptr, y_pairs, y_shared, fit.items_cap, fit.spc);
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }

@@ -39,7 +39,9 @@ moe_status launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
 moe_status launch_route_gemv(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
                              float* logits, hipStream_t s);
 size_t decode_scratch_floats(const LayerView& L, int T);
-size_t decode_smem_bytes(const LayerView& L, int T, bool combine);
+// Whether the decode kernels fit this shape (their LDS holds x, the routing plan and the SwiGLU
+// activations of every chosen pair): with the combine fused (combine) or with per-pair outputs.
+bool decode_fits(const LayerView& L, int T, bool combine);
 // logits != NULL: route inside (ids/p written); else ids given. out != NULL: combined output [T][H]
 // (p required); else y_pairs [T*k][H] and y_shared [T][H].
 moe_status launch_decode_experts(const LayerView& L, const uint16_t* x, int T, const float* logits, int32_t* ids,
@@ -47,15 +49,21 @@ moe_status launch_decode_experts(const LayerView& L, const uint16_t* x, int T, c
 
 // prefill experts
 size_t prefill_scratch_bytes(const LayerView& L, int T);
-// y_sorted / y_shared: fp32 rows, or fp16 rows when y16 (the fused layer's internal buffers).
+// Output rows: fp32 or fp16 at the true scale, or fp16 at each token's activation scale 2^(2 e_t)
+// (the fused layer's internal rows; its combine multiplies by 2^(-2 e_t)).
+enum class PrefillOut { kF32, kF16, kF16Scaled };
 moe_status launch_prefill_experts(const LayerView& L, const uint16_t* x, int T, const int32_t* offsets,
-                                  const int32_t* perm, void* y_sorted, void* y_shared, bool y16, void* scratch,
-                                  hipStream_t s);
+                                  const int32_t* perm, void* y_sorted, void* y_shared, PrefillOut mode,
+                                  void* scratch, hipStream_t s);
+// e_t of every token, in the scratch of the last launch_prefill_experts on it
+const int32_t* prefill_token_exps(const LayerView& L, int T, void* scratch);
 
 moe_status launch_combine(int T, int k, int H, const float* p, const float* y_rows, const int32_t* row_of_pair,
                           const float* y_shared, float* out, hipStream_t s);
+// fp16 rows at the scale 2^(2 e_t) of their token (texp[t] = e_t); the sum is unscaled in fp32
 moe_status launch_combine_f16(int T, int k, int H, const float* p, const _Float16* y_rows,
-                              const int32_t* row_of_pair, const _Float16* y_shared, float* out, hipStream_t s);
+                              const int32_t* row_of_pair, const _Float16* y_shared, const int32_t* texp, float* out,
+                              hipStream_t s);
 
 // KV cache codec
 moe_status launch_kv_encode(const uint16_t* src, int32_t rows, int32_t D, int8_t* codes, uint16_t* scales,

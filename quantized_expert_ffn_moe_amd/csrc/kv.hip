@@ -4,9 +4,10 @@
 // positions per query with an indexer (648news 07-nano-cuda-moe-qwen38-release, section "memory
 // hierarchy spanning VRAM and RAM"; cache sizes in 648news 10-cyber-on-strata-moe-local-inference,
 // section "KV transfer and next update"). Both kernels are HBM-bound streams:
-//   k_kv_encode  one thread per 32-value block: 64 bytes of bf16 in, max |v| in fp32,
-//                s = fp16(max / 127) saturating at 65504, codes rne(v / s) (fp32 division, correctly
-//                rounded) clamped to +-127, 32 bytes of codes and 2 bytes of scale out;
+//   k_kv_encode  one thread per 32-value block: 64 bytes of bf16 in, max |v| in fp32 (NaNs left
+//                out), s = fp16(max / 127) saturating at 65504, codes rne(v / s) (fp32 division,
+//                correctly rounded) clamped to +-127 (a NaN value: code 0), 32 bytes of codes and 2
+//                bytes of scale out;
 //   k_kv_gather  nb = D / 32 threads per output row, each taking 8 chunks of 4 values strided by
 //                nb chunks: all 8 code words and scales of a thread are in flight together, and
 //                at each of the 8 steps the row's threads read contiguous code bytes and write
@@ -32,9 +33,14 @@ __global__ __launch_bounds__(256) void k_kv_encode(const uint16_t* __restrict__ 
         v[2 * i] = bf16_lo(w[i]);
         v[2 * i + 1] = bf16_hi(w[i]);
     }
+    // block maximum by comparison, so that NaNs (quiet or signalling) never enter it: fmaxf follows
+    // IEEE maxNum, which returns NaN for a signalling NaN and would drop the earlier elements
     float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+    for (int i = 0; i < 32; ++i) {
+        const float a = fabsf(v[i]);
+        m = a > m ? a : m;
+    }
     _Float16 s16 = (_Float16)(m / 127.0f);
     if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;   // scale saturates at the largest finite fp16
     const float sf = (float)s16;
@@ -44,8 +50,10 @@ __global__ __launch_bounds__(256) void k_kv_encode(const uint16_t* __restrict__ 
         uint32_t packed = 0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            // a NaN value gets code 0 (it took no part in the block maximum either)
+            const float xv = v[4 * i + j];
             int c = 0;
-            if (sf != 0.f) c = (int)fminf(fmaxf(rintf(v[4 * i + j] / sf), -127.f), 127.f);
+            if (sf != 0.f && xv == xv) c = (int)fminf(fmaxf(rintf(xv / sf), -127.f), 127.f);
             packed |= ((uint32_t)c & 0xFFu) << (8 * j);
         }
         out[i] = packed;

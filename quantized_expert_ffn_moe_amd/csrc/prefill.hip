@@ -47,6 +47,7 @@ constexpr int kStages = 4;                 // A stages in LDS (a ring of four, l
 constexpr int kStageBytes = kTM * 128;     // one K step (64 fp16) of 128 rows
 constexpr int kHS = 128 + 8;               // fp16 per row of the staged h tile (padded)
 constexpr int kScaleBytes = 2 * kGW * 1024; // two groups of 4 K steps of scales, 1 KB per wave each
+constexpr int kRowExpBytes = kTM * 4;      // the exponent e of each row's activation scale
 constexpr int kXcds = 8;
 // Word 3 of a raw buffer descriptor (no stride, no swizzle) with the 32-bit data format; loads past
 // num_records bytes return zero.
@@ -158,43 +159,72 @@ __host__ __device__ inline int kperm(int e, int G) {
 }
 
 // -------------------------------------------------------------------------------- x to fp16
-// x (bf16) -> fp16, stored with the format's K permutation: VPT = 8 elements per thread when the
-// permutation groups hold at most 8 (one 16-byte load and store per thread, contiguous over a
-// wave), else 16.
+// x (bf16) -> fp16 times the token's power-of-two scale 2^e_t (e_t from its largest |x|, see
+// common.h; written to xexp[t]), stored with the format's K permutation. One wave per token:
+// lane l takes the 32-element chunks l, l + 64, ... of the row (a permutation group never crosses a
+// chunk), a wave maximum gives e_t, then each chunk goes out as four 16-byte stores; chunks past
+// the first 64 of a row are read twice (the second time from L2).
 // Block 0 builds the tile list instead (the two do not depend on each other; the first block is
 // dispatched first, so the longer tile build overlaps the conversion).
-template <int G, int VPT>
-__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, int64_t nv, _Float16* __restrict__ x16,
-                                                  const int32_t* __restrict__ offsets, int E, int T, int k,
-                                                  int has_shared, int tiles_max, TileDesc* __restrict__ tiles,
-                                                  int32_t* __restrict__ ntiles) {
-    static_assert(VPT % G == 0, "a thread holds whole permutation groups");
+constexpr int kXTokensPerBlock = 4;
+template <int G>
+__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, int T, int H, _Float16* __restrict__ x16,
+                                                  int32_t* __restrict__ xexp, const int32_t* __restrict__ offsets,
+                                                  int E, int k, int has_shared, int tiles_max,
+                                                  TileDesc* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+    static_assert(32 % G == 0, "a chunk holds whole permutation groups");
     if (blockIdx.x == 0) {
         build_tiles_block(offsets, E, T, k, has_shared, tiles_max, tiles, ntiles);
         return;
     }
-    const int64_t i = (int64_t)(blockIdx.x - 1) * 256 + threadIdx.x;
-    if (i >= nv) return;
-    const uint4* src = reinterpret_cast<const uint4*>(x) + (VPT / 8) * i;
-    uint32_t w[VPT / 2];
+    const int lane = threadIdx.x % kWave;
+    const int t = (int)(blockIdx.x - 1) * kXTokensPerBlock + (int)threadIdx.x / kWave;
+    if (t >= T) return;   // uniform per wave
+    const int nb = H / 32;
+    const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
+    auto load = [&](int c, u32x4 (&r)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int h = 0; h < VPT / 8; ++h) {
-        const uint4 a = src[h];
-        w[4 * h] = a.x; w[4 * h + 1] = a.y; w[4 * h + 2] = a.z; w[4 * h + 3] = a.w;
+        for (int i = 0; i < 4; ++i) r[i] = row[4 * c + i];
+    };
+    auto absmax = [&](const u32x4 (&r)[4]) __attribute__((always_inline)) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, bf16_absmax_bits(make_uint4(r[i].x, r[i].y, r[i].z, r[i].w)));
+        return m;
+    };
+    u32x4 keep[4];
+    load(min(lane, nb - 1), keep);
+    uint32_t m = lane < nb ? absmax(keep) : 0u;
+    for (int c = lane + kWave; c < nb; c += kWave) {
+        u32x4 r[4];
+        load(c, r);
+        m = max(m, absmax(r));
     }
-    _Float16 o[VPT];
+    const int e = token_exp_from_bits(wave_max_u32(m));
+    if (lane == 0) xexp[t] = e;
+    const float sc = pow2f(e);
+    half8* dst = reinterpret_cast<half8*>(x16 + (size_t)t * H);
+    auto convert = [&](const u32x4 (&r)[4], int c) __attribute__((always_inline)) {
+        _Float16 o[32];
 #pragma unroll
-    for (int e = 0; e < VPT; ++e) {
-        const float v = (e & 1) ? bf16_hi(w[e / 2]) : bf16_lo(w[e / 2]);
-        o[kperm(e, G)] = (_Float16)v;
-    }
-    half8* dst = reinterpret_cast<half8*>(x16) + (VPT / 8) * i;
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t w = r[i / 4][i % 4];
+            o[kperm(2 * i, G)] = (_Float16)(bf16_lo(w) * sc);
+            o[kperm(2 * i + 1, G)] = (_Float16)(bf16_hi(w) * sc);
+        }
 #pragma unroll
-    for (int h = 0; h < VPT / 8; ++h) {
-        half8 v;
+        for (int h = 0; h < 4; ++h) {
+            half8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = o[8 * h + e];
-        dst[h] = v;
+            for (int q = 0; q < 8; ++q) v[q] = o[8 * h + q];
+            dst[4 * c + h] = v;
+        }
+    };
+    if (lane < nb) convert(keep, lane);
+    for (int c = lane + kWave; c < nb; c += kWave) {
+        u32x4 r[4];
+        load(c, r);
+        convert(r, c);
     }
 }
 
@@ -336,10 +366,16 @@ template <int VM> __device__ __forceinline__ void step_barrier() {
 
 // One tile of 32 * NI rows against the block's 256 weight rows (gate/up: 128 h columns). SD: the
 // scales come as groups of four K steps straight into LDS (the scale rows are 16-byte aligned).
-template <int FMT, bool GATEUP, typename YT, int NI, bool SD>
+// Activation scales (common.h): every A row carries the exponent e of its token's scale 2^e, read
+// from rexp (gate/up: by token; down: by h row, as the gate/up epilogue wrote it to hexp). Gate/up
+// turns the scaled accumulators into h * 2^(2e); down multiplies its outputs by 2^(-2e) when UNSC
+// (fp32 rows, and the fp16 rows of moe_experts_prefill_f16), else leaves them at that scale (the
+// fused layer's internal fp16 rows, unscaled by its combine). fp16 values saturate at +-65504.
+template <int FMT, bool GATEUP, typename YT, int NI, bool SD, bool UNSC>
 __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileDesc& td, int ntile,
                                           const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-                                          const _Float16* __restrict__ asrc, _Float16* __restrict__ h16,
+                                          const _Float16* __restrict__ asrc, const int32_t* __restrict__ rexp,
+                                          _Float16* __restrict__ h16, int32_t* __restrict__ hexp,
                                           YT* __restrict__ y_sorted, YT* __restrict__ y_shared, uint8_t* smem) {
     constexpr int G = perm_group<FMT>();
     constexpr int BB = FMT == MOE_Q8_B32 ? 32 : FMT == MOE_Q4_B32 ? 16 : 8;   // bytes per block
@@ -375,8 +411,13 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     // c ^ ((r >> 1) & 7). Wave load u fills rows 8 q .. 8 q + 7 (q = wave + 4 u); lane l writes
     // slot l % 8 of row 8 q + l / 8, so it fetches the chunk that belongs there. Rows past the
     // tile are clamped to a valid row: they only feed output rows that are never stored.
+    // The exponents of the rows' activation scales are loaded here and written to LDS (row r at
+    // rexp_s[r]) after the prologue's wait, which they precede in the load order.
+    constexpr bool kRowExp = GATEUP || UNSC;
+    int* rexp_s = reinterpret_cast<int*>(smem + kStages * kStageBytes + kScaleBytes);
     const _Float16* arow[QW];
     int ach[QW];
+    int rexp_v[QW];
 #pragma unroll
     for (int u = 0; u < QW; ++u) {
         const int q = wave + kGW * u;
@@ -387,9 +428,11 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
             const int qq = shared ? pos * L.k : perm[base + pos];
             const int tok = (unsigned)qq < (unsigned)Tk ? qq / L.k : 0;
             arow[u] = asrc + (size_t)tok * H;
+            rexp_v[u] = rexp[tok];
         } else {
             const int64_t hrow = shared ? (int64_t)Tk + pos : (int64_t)base + pos;
             arow[u] = asrc + (size_t)hrow * Imax;
+            if constexpr (kRowExp) rexp_v[u] = rexp[hrow];
         }
     }
     // fragment of lane (frow, g) for K sub-step kk: row 32 i + frow, chunk 4 g + kk
@@ -467,18 +510,25 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     // A chunk past K (the second half of the last step when K % 64 == 32) reloads the row's last
     // chunk instead (its weights are zero, see below).
     auto issue = [&](BSlot (&sl)[2], int t, int stage, auto group_start) __attribute__((always_inline)) {
+        // A step past the end issues no direct-to-LDS load at all: the stages and the scale buffers
+        // are reused by the epilogue, and a transfer still landing there after the final wait would
+        // overwrite the staged outputs (such late writes were observed). Its register loads still go
+        // out (clamped, unused); the waits of the last steps cover everything.
+        const bool live = t < nsteps;
         t = min(t, nsteps - 1);
         uint8_t* st = smem + stage * kStageBytes + wave * 1024;
+        if (live) {
 #pragma unroll
-        for (int u = 0; u < QW; ++u)
-            __builtin_amdgcn_global_load_lds(abase[u] + min(128 * t + 2 * ach[u], klim), (lds_void*)(st + u * kGW * 1024),
-                                             16, 0, 0);
-        // the scales of steps t .. t + 3 (blocks 2 t .. 2 t + 7), issued by the steps that start a group
-        // of four (known at compile time; a clamped step past the end rewrites the last group with the
-        // same bytes)
-        if constexpr (SD && decltype(group_start)::value)
-            __builtin_amdgcn_global_load_lds(sgsrc + 4 * (t & ~3), (lds_void*)(sbuf + ((t >> 2) & 1) * (kGW * 1024) + wave * 1024),
-                                             16, 0, 0);
+            for (int u = 0; u < QW; ++u)
+                __builtin_amdgcn_global_load_lds(abase[u] + min(128 * t + 2 * ach[u], klim),
+                                                 (lds_void*)(st + u * kGW * 1024), 16, 0, 0);
+            // the scales of steps t .. t + 3 (blocks 2 t .. 2 t + 7), issued by the steps that start a
+            // group of four (known at compile time)
+            if constexpr (SD && decltype(group_start)::value)
+                __builtin_amdgcn_global_load_lds(sgsrc + 4 * (t & ~3),
+                                                 (lds_void*)(sbuf + ((t >> 2) & 1) * (kGW * 1024) + wave * 1024), 16,
+                                                 0, 0);
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int cofs = 2 * t * BB, sofs = 4 * t;
@@ -575,7 +625,10 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
                 frag(st, std::integral_constant<int, kk + 1>{}, nxt_a);
                 deq(cur, std::integral_constant<int, kk + 1>{}, svc0, svc1, nxt_b);
             } else {
-                step_barrier<2 * BATCH + kInFlightGroups>();
+                // the counted wait holds while steps s + 2 and s + 3 exist; near the end fewer loads
+                // are in flight, so everything is waited for
+                if (s + 3 < nsteps) step_barrier<2 * BATCH + kInFlightGroups>();
+                else step_barrier<0>();
                 issue(slot(sc), s + 4, SL, std::integral_constant<bool, kIssueGroup>{});
                 scales(s + 1, nxt, svn0, svn1);
                 frag(stn, std::integral_constant<int, 0>{}, nxt_a);
@@ -606,7 +659,14 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     issue(slot1, 1, 1, std::integral_constant<bool, false>{});
     issue(slot2, 2, 2, std::integral_constant<bool, false>{});
     issue(slot3, 3, 3, std::integral_constant<bool, false>{});
-    step_barrier<3 * BATCH>();
+    if (nsteps >= 4) step_barrier<3 * BATCH>();
+    else step_barrier<0>();
+    if constexpr (kRowExp) {
+        if ((lane & 7) == 0) {
+#pragma unroll
+            for (int u = 0; u < QW; ++u) rexp_s[8 * (wave + kGW * u) + lane / 8] = rexp_v[u];
+        }
+    }
     scales(0, slot0, svc0, svc1);
     frag(smem, std::integral_constant<int, 0>{}, fa);
     deq(slot0, std::integral_constant<int, 0>{}, svc0, svc1, ba);
@@ -632,10 +692,24 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
-                hs[row * kHS + pc] = (_Float16)silu_mul_fast(acc[i][0][r], acc[i][1][r]);
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int4 ev = *reinterpret_cast<const int4*>(rexp_s + 32 * i + 8 * r4 + rq);
+                const int ee[4] = {ev.x, ev.y, ev.z, ev.w};
+#pragma unroll
+                for (int r1 = 0; r1 < 4; ++r1) {
+                    const int r = 4 * r4 + r1;
+                    const int row = 32 * i + 8 * r4 + rq + r1;
+                    hs[row * kHS + pc] =
+                        (_Float16)sat_f16(silu_mul_scaled_fast(acc[i][0][r], acc[i][1][r], pow2f(-ee[r1])));
+                }
             }
+        // the h rows' exponents for the down GEMM (written once, by the first column tile)
+        if (ntile == 0) {
+            for (int row = tid; row < nrows; row += kGT) {
+                const int64_t hrow = shared ? (int64_t)Tk + td.row0 + row : (int64_t)base + td.row0 + row;
+                hexp[hrow] = rexp_s[row];
+            }
+        }
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < 2 * NI; ++it) {
@@ -660,9 +734,18 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
 #pragma unroll
             for (int i = 0; i < NI; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
-                    ys[row * kHS + 32 * wave + frow] = (_Float16)acc[i][j][r];
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    int ee[4] = {0, 0, 0, 0};
+                    if constexpr (UNSC) {
+                        const int4 ev = *reinterpret_cast<const int4*>(rexp_s + 32 * i + 8 * r4 + rq);
+                        ee[0] = ev.x; ee[1] = ev.y; ee[2] = ev.z; ee[3] = ev.w;
+                    }
+#pragma unroll
+                    for (int r1 = 0; r1 < 4; ++r1) {
+                        const int row = 32 * i + 8 * r4 + rq + r1;
+                        const float v = acc[i][j][4 * r4 + r1];
+                        ys[row * kHS + 32 * wave + frow] = (_Float16)sat_f16(UNSC ? v * pow2f(-2 * ee[r1]) : v);
+                    }
                 }
             __syncthreads();
 #pragma unroll
@@ -684,25 +767,34 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
 #pragma unroll
             for (int i = 0; i < NI; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * i + 8 * (r / 4) + rq + r % 4;
-                    if (row >= nrows) continue;
-                    if (shared) y_shared[(int64_t)(td.row0 + row) * H + m] = (YT)acc[i][j][r];
-                    else y_sorted[((int64_t)base + td.row0 + row) * H + m] = (YT)acc[i][j][r];
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int4 ev = *reinterpret_cast<const int4*>(rexp_s + 32 * i + 8 * r4 + rq);
+                    const int ee[4] = {ev.x, ev.y, ev.z, ev.w};
+#pragma unroll
+                    for (int r1 = 0; r1 < 4; ++r1) {
+                        const int row = 32 * i + 8 * r4 + rq + r1;
+                        if (row >= nrows) continue;
+                        const float v = acc[i][j][4 * r4 + r1] * pow2f(-2 * ee[r1]);
+                        if (shared) y_shared[(int64_t)(td.row0 + row) * H + m] = (YT)v;
+                        else y_sorted[((int64_t)base + td.row0 + row) * H + m] = (YT)v;
+                    }
                 }
         }
     }
 }
 
-// YT: type of the down outputs (float, or _Float16 for the fused layer's internal rows).
-template <int FMT, bool GATEUP, typename YT = float>
+// YT: type of the down outputs (float, or _Float16); UNSC: down outputs at the true scale (see
+// gemm_tile).
+template <int FMT, bool GATEUP, typename YT = float, bool UNSC = true>
 __global__ __launch_bounds__(kGT, 2) void k_grouped_gemm(LayerView L, int T, const TileDesc* __restrict__ tiles,
                                                          const int32_t* __restrict__ ntiles, int n_ntile,
                                                          const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ perm,
-                                                         const _Float16* __restrict__ asrc, _Float16* __restrict__ h16,
-                                                         YT* __restrict__ y_sorted, YT* __restrict__ y_shared) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes + kScaleBytes];
+                                                         const _Float16* __restrict__ asrc,
+                                                         const int32_t* __restrict__ rexp, _Float16* __restrict__ h16,
+                                                         int32_t* __restrict__ hexp, YT* __restrict__ y_sorted,
+                                                         YT* __restrict__ y_shared) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes + kScaleBytes + kRowExpBytes];
     // XCD-aware work index: block b runs on XCD b % 8, and consecutive work items go to the same
     // XCD. Work items are ordered tile-major: the weight-row tiles of one row tile (same A rows)
     // run side by side, and so do the row tiles of one expert (same weights). The grid is sized for
@@ -720,8 +812,9 @@ __global__ __launch_bounds__(kGT, 2) void k_grouped_gemm(LayerView L, int T, con
     // scale rows are 16-byte aligned when the scale count per row is a multiple of 8
     const int K = GATEUP ? L.H : (td.group == L.E ? L.Is : L.I);
     const bool sd = (K / 32) % 8 == 0;
-#define MOE_GEMM_TILE(NI_, SD_) \
-    gemm_tile<FMT, GATEUP, YT, NI_, SD_>(L, T, td, ntile, offsets, perm, asrc, h16, y_sorted, y_shared, smem)
+#define MOE_GEMM_TILE(NI_, SD_)                                                                              \
+    gemm_tile<FMT, GATEUP, YT, NI_, SD_, UNSC>(L, T, td, ntile, offsets, perm, asrc, rexp, h16, hexp, y_sorted, \
+                                               y_shared, smem)
     switch (td.ni) {
         case 4: if (sd) MOE_GEMM_TILE(4, true); else MOE_GEMM_TILE(4, false); break;
         case 2: if (sd) MOE_GEMM_TILE(2, true); else MOE_GEMM_TILE(2, false); break;
@@ -737,6 +830,8 @@ struct PrefillScratch {
     int32_t* ntiles;
     _Float16* x16;
     _Float16* h16;
+    int32_t* xexp;   // [T]: e of each token's activation scale
+    int32_t* hexp;   // [T*k + T]: e of each h row's token
 };
 
 static PrefillScratch carve_prefill(const LayerView& L, int T, void* base, size_t* bytes) {
@@ -746,6 +841,8 @@ static PrefillScratch carve_prefill(const LayerView& L, int T, void* base, size_
     s.ntiles = c.take<int32_t>(1);
     s.x16 = c.take<_Float16>((size_t)T * L.H);
     s.h16 = c.take<_Float16>((size_t)(T * L.k + T) * L.Imax());
+    s.xexp = c.take<int32_t>((size_t)T);
+    s.hexp = c.take<int32_t>((size_t)T * L.k + T);
     if (bytes) *bytes = c.bytes();
     return s;
 }
@@ -756,44 +853,56 @@ size_t prefill_scratch_bytes(const LayerView& L, int T) {
     return b;
 }
 
+const int32_t* prefill_token_exps(const LayerView& L, int T, void* scratch) {
+    return carve_prefill(L, T, scratch, nullptr).xexp;
+}
+
 template <int FMT>
 static moe_status launch_prefill_f(const LayerView& L, const uint16_t* x, int T, const int32_t* offsets,
-                                   const int32_t* perm, void* y_sorted, void* y_shared, bool y16,
+                                   const int32_t* perm, void* y_sorted, void* y_shared, PrefillOut mode,
                                    const PrefillScratch& s, hipStream_t st) {
     constexpr int G = perm_group<FMT>();
-    constexpr int VPT = G <= 8 ? 8 : 16;
-    const int64_t nv = (int64_t)T * L.H / VPT;
-    hipLaunchKernelGGL((k_x_to_f16<G, VPT>), dim3((unsigned)((nv + 255) / 256 + 1)), dim3(kTileThreads), 0, st, x, nv,
-                       s.x16, offsets, L.E, T, L.k, L.Is > 0 ? 1 : 0, max_tiles(T, L.k, L.E), s.tiles, s.ntiles);
+    const int xblocks = (T + kXTokensPerBlock - 1) / kXTokensPerBlock;
+    hipLaunchKernelGGL((k_x_to_f16<G>), dim3((unsigned)(xblocks + 1)), dim3(kTileThreads), 0, st, x, T, L.H, s.x16,
+                       s.xexp, offsets, L.E, L.k, L.Is > 0 ? 1 : 0, max_tiles(T, L.k, L.E), s.tiles, s.ntiles);
     MOE_LAUNCH_CHECK();
     const int mt = max_tiles(T, L.k, L.E);
     const int nt1 = (L.Imax() + 127) / 128;
     const int g1 = ((mt * nt1 + kXcds - 1) / kXcds) * kXcds;
     hipLaunchKernelGGL((k_grouped_gemm<FMT, true>), dim3(g1), dim3(kGT), 0, st, L, T, s.tiles, s.ntiles, nt1,
-                       offsets, perm, s.x16, s.h16, (float*)nullptr, (float*)nullptr);
+                       offsets, perm, s.x16, s.xexp, s.h16, s.hexp, (float*)nullptr, (float*)nullptr);
     MOE_LAUNCH_CHECK();
     const int nt2 = (L.H + 255) / 256;
     const int g2 = ((mt * nt2 + kXcds - 1) / kXcds) * kXcds;
-    if (y16)
-        hipLaunchKernelGGL((k_grouped_gemm<FMT, false, _Float16>), dim3(g2), dim3(kGT), 0, st, L, T, s.tiles,
-                           s.ntiles, nt2, offsets, perm, s.h16, nullptr, static_cast<_Float16*>(y_sorted),
-                           static_cast<_Float16*>(y_shared));
-    else
-        hipLaunchKernelGGL((k_grouped_gemm<FMT, false, float>), dim3(g2), dim3(kGT), 0, st, L, T, s.tiles,
-                           s.ntiles, nt2, offsets, perm, s.h16, nullptr, static_cast<float*>(y_sorted),
-                           static_cast<float*>(y_shared));
+    switch (mode) {
+        case PrefillOut::kF16Scaled:
+            hipLaunchKernelGGL((k_grouped_gemm<FMT, false, _Float16, false>), dim3(g2), dim3(kGT), 0, st, L, T,
+                               s.tiles, s.ntiles, nt2, offsets, perm, s.h16, s.hexp, nullptr, nullptr,
+                               static_cast<_Float16*>(y_sorted), static_cast<_Float16*>(y_shared));
+            break;
+        case PrefillOut::kF16:
+            hipLaunchKernelGGL((k_grouped_gemm<FMT, false, _Float16, true>), dim3(g2), dim3(kGT), 0, st, L, T,
+                               s.tiles, s.ntiles, nt2, offsets, perm, s.h16, s.hexp, nullptr, nullptr,
+                               static_cast<_Float16*>(y_sorted), static_cast<_Float16*>(y_shared));
+            break;
+        default:
+            hipLaunchKernelGGL((k_grouped_gemm<FMT, false, float, true>), dim3(g2), dim3(kGT), 0, st, L, T,
+                               s.tiles, s.ntiles, nt2, offsets, perm, s.h16, s.hexp, nullptr, nullptr,
+                               static_cast<float*>(y_sorted), static_cast<float*>(y_shared));
+            break;
+    }
     MOE_LAUNCH_CHECK();
     return MOE_OK;
 }
 
 moe_status launch_prefill_experts(const LayerView& L, const uint16_t* x, int T, const int32_t* offsets,
-                                  const int32_t* perm, void* y_sorted, void* y_shared, bool y16, void* scratch,
+                                  const int32_t* perm, void* y_sorted, void* y_shared, PrefillOut mode, void* scratch,
                                   hipStream_t st) {
     const PrefillScratch s = carve_prefill(L, T, scratch, nullptr);
     switch (L.fmt) {
-        case MOE_Q8_B32: return launch_prefill_f<MOE_Q8_B32>(L, x, T, offsets, perm, y_sorted, y_shared, y16, s, st);
-        case MOE_Q4_B32: return launch_prefill_f<MOE_Q4_B32>(L, x, T, offsets, perm, y_sorted, y_shared, y16, s, st);
-        case MOE_Q2_B32: return launch_prefill_f<MOE_Q2_B32>(L, x, T, offsets, perm, y_sorted, y_shared, y16, s, st);
+        case MOE_Q8_B32: return launch_prefill_f<MOE_Q8_B32>(L, x, T, offsets, perm, y_sorted, y_shared, mode, s, st);
+        case MOE_Q4_B32: return launch_prefill_f<MOE_Q4_B32>(L, x, T, offsets, perm, y_sorted, y_shared, mode, s, st);
+        case MOE_Q2_B32: return launch_prefill_f<MOE_Q2_B32>(L, x, T, offsets, perm, y_sorted, y_shared, mode, s, st);
         default: return MOE_ERR_INVALID_ARG;
     }
 }

@@ -189,9 +189,10 @@ CONFIGS = {
 }
 
 
-def make_x(spec: LayerSpec, layer: int = 0, seed: int = 0, T: int | None = None) -> np.ndarray:
+def make_x(spec: LayerSpec, layer: int = 0, seed: int = 0, T: int | None = None, sigma: float = 1.0) -> np.ndarray:
+    """bf16 activations [T][H], N(0, sigma^2) (sigma = 1 for every named workload)."""
     T = spec.T if T is None else T
-    return normal_bf16(key(seed, spec.cfg_id, layer, T_X), T * spec.H).reshape(T, spec.H)
+    return normal_bf16(key(seed, spec.cfg_id, layer, T_X), T * spec.H, sigma).reshape(T, spec.H)
 
 
 def make_router(spec: LayerSpec, layer: int = 0, seed: int = 0):

@@ -110,6 +110,30 @@ def test_host_validation_rejects_before_launch():
                 None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_decode_lds_limit_settled_before_launch():
+    """The decode kernels keep every chosen pair's SwiGLU activations in LDS (160 KB per workgroup).
+    A shape beyond that makes moe_experts_decode return MOE_ERR_UNSUPPORTED from the host check,
+    before anything is enqueued (fake device addresses, no GPU here: a launch would fail
+    differently), moe_workspace_size says the same, and moe_layer sizes its workspace for the
+    grouped-GEMM path it then takes."""
+    big = D(H=1024, I=1536, E=64, k=8, Is=0)            # 36 pairs x 1536 activations x 4 B = 221 KB
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_workspace_size(big, 4, moe.MOE_CALL_EXPERTS_DECODE)
+    assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+    fake = 0x10000
+    w = moe._Weights(fake, None, moe._QMat(fake, fake), moe._QMat(fake, fake), moe._QMat(fake, fake),
+                     moe._QMat(None, None), moe._QMat(None, None), moe._QMat(None, None))
+    assert _raw("moe_experts_decode", ctypes.byref(big.c), ctypes.byref(w), fake, 4, fake, fake, None, fake,
+                1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    # the layer's workspace holds the grouped-GEMM path's fp16 expert rows for this shape
+    assert moe.moe_workspace_size(big, 4, moe.MOE_CALL_LAYER) >= 4 * 8 * 1024 * 2
+    # one token fits the decode kernels; the 512-expert top-10 2-bit shape fits at T = 4 too (the
+    # per-pair partial sums are then reduced in chunks of slots)
+    assert moe.moe_workspace_size(big, 1, moe.MOE_CALL_EXPERTS_DECODE) > 0
+    s48 = D(H=2048, I=768, E=512, k=10, Is=0, fmt=moe.MOE_Q2_B32)
+    assert moe.moe_workspace_size(s48, 4, moe.MOE_CALL_EXPERTS_DECODE) > 0
+
+
 def test_kv_validation_rejects_before_launch():
     fake = 0x10000
     assert _raw("moe_kv_encode", fake, 4, 48, fake, fake, None) == moe.MOE_ERR_INVALID_ARG        # D % 32

@@ -131,6 +131,47 @@ def test_stack48_layer(layer):
     assert_float_match(Y, ref["Y"], "Y")
 
 
+def test_layer_decode_lds_fallback():
+    """T = 4, k = 8, I = 1536: the 36 pairs' activations (221 KB) exceed the decode kernels' LDS, so
+    moe_layer takes the grouped-GEMM path; it still meets the rule against the oracle, and
+    moe_experts_decode refuses the shape before enqueueing anything."""
+    _need_gpu()
+    spec = synth.LayerSpec("ldsfb", T=4, H=1024, E=64, k=8, I=1536, Is=0, fmt=synth.Q4, zipf=True, cfg_id=97)
+    d = synth.make_layer(spec)
+    say("decode LDS fallback T=4 k=8 I=1536")
+    O = orc_layer(spec, d)
+    g_logits, g_ids, g_p, Y = run_layer(spec, d)
+    check_routing(O, d["x"], g_logits, g_ids, g_p)
+    ref = oracle_tokens(O, d["x"], g_logits, range(spec.T))
+    assert_float_match(Y, ref["Y"], "Y")
+    L = dev_layer(spec, d)
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_experts_decode(L, dev_x(d["x"]), torch.from_numpy(g_ids).cuda())
+    assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_experts_decode_stack48_four_tokens():
+    """moe_experts_decode on a full-size stack48 layer (512 experts, top-10, 2-bit) with 4 tokens:
+    the per-pair partial sums are reduced in chunks of slots to fit the LDS."""
+    _need_gpu()
+    spec, d = host_layer("stack48", 0)
+    x = synth.make_x(spec, layer=0, seed=5, T=4)
+    say("stack48 moe_experts_decode T=4")
+    O = orc_layer(spec, d)
+    L = dev_layer(spec, d)
+    xd = dev_x(x)
+    logits = torch.empty((4, spec.E), dtype=torch.float32, device="cuda")
+    _, ids, p = moe.moe_route(L, xd, logits=logits)
+    y_pairs, _ = moe.moe_experts_decode(L, xd, ids)
+    Y = moe.moe_layer(L, xd)
+    torch.cuda.synchronize()
+    g_logits = logits.cpu().numpy()
+    check_routing(O, x, g_logits, ids.cpu().numpy(), p.cpu().numpy())
+    ref = oracle_tokens(O, x, g_logits, range(4))
+    assert_float_match(y_pairs.cpu().numpy().reshape(4, spec.k, spec.H), ref["y_pairs"], "y_pairs")
+    assert_float_match(Y.cpu().numpy(), ref["Y"], "Y")
+
+
 def test_golden_examples_on_gpu():
     """The hand-computed worked examples through moe_layer (T = 1, decode path)."""
     _need_gpu()
@@ -484,6 +525,34 @@ def test_determinism():
         assert np.array_equal(u, v)
 
 
+@pytest.mark.parametrize("T,H,E,k,I,Is", [(4, 1024, 64, 8, 1536, 0), (64, 2048, 256, 8, 512, 512),
+                                          (5, 256, 16, 4, 128, 64)])
+def test_prefill_repeat_bitwise(T, H, E, k, I, Is):
+    """Repeated grouped-GEMM calls on identical inputs give identical bits (fp32 entry and fused
+    layer). Guards the end of each tile's K loop: no transfer into LDS may still be in flight when
+    the epilogue reuses the stages (small T, few tiles, short K loops expose any such race)."""
+    _need_gpu()
+    spec = synth.LayerSpec("rep", T=T, H=H, E=E, k=k, I=I, Is=Is, fmt=synth.Q4, zipf=True, cfg_id=98)
+    d = synth.make_layer(spec)
+    say("prefill repeat T=%d H=%d I=%d" % (T, H, I))
+    L = dev_layer(spec, d)
+    xd = dev_x(d["x"])
+    _, ids, p = moe.moe_route(L, xd)
+    off, perm, inv = moe.moe_permute(L, ids)
+    first_y = first_Y = None
+    for rep in range(6):
+        ws = torch.full((moe.moe_workspace_size(L.desc, T, moe.MOE_CALL_EXPERTS_PREFILL),), rep * 37 % 256,
+                        dtype=torch.uint8, device="cuda")
+        y, _ = moe.moe_experts_prefill(L, xd, off, perm, ws=ws)
+        Y = moe.moe_layer(L, xd)
+        torch.cuda.synchronize()
+        if first_y is None:
+            first_y, first_Y = y.clone(), Y.clone()
+        else:
+            assert torch.equal(y, first_y), rep
+            assert torch.equal(Y, first_Y), rep
+
+
 def test_decode_layer_in_hip_graph():
     """moe_layer captured in a HIP graph: every replay (with eager work and syncs in between) gives
     the eager result bit for bit (the graph holds no memset nodes)."""
@@ -532,7 +601,15 @@ def _kv_rows(rng, rows, D):
                 blk *= 5e6                   # scale near / above the fp16 range
             elif kind[r, b] == 4:
                 blk[::3] = -0.0
-    return (v.view(np.uint32) >> 16).astype(np.uint16)
+    bits = (v.view(np.uint32) >> 16).astype(np.uint16)
+    # NaNs (code 0, left out of the block maximum) and infinities (scale saturates, code +-127)
+    nan_at = rng.random(bits.shape) < 0.01
+    bits[nan_at] = rng.choice(np.array([0x7FC0, 0xFFC0, 0x7F81, 0xFFFF], np.uint16), size=int(nan_at.sum()))
+    inf_at = rng.random(bits.shape) < 0.002
+    bits[inf_at] = rng.choice(np.array([0x7F80, 0xFF80], np.uint16), size=int(inf_at.sum()))
+    if rows > 1:
+        bits[1, :32] = 0x7FC0   # a whole block of NaNs
+    return bits
 
 
 def test_kv_encode_bit_exact():
@@ -563,7 +640,7 @@ def test_kv_gather_exact():
     torch.cuda.synchronize()
     want = oracle.kv_gather(o_codes, o_scales, idx)
     got = out.cpu().numpy().astype(np.float64)
-    assert np.all(np.isfinite(got))
+    assert np.all(np.isfinite(got))   # NaN and inf inputs still give finite rows
     assert np.array_equal(got, want)
 
 
