@@ -620,8 +620,11 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
     const int64_t rbI = row_bytes(FMT, L.I), rbS = row_bytes(FMT, L.Is);
     const int m0 = (blockIdx.x * kDownWaves + wave) * RPW;
     float* mypart = part + (size_t)wave * RPW * T * items_cap;
-    const int nrc = COMBINE ? 1 : (nU + spc - 1) / spc;   // chunks of routed slots
-    const int nch = COMBINE ? 1 : nrc + (nbS > 0 ? 1 : 0);
+    // every item in one pass when the partials fit (always with the combine fused), else chunks of
+    // spc routed slots and then the shared expert's blocks
+    const bool one = COMBINE || nU * nbI + nbS <= items_cap;
+    const int nrc = one ? 1 : (nU + spc - 1) / spc;   // chunks of routed slots
+    const int nch = one ? 1 : nrc + (nbS > 0 ? 1 : 0);
 
     float acc[RPW][T];
 #pragma unroll
@@ -631,10 +634,13 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
 
     bool h_in = false;   // h staged into LDS (by the first batch of loads; uniform over the block)
     for (int ch = 0; ch < nch; ++ch) {
-        int it0, it1;    // items [it0, it1) of this chunk
-        if (COMBINE) { it0 = 0; it1 = nU * nbI + nbS; }
-        else if (ch < nrc) { it0 = ch * spc * nbI; it1 = min((ch + 1) * spc, nU) * nbI; }
-        else { it0 = nU * nbI; it1 = it0 + nbS; }
+        // routed slots [s0, s1) and, with has_sh, the shared expert: items [it0, it1)
+        int s0, s1;
+        bool has_sh;
+        if (one) { s0 = 0; s1 = nU; has_sh = nbS > 0; }
+        else if (ch < nrc) { s0 = ch * spc; s1 = min(s0 + spc, nU); has_sh = false; }
+        else { s0 = s1 = nU; has_sh = true; }
+        const int it0 = s0 * nbI, it1 = s1 * nbI + (has_sh ? nbS : 0);
         const int nit = (it1 - it0 + kWave - 1) / kWave;
     for (int j0 = 0; j0 < nit; j0 += MAXJ) {
         uint32_t w[RPW][MAXJ][8];
@@ -736,9 +742,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             // lane -> (row, slot of the chunk, token): the slot's block partials summed in order
-            const bool routed = ch < nrc;
-            const int s0 = routed ? ch * spc : nU;
-            const int ns = routed ? min(spc, nU - s0) : 1;
+            const int nr = s1 - s0, ns = nr + (has_sh ? 1 : 0);
             for (int st = lane; st < RPW * ns * T; st += kWave) {
                 const int r = st / (ns * T), rem = st % (ns * T);
                 const int sl = rem / T, t = rem % T;
@@ -746,7 +750,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
                 if (m >= H) continue;
                 const float* pr = mypart + ((size_t)r * T + t) * items_cap;
                 const float sc = pow2f(-2 * P.xexp[t]);
-                if (routed) {
+                if (sl < nr) {
                     const int q = P.pair_of[s0 + sl][t];
                     if (q < 0) continue;
                     float sum = 0.f;
@@ -754,7 +758,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
                     y_pairs[(size_t)q * H + m] = sum * sc;
                 } else {
                     float sum = 0.f;
-                    for (int b = 0; b < nbS; ++b) sum += pr[b];
+                    for (int b = 0; b < nbS; ++b) sum += pr[nr * nbI + b];
                     y_shared[(size_t)t * H + m] = sum * sc;
                 }
             }

@@ -160,69 +160,77 @@ __host__ __device__ inline int kperm(int e, int G) {
 
 // -------------------------------------------------------------------------------- x to fp16
 // x (bf16) -> fp16 times the token's power-of-two scale 2^e_t (e_t from its largest |x|, see
-// common.h; written to xexp[t]), stored with the format's K permutation. One wave per token:
-// lane l takes the 32-element chunks l, l + 64, ... of the row (a permutation group never crosses a
-// chunk), a wave maximum gives e_t, then each chunk goes out as four 16-byte stores; chunks past
-// the first 64 of a row are read twice (the second time from L2).
+// common.h; written to xexp[t]), stored with the format's K permutation. One block of 256 threads
+// per token: thread i takes the VPT-element pieces i, i + 256, ... of the row (one 16- or 32-byte
+// load each, contiguous over the block; a permutation group never crosses a piece), the block
+// maximum comes from a wave reduction and four LDS words, then every piece goes out converted.
+// Pieces beyond the first two of a thread (rows longer than 512 VPT) are read again from L2.
 // Block 0 builds the tile list instead (the two do not depend on each other; the first block is
 // dispatched first, so the longer tile build overlaps the conversion).
-constexpr int kXTokensPerBlock = 4;
-template <int G>
+template <int G, int VPT>
 __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, int T, int H, _Float16* __restrict__ x16,
                                                   int32_t* __restrict__ xexp, const int32_t* __restrict__ offsets,
                                                   int E, int k, int has_shared, int tiles_max,
                                                   TileDesc* __restrict__ tiles, int32_t* __restrict__ ntiles) {
-    static_assert(32 % G == 0, "a chunk holds whole permutation groups");
+    static_assert(VPT % G == 0 && VPT % 8 == 0, "a piece holds whole permutation groups");
+    constexpr int NV = VPT / 8;   // 16-byte vectors per piece
     if (blockIdx.x == 0) {
         build_tiles_block(offsets, E, T, k, has_shared, tiles_max, tiles, ntiles);
         return;
     }
-    const int lane = threadIdx.x % kWave;
-    const int t = (int)(blockIdx.x - 1) * kXTokensPerBlock + (int)threadIdx.x / kWave;
-    if (t >= T) return;   // uniform per wave
-    const int nb = H / 32;
+    __shared__ uint32_t wmax[kTileThreads / kWave];
+    const int t = (int)blockIdx.x - 1;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int np = H / VPT;
     const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
-    auto load = [&](int c, u32x4 (&r)[4]) __attribute__((always_inline)) {
+    auto load = [&](int c, u32x4 (&r)[NV]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = row[4 * c + i];
+        for (int i = 0; i < NV; ++i) r[i] = row[NV * c + i];
     };
-    auto absmax = [&](const u32x4 (&r)[4]) __attribute__((always_inline)) {
+    auto absmax = [&](const u32x4 (&r)[NV]) __attribute__((always_inline)) {
         uint32_t m = 0u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = max(m, bf16_absmax_bits(make_uint4(r[i].x, r[i].y, r[i].z, r[i].w)));
+        for (int i = 0; i < NV; ++i) m = max(m, bf16_absmax_bits(make_uint4(r[i].x, r[i].y, r[i].z, r[i].w)));
         return m;
     };
-    u32x4 keep[4];
-    load(min(lane, nb - 1), keep);
-    uint32_t m = lane < nb ? absmax(keep) : 0u;
-    for (int c = lane + kWave; c < nb; c += kWave) {
-        u32x4 r[4];
+    u32x4 k0[NV], k1[NV];
+    load(min(tid, np - 1), k0);
+    load(min(tid + kTileThreads, np - 1), k1);
+    uint32_t m = tid < np ? absmax(k0) : 0u;
+    if (tid + kTileThreads < np) m = max(m, absmax(k1));
+    for (int c = tid + 2 * kTileThreads; c < np; c += kTileThreads) {
+        u32x4 r[NV];
         load(c, r);
         m = max(m, absmax(r));
     }
-    const int e = token_exp_from_bits(wave_max_u32(m));
-    if (lane == 0) xexp[t] = e;
+    m = wave_max_u32(m);
+    if (lane == 0) wmax[wave] = m;
+    __syncthreads();
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const int e = token_exp_from_bits(m);
+    if (tid == 0) xexp[t] = e;
     const float sc = pow2f(e);
     half8* dst = reinterpret_cast<half8*>(x16 + (size_t)t * H);
-    auto convert = [&](const u32x4 (&r)[4], int c) __attribute__((always_inline)) {
-        _Float16 o[32];
+    auto convert = [&](const u32x4 (&r)[NV], int c) __attribute__((always_inline)) {
+        _Float16 o[VPT];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < VPT / 2; ++i) {
             const uint32_t w = r[i / 4][i % 4];
             o[kperm(2 * i, G)] = (_Float16)(bf16_lo(w) * sc);
             o[kperm(2 * i + 1, G)] = (_Float16)(bf16_hi(w) * sc);
         }
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
+        for (int h = 0; h < NV; ++h) {
             half8 v;
 #pragma unroll
             for (int q = 0; q < 8; ++q) v[q] = o[8 * h + q];
-            dst[4 * c + h] = v;
+            dst[NV * c + h] = v;
         }
     };
-    if (lane < nb) convert(keep, lane);
-    for (int c = lane + kWave; c < nb; c += kWave) {
-        u32x4 r[4];
+    if (tid < np) convert(k0, tid);
+    if (tid + kTileThreads < np) convert(k1, tid + kTileThreads);
+    for (int c = tid + 2 * kTileThreads; c < np; c += kTileThreads) {
+        u32x4 r[NV];
         load(c, r);
         convert(r, c);
     }
@@ -509,12 +517,12 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     // lane offsets stay fixed; a block past the end of the matrix reads as zero (bounds-checked).
     // A chunk past K (the second half of the last step when K % 64 == 32) reloads the row's last
     // chunk instead (its weights are zero, see below).
-    auto issue = [&](BSlot (&sl)[2], int t, int stage, auto group_start) __attribute__((always_inline)) {
-        // A step past the end issues no direct-to-LDS load at all: the stages and the scale buffers
-        // are reused by the epilogue, and a transfer still landing there after the final wait would
-        // overwrite the staged outputs (such late writes were observed). Its register loads still go
-        // out (clamped, unused); the waits of the last steps cover everything.
-        const bool live = t < nsteps;
+    // TAIL: the step may lie past the end of K. Such a step issues no direct-to-LDS load at all: the
+    // stages and the scale buffers are reused by the epilogue, and a transfer still landing there
+    // after the final wait would overwrite the staged outputs (such late writes were observed). Its
+    // register loads still go out (clamped, unused), so every step issues a known number of loads.
+    auto issue = [&](BSlot (&sl)[2], int t, int stage, auto group_start, auto tail) __attribute__((always_inline)) {
+        const bool live = !decltype(tail)::value || t < nsteps;
         t = min(t, nsteps - 1);
         uint8_t* st = smem + stage * kStageBytes + wave * 1024;
         if (live) {
@@ -604,8 +612,11 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     // free, and step s + 4 is loaded into them while sub-step 3 runs and step s + 1's first
     // operands are prepared. The barrier is written out so that no memory fence makes it wait for
     // the loads still in flight.
-    auto kstep = [&](int s, auto sc) __attribute__((always_inline)) {
+    // TAIL: one of the last steps, where steps s + 2 .. s + 4 may lie past the end (the steady-state
+    // loop runs only steps whose loads are all live).
+    auto kstep = [&](int s, auto sc, auto tail) __attribute__((always_inline)) {
         constexpr int SL = decltype(sc)::value;   // = s % 4
+        constexpr bool TAIL = decltype(tail)::value;
         constexpr int SN = (SL + 1) % 4;
         constexpr bool kIssueGroup = SD && SL == 0;                  // step s + 4 starts a scale group
         constexpr int kInFlightGroups = (SD && (SL == 1 || SL == 2)) ? 1 : 0;   // s + 2 or s + 3 does
@@ -625,11 +636,18 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
                 frag(st, std::integral_constant<int, kk + 1>{}, nxt_a);
                 deq(cur, std::integral_constant<int, kk + 1>{}, svc0, svc1, nxt_b);
             } else {
-                // the counted wait holds while steps s + 2 and s + 3 exist; near the end fewer loads
-                // are in flight, so everything is waited for
-                if (s + 3 < nsteps) step_barrier<2 * BATCH + kInFlightGroups>();
-                else step_barrier<0>();
-                issue(slot(sc), s + 4, SL, std::integral_constant<bool, kIssueGroup>{});
+                // leave in flight exactly the loads of steps s + 2 and s + 3: a full batch (and a scale
+                // group) for a live step, only the register loads for a step past the end
+                if constexpr (!TAIL) {
+                    step_barrier<2 * BATCH + kInFlightGroups>();
+                } else {
+                    constexpr int kDead = BATCH - QW;                          // loads of a dead step
+                    constexpr int kG2 = (SD && SL == 2) ? 1 : 0;               // s + 2 starts a group
+                    if (s + 3 < nsteps) step_barrier<2 * BATCH + kInFlightGroups>();
+                    else if (s + 2 < nsteps) step_barrier<BATCH + kG2 + kDead>();
+                    else step_barrier<2 * kDead>();
+                }
+                issue(slot(sc), s + 4, SL, std::integral_constant<bool, kIssueGroup>{}, tail);
                 scales(s + 1, nxt, svn0, svn1);
                 frag(stn, std::integral_constant<int, 0>{}, nxt_a);
                 deq(nxt, std::integral_constant<int, 0>{}, svn0, svn1, nxt_b);
@@ -655,10 +673,12 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     };
 
     // prologue: steps 0-3 in flight, then step 0's first operands
-    issue(slot0, 0, 0, std::integral_constant<bool, SD>{});
-    issue(slot1, 1, 1, std::integral_constant<bool, false>{});
-    issue(slot2, 2, 2, std::integral_constant<bool, false>{});
-    issue(slot3, 3, 3, std::integral_constant<bool, false>{});
+    const std::integral_constant<bool, true> kTail{};
+    const std::integral_constant<bool, false> kSteady{};
+    issue(slot0, 0, 0, std::integral_constant<bool, SD>{}, kTail);
+    issue(slot1, 1, 1, std::integral_constant<bool, false>{}, kTail);
+    issue(slot2, 2, 2, std::integral_constant<bool, false>{}, kTail);
+    issue(slot3, 3, 3, std::integral_constant<bool, false>{}, kTail);
     if (nsteps >= 4) step_barrier<3 * BATCH>();
     else step_barrier<0>();
     if constexpr (kRowExp) {
@@ -671,15 +691,22 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     frag(smem, std::integral_constant<int, 0>{}, fa);
     deq(slot0, std::integral_constant<int, 0>{}, svc0, svc1, ba);
     int s = 0;
-    for (; s + 4 <= nsteps; s += 4) {
-        kstep(s, std::integral_constant<int, 0>{});
-        kstep(s + 1, std::integral_constant<int, 1>{});
-        kstep(s + 2, std::integral_constant<int, 2>{});
-        kstep(s + 3, std::integral_constant<int, 3>{});
+    for (; s + 8 <= nsteps; s += 4) {   // every load these steps issue is live
+        kstep(s, std::integral_constant<int, 0>{}, kSteady);
+        kstep(s + 1, std::integral_constant<int, 1>{}, kSteady);
+        kstep(s + 2, std::integral_constant<int, 2>{}, kSteady);
+        kstep(s + 3, std::integral_constant<int, 3>{}, kSteady);
     }
-    if (s < nsteps) kstep(s, std::integral_constant<int, 0>{});
-    if (s + 1 < nsteps) kstep(s + 1, std::integral_constant<int, 1>{});
-    if (s + 2 < nsteps) kstep(s + 2, std::integral_constant<int, 2>{});
+    if (s + 4 <= nsteps) {
+        kstep(s, std::integral_constant<int, 0>{}, kTail);
+        kstep(s + 1, std::integral_constant<int, 1>{}, kTail);
+        kstep(s + 2, std::integral_constant<int, 2>{}, kTail);
+        kstep(s + 3, std::integral_constant<int, 3>{}, kTail);
+        s += 4;
+    }
+    if (s < nsteps) kstep(s, std::integral_constant<int, 0>{}, kTail);
+    if (s + 1 < nsteps) kstep(s + 1, std::integral_constant<int, 1>{}, kTail);
+    if (s + 2 < nsteps) kstep(s + 2, std::integral_constant<int, 2>{}, kTail);
     // every direct load has landed and every wave is done with the stages: LDS is free
     step_barrier<0>();
 
@@ -862,8 +889,8 @@ static moe_status launch_prefill_f(const LayerView& L, const uint16_t* x, int T,
                                    const int32_t* perm, void* y_sorted, void* y_shared, PrefillOut mode,
                                    const PrefillScratch& s, hipStream_t st) {
     constexpr int G = perm_group<FMT>();
-    const int xblocks = (T + kXTokensPerBlock - 1) / kXTokensPerBlock;
-    hipLaunchKernelGGL((k_x_to_f16<G>), dim3((unsigned)(xblocks + 1)), dim3(kTileThreads), 0, st, x, T, L.H, s.x16,
+    constexpr int VPT = G <= 8 ? 8 : 16;
+    hipLaunchKernelGGL((k_x_to_f16<G, VPT>), dim3((unsigned)(T + 1)), dim3(kTileThreads), 0, st, x, T, L.H, s.x16,
                        s.xexp, offsets, L.E, L.k, L.Is > 0 ? 1 : 0, max_tiles(T, L.k, L.E), s.tiles, s.ntiles);
     MOE_LAUNCH_CHECK();
     const int mt = max_tiles(T, L.k, L.E);
