@@ -213,6 +213,8 @@ def decode_workload(name: str, steps: int, warmup: int, graph: bool = True):
            "inter": spec.I, "shared_inter": spec.Is, "format": synth.FMT_NAMES[spec.fmt],
            "layer_calls_per_step": len(layers), "resident_layers": len(layers),
            "launch": "hip_graph" if graph else "eager"}
+    del layers, calls, ecalls
+    torch.cuda.empty_cache()
     return value, ms_per_step, roof, cfg
 
 
@@ -252,7 +254,8 @@ def prefill_workload(steps: int, warmup: int):
             "kernel": "moe_experts_prefill_f16 (k_x_to_f16 with the tile list + k_grouped_gemm gate/up + k_grouped_gemm down)",
             "flops_per_launch": flops, "avg_launch_us": round(avg_ms * 1e3, 1)}
     return {"metric": "MoE-layer tokens/s (8192-token prefill chunk)", "value": round(value, 1),
-            "unit": "tokens/s", "dtype": "f16", "ms_per_step": round(ms_per_step, 4), "roofline": roof,
+            "unit": "tokens/s", "dtype": "f16", "ms_per_step": round(ms_per_step, 4),
+            "roofline": roof,
             "config": {"workload": "prefill8k", "tokens_per_call": T, "hidden": spec.H, "experts": spec.E,
                        "top_k": spec.k, "inter": spec.I, "shared_inter": spec.Is,
                        "format": synth.FMT_NAMES[spec.fmt]}}
@@ -318,24 +321,45 @@ def sweep_tokens(reps: int = 10):
     return rows
 
 
-def cpu_baseline(name: str, budget_s: float = 12.0):
-    """The fp64 oracle (single thread) on a bounded sample of the workload's tokens."""
+def host_cpu():
+    """CPU model and logical core count of this host (for the CPU-baseline records)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count() or 0
+
+
+def cpu_baseline(name: str, budget_s: float = 6.0):
+    """The fp64 oracle, single-threaded, on a bounded sample of the same workload: the same layer
+    and the same input tokens the GPU run uses (layer 0 for the 48-layer stack, whose layers all
+    have the same shape; the first tokens of the 8192-token chunk for prefill, whose cost is
+    linear in tokens, so tokens/s of the sample is the chunk's rate)."""
     import oracle
     spec = synth.CONFIGS[name]
     d = synth.make_layer(spec, layer=0)
     O = oracle.Layer.from_synth(spec, d)
-    xs = synth.make_x(spec, layer=0, seed=1, T=64)
+    xs = d["x"]
     n = 0
     t0 = time.perf_counter()
     while True:
-        O.token(xs[n % 64])
+        O.token(xs[n % xs.shape[0]])
         n += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
+    model, nproc = host_cpu()
+    what = {"prefill8k": "the first %d of the 8192 tokens of the chunk (extrapolated: cost is linear in tokens)" % n,
+            "stack48": "%d tokens through layer 0 of the stack (every layer has the same shape)" % n}.get(
+        name, "%d tokens (the GPU run's own input%s) through the full layer" % (n, "s, cycled" if spec.T > 1 else ""))
     return {"value": round(n / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d tokens through one full %s layer (router, top-k, experts, combine), fp64, 1 thread, %.1f s"
-                      % (n, name, el)}
+            "sample": "%s: router, top-k, experts, combine in fp64 on 1 thread, %.1f s" % (what, el),
+            "host_nproc": nproc, "host_cpu": model, "workload": name}
 
 
 def main():
@@ -347,6 +371,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary 8K prefill measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kv", action="store_true", help="skip the secondary KV-codec measurement")
+    ap.add_argument("--no-other-decode", action="store_true",
+                    help="with the default decode1 workload, skip the secondary verify4 and stack48 lines")
     ap.add_argument("--eager", action="store_true",
                     help="launch every decode call from Python instead of replaying one captured HIP graph per step")
     ap.add_argument("--sweep-tokens", action="store_true",
@@ -369,6 +395,7 @@ def main():
                           "rows": sweep_tokens()}), flush=True)
         return
 
+    others = {}
     if args.workload == "prefill8k":
         r = prefill_workload(args.steps, args.warmup)
         value, ms, roof, cfg, metric = r["value"], r["ms_per_step"], r["roofline"], r["config"], r["metric"]
@@ -377,18 +404,31 @@ def main():
         value, ms, roof, cfg = decode_workload(args.workload, args.steps, args.warmup, graph=not args.eager)
         metric = "MoE-layer tokens/s (decode, %% HBM peak on expert-weight bytes)"
         secondary = None if args.no_prefill else prefill_workload(max(10, args.steps), 3)
+        if args.workload == "decode1" and not args.no_other_decode:
+            # the other decode workloads as secondary lines of the same run
+            for w in ("verify4", "stack48"):
+                v2, ms2, roof2, cfg2 = decode_workload(w, max(5, args.steps // 2), 2, graph=not args.eager)
+                others[w] = {"metric": "MoE-layer tokens/s (decode, % HBM peak on expert-weight bytes)",
+                             "value": round(v2, 1), "unit": "tokens/s", "ms_per_step": round(ms2, 4),
+                             "dtype": "f16", "roofline": roof2, "config": cfg2}
     line = {"metric": metric.replace("%%", "%"), "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "f16" if args.workload == "prefill8k" else "f32",
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16",
             "data": "synthetic (seeded N(0,0.02) weights quantised to block-32 codes, bf16 N(0,1) activations, "
                     "Zipf-biased router)",
             "config": cfg, "roofline": roof}
+    for w, o in others.items():
+        line[w] = o
     if secondary is not None:
         line["prefill"] = secondary
     if not args.no_kv and args.workload != "prefill8k":
         line["kv_cache"] = kv_workload()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.workload if args.workload != "stack48" else "stack48", 12.0)
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+        if args.workload == "decode1":
+            for w in list(others) + ([] if secondary is None else ["prefill8k"]):
+                obj = line["prefill"] if w == "prefill8k" else line[w]
+                obj["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
 
 

@@ -378,26 +378,64 @@ def test_decode_and_prefill_agree():
     assert_float_match(Yp.cpu().numpy(), ref["Y"], "prefill Y")
 
 
+def _pool_map(fn, items):
+    """The oracle is single-threaded C called through ctypes (which releases the GIL) and keeps no
+    state between calls, so independent calls run side by side on the host's cores."""
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+        return list(ex.map(fn, items))
+
+
+def host_tiles(counts, T, has_shared, tm=128):
+    """The grouped GEMM's row tiles, by the kernel's rule: per group, full tiles of 128 rows and one
+    remainder tile; the shared group (all T tokens) last. Returns (group, first row, rows)."""
+    tiles = []
+    for e, n in enumerate(counts):
+        for r0 in range(0, int(n), tm):
+            tiles.append((e, r0, min(tm, int(n) - r0)))
+    if has_shared:
+        for r0 in range(0, T, tm):
+            tiles.append((len(counts), r0, min(tm, T - r0)))
+    return tiles
+
+
 def test_prefill8k_full_size():
-    """The 8192-token chunk at full size, in the launch configuration the benchmark times."""
+    """The 8192-token chunk at full size, in the launch configuration the benchmark times: every
+    token's ids and p, the full permutation, one y_sorted row in every row tile of the grouped GEMMs
+    (all column tiles of that row) and one shared-expert row per shared tile against the oracle's
+    expert outputs, and Y on sampled tokens."""
     _need_gpu()
     spec, d = host_layer("prefill8k")
     say("prefill8k: GPU layer")
     O = orc_layer(spec, d)
     g_logits, g_ids, g_p, Y = run_layer(spec, d)
-    T = spec.T
-    # every token's ids and p from the GPU logits; logits on a sample of rows
+    T, k, H = spec.T, spec.k, spec.H
     rows = np.unique(np.concatenate([[0, 1, T - 1], np.random.default_rng(0).integers(0, T, 125)]))
     say("prefill8k: routing check")
     flips = check_routing(O, d["x"], g_logits, g_ids, g_p, token_rows=rows)
-    # permutation of all pairs, bit-exact
     L = dev_layer(spec, d)
+    xd = dev_x(d["x"])
     off, perm, inv = moe.moe_permute(L, torch.from_numpy(g_ids).cuda())
+    ys, ysh = moe.moe_experts_prefill(L, xd, off, perm)
+    torch.cuda.synchronize()
     o_off, o_perm, o_inv = oracle.permute(g_ids, spec.E)
     assert np.array_equal(off.cpu().numpy(), o_off) and np.array_equal(perm.cpu().numpy(), o_perm)
     assert np.array_equal(inv.cpu().numpy(), o_inv)
-    # Y on sampled tokens (incl. tokens of the hottest and of a 1-token expert)
+    # one checked row in every tile of the tile list
     counts = np.diff(o_off)
+    tiles = host_tiles(counts, T, spec.Is > 0)
+    rng = np.random.default_rng(2)
+    picks = [(g, r0 + int(rng.integers(0, n))) for g, r0, n in tiles]
+    routed = [(g, o_off[g] + r) for g, r in picks if g < spec.E]
+    shared = [r for g, r in picks if g == spec.E]
+    xf = oracle.bf16_to_f64(d["x"])
+    say("prefill8k: oracle on %d routed tile rows, %d shared tile rows" % (len(routed), len(shared)))
+    want_r = np.stack(_pool_map(lambda it: O.expert(int(it[0]), xf[o_perm[it[1]] // k]), routed))
+    want_s = np.stack(_pool_map(lambda t: O.shared(xf[t]), shared))
+    ysn, yshn = ys.cpu().numpy(), ysh.cpu().numpy()
+    rel_r, mx_r = assert_float_match(ysn[[i for _, i in routed]], want_r, "y_sorted (a row of every tile)")
+    assert_float_match(yshn[shared], want_s, "y_shared (a row of every shared tile)")
+    # Y on sampled tokens (incl. tokens of the hottest and of a 1-token expert)
     hot = int(np.argmax(counts))
     single = np.nonzero(counts == 1)[0]
     pick = [0, T - 1, int(np.nonzero((g_ids == hot).any(1))[0][0])]
@@ -406,9 +444,10 @@ def test_prefill8k_full_size():
     pick += np.random.default_rng(1).integers(0, T, 12).tolist()
     pick = sorted(set(pick))
     say("prefill8k: oracle on %d tokens" % len(pick))
-    ref = oracle_tokens(O, d["x"], g_logits, pick)
-    rel, mx = assert_float_match(Y[pick], ref["Y"], "Y (sampled)")
-    say("prefill8k Y rel %.2e maxabs/rms %.2e flips %d of %d sampled" % (rel, mx, flips, len(rows)))
+    outs = _pool_map(lambda t: O.token(d["x"][t], logits_in=g_logits[t].astype(np.float64)), pick)
+    rel, mx = assert_float_match(Y[pick], np.stack([o["Y"] for o in outs]), "Y (sampled)")
+    say("prefill8k %d tiles: y_sorted rel %.2e; Y rel %.2e maxabs/rms %.2e; flips %d of %d sampled"
+        % (len(tiles), rel_r, rel, mx, flips, len(rows)))
 
 
 # ------------------------------------------------------------------------- permutation edge cases
@@ -554,30 +593,87 @@ def test_prefill_repeat_bitwise(T, H, E, k, I, Is):
 
 
 def test_decode_layer_in_hip_graph():
-    """moe_layer captured in a HIP graph: every replay (with eager work and syncs in between) gives
-    the eager result bit for bit (the graph holds no memset nodes)."""
+    """moe_layer captured in a HIP graph: every replay (with eager work and syncs in between) meets
+    the oracle (ids bit-exact from the replay's own logits, Y within the float rule) and equals the
+    eager result bit for bit (the graph holds no memset nodes)."""
     _need_gpu()
     spec, d = host_layer("decode1")
+    O = orc_layer(spec, d)
     L = dev_layer(spec, d)
     x = dev_x(d["x"])
     ws = moe.Workspace()
     out = torch.empty((spec.T, spec.H), dtype=torch.float32, device="cuda")
     ids = torch.empty((spec.T, spec.k), dtype=torch.int32, device="cuda")
-    moe.moe_layer(L, x, out=out, ids=ids, ws=ws)
+    logits = torch.empty((spec.T, spec.E), dtype=torch.float32, device="cuda")
+    moe.moe_layer(L, x, out=out, logits=logits, ids=ids, ws=ws)
     torch.cuda.synchronize()
     want_out, want_ids = out.clone(), ids.clone()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        moe.moe_layer(L, x, out=out, ids=ids, ws=ws)
+        moe.moe_layer(L, x, out=out, logits=logits, ids=ids, ws=ws)
+    ref = None
     for rep in range(3):
         out.fill_(float("nan"))
         ids.fill_(-7)
         g.replay()
         torch.cuda.synchronize()
+        lg = logits.cpu().numpy()
+        if ref is None:
+            ref = oracle_tokens(O, d["x"], lg, range(spec.T))
+        assert np.array_equal(ids.cpu().numpy(), oracle.topk_softmax(lg.astype(np.float64), spec.k)[0]), rep
+        assert_float_match(out.cpu().numpy(), ref["Y"], "graph replay %d: Y" % rep)
         assert torch.equal(ids, want_ids), rep
         assert torch.equal(out, want_out), rep
         moe.moe_layer(L, x, out=torch.empty_like(out), ws=moe.Workspace())   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_stack48_graph_replay():
+    """The 48-layer decode stack as the benchmark runs it: 48 moe_layer calls (one per layer, each
+    with its own input token and output) captured once as a HIP graph and replayed twice. Layers 0,
+    23 and 47 carry their own generated weights and are checked against the oracle after every
+    replay; the other 45 positions hold device copies of layer 0's weights (distinct addresses, same
+    bytes) with their own inputs, so that the graph has the full length and memory footprint."""
+    _need_gpu()
+    spec = synth.CONFIGS["stack48"]
+    checked = {}
+    for l in (0, 23, 47):
+        _, dl = host_layer("stack48", l)
+        checked[l] = dl
+    base = dev_layer(spec, checked[0])
+    layers, xs = [], []
+    for l in range(spec.layers):
+        if l in checked:
+            layers.append(base if l == 0 else dev_layer(spec, checked[l]))
+            xs.append(dev_x(checked[l]["x"]))
+        else:
+            m = base.mats
+            layers.append(moe.DeviceLayer(base.desc, base.w_router.clone(),
+                                          None if base.router_bias is None else base.router_bias.clone(),
+                                          *[(m[n][0].clone(), m[n][1].clone()) for n in ("gate", "up", "down")]))
+            xs.append(dev_x(synth.make_x(spec, layer=l)))
+    say("stack48 graph: %d layers resident" % len(layers))
+    ws = moe.Workspace()
+    outs = [torch.empty((1, spec.H), dtype=torch.float32, device="cuda") for _ in layers]
+    lgs = [torch.empty((1, spec.E), dtype=torch.float32, device="cuda") for _ in layers]
+    for L, x, o, lg in zip(layers, xs, outs, lgs):   # warm-up (workspace sized outside the capture)
+        moe.moe_layer(L, x, out=o, logits=lg, ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for L, x, o, lg in zip(layers, xs, outs, lgs):
+            moe.moe_layer(L, x, out=o, logits=lg, ws=ws)
+    for rep in range(2):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for l, dl in checked.items():
+            O = orc_layer(spec, dl)
+            lg = lgs[l].cpu().numpy()
+            ref = oracle_tokens(O, dl["x"], lg, range(1))
+            assert_float_match(outs[l].cpu().numpy(), ref["Y"], "replay %d, layer %d: Y" % (rep, l))
+        say("stack48 graph replay %d: layers 0, 23, 47 match the oracle" % rep)
 
 
 # ------------------------------------------------------------------------- KV int8 codec
