@@ -30,8 +30,9 @@
  *     call returns without waiting; buffers must stay valid until the stream has passed the work.
  *   - Arguments are checked on the host before anything is enqueued. A failed check returns a
  *     status other than MOE_OK and enqueues nothing. A failed launch returns MOE_ERR_HIP.
- *   - The library has no global mutable state and is reentrant. Two calls that share a workspace
- *     must be ordered on one stream.
+ *   - Calls keep no state between them and are reentrant; the only process-wide state is per
+ *     device and written once (the compute-unit count, and the device address of
+ *     moe_layer_static's array). Two calls that share a workspace must be ordered on one stream.
  *   - Workspaces: size them with moe_workspace_size(), 16-byte aligned, any contents. No kernel
  *     waits on another block of its own grid; every cross-block dependency is a kernel boundary,
  *     so calls may be captured in a HIP graph. Expert ids read from memory are range-checked
@@ -229,6 +230,25 @@ moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const float* p, co
 moe_status moe_layer(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x, int32_t T,
                      float* out, float* logits, int32_t* ids, float* p, void* ws, size_t ws_bytes,
                      void* stream);
+
+/*
+ * moe_layer for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same computation, with the workspace taken
+ * from a fixed device array inside the library (moe_layer_static_max_bytes() = 16 MiB per GPU, held
+ * from load until the process ends) instead of a caller buffer. The caller still passes x, out and
+ * the optional logits/ids/p. A shape whose moe_workspace_size(MOE_CALL_LAYER) exceeds the array
+ * returns MOE_ERR_UNSUPPORTED before anything is enqueued (every decode shape fits; prefill batches
+ * up to a few hundred tokens at H = 2048). Nothing is allocated: the array's device address is
+ * looked up once per device, on the first call made with that device current. Every call on a GPU
+ * shares that GPU's array, so calls that may overlap on one GPU (other streams, other host threads)
+ * race and must be ordered by the caller; consecutive calls on one stream are safe (the workspace
+ * needs no clearing between calls).
+ */
+moe_status moe_layer_static(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x, int32_t T,
+                            float* out, float* logits, int32_t* ids, float* p, void* stream);
+
+/* Bytes of moe_layer_static's device array (host only). */
+size_t moe_layer_static_max_bytes(void);
 
 /*
  * KV cache codec: the same block-32 int8 format as the Q8 weights, for the attention cache (648news

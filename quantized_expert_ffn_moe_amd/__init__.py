@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "MoeError", "LayerDesc", "DeviceLayer", "Workspace", "lib", "library_path",
     "moe_route", "moe_permute", "moe_experts_decode", "moe_experts_prefill", "moe_combine", "moe_layer",
+    "moe_layer_static", "moe_layer_static_max_bytes",
     "moe_kv_encode", "moe_kv_gather",
     "moe_workspace_size", "moe_status_string", "moe_abi_version",
     "MOE_Q8_B32", "MOE_Q4_B32", "MOE_Q2_B32",
@@ -87,6 +88,10 @@ def lib():
         L.moe_combine.argtypes = [D, i32, vp, vp, vp, vp, vp, vp]
         L.moe_layer.restype = st
         L.moe_layer.argtypes = [D, W, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_layer_static.restype = st
+        L.moe_layer_static.argtypes = [D, W, vp, i32, vp, vp, vp, vp, vp]
+        L.moe_layer_static_max_bytes.restype = sz
+        L.moe_layer_static_max_bytes.argtypes = []
         L.moe_workspace_size.restype = st
         L.moe_workspace_size.argtypes = [D, i32, i32, ctypes.POINTER(sz)]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -302,6 +307,22 @@ def moe_layer(layer: DeviceLayer, x, out=None, logits=None, ids=None, p=None, ws
                            _ptr(ids), _ptr(p), _ptr(buf), nb, _stream(stream)), "moe_layer")
     _keep(stream, buf, out)
     return out
+
+
+def moe_layer_static(layer: DeviceLayer, x, out=None, logits=None, ids=None, p=None, stream=None):
+    """moe_layer with the library's own fixed device workspace (no workspace argument): for callers
+    that cannot allocate. Calls that may overlap on one GPU must be ordered by the caller."""
+    d = layer.desc
+    T = x.shape[0]
+    out = torch.empty((T, d.hidden), dtype=torch.float32, device=x.device) if out is None else out
+    _check(lib().moe_layer_static(ctypes.byref(d.c), ctypes.byref(layer.c), _ptr(_x_bits(x)), T, _ptr(out),
+                                  _ptr(logits), _ptr(ids), _ptr(p), _stream(stream)), "moe_layer_static")
+    _keep(stream, out)
+    return out
+
+
+def moe_layer_static_max_bytes() -> int:
+    return int(lib().moe_layer_static_max_bytes())
 
 
 def moe_kv_encode(src, codes=None, scales=None, stream=None):

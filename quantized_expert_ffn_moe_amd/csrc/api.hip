@@ -1,5 +1,6 @@
 // The C ABI of include/moe.h: host-side argument checks, workspace carving and stream-ordered
 // launches. Nothing here allocates device memory or synchronises the stream.
+#include <mutex>
 #include <string.h>
 
 #include "kernels.h"
@@ -144,6 +145,38 @@ moe_status check_ws(void* ws, size_t ws_bytes, size_t need) {
     if (need == 0) return MOE_OK;
     if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
     return ws_bytes >= need ? MOE_OK : MOE_ERR_WORKSPACE;
+}
+
+// ------------------------------------------------------------------ static workspace
+
+// moe_layer_static's workspace: a file-scope device array (each GPU holds its own copy from load
+// until the process ends). Host code never uses the array's name as an address: its device address
+// comes from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's copy of scratch (nullptr and a status on failure).
+void* static_scratch(moe_status* st) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *st = MOE_ERR_HIP;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            *st = MOE_ERR_HIP;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *st = MOE_OK;
+    return g_scratch_ptr[dev];
 }
 
 #define MOE_TRY(expr)                   \
@@ -334,5 +367,20 @@ moe_status moe_layer(const moe_layer_desc* d, const moe_layer_weights* w, const 
                                    lw.prefill, s));
     return launch_combine_f16(T, L.k, L.H, pr, lw.y_rows, lw.inv, ysh, prefill_token_exps(L, T, lw.prefill), out, s);
 }
+
+moe_status moe_layer_static(const moe_layer_desc* d, const moe_layer_weights* w, const uint16_t* x, int32_t T,
+                            float* out, float* logits, int32_t* ids, float* p, void* stream) {
+    MOE_TRY(check_desc(d));
+    MOE_TRY(check_T(T));
+    size_t need = 0;
+    carve_layer(d, T, nullptr, &need);
+    if (need > kStaticScratchBytes) return MOE_ERR_UNSUPPORTED;
+    moe_status st = MOE_OK;
+    void* ws = static_scratch(&st);
+    if (st != MOE_OK) return st;
+    return moe_layer(d, w, x, T, out, logits, ids, p, ws, kStaticScratchBytes, stream);
+}
+
+size_t moe_layer_static_max_bytes(void) { return kStaticScratchBytes; }
 
 }  // extern "C"

@@ -134,6 +134,22 @@ def test_decode_lds_limit_settled_before_launch():
     assert moe.moe_workspace_size(s48, 4, moe.MOE_CALL_EXPERTS_DECODE) > 0
 
 
+def test_layer_static_limits_on_host():
+    """moe_layer_static: a 16 MiB device array; a shape whose layer workspace exceeds it is refused
+    with MOE_ERR_UNSUPPORTED by the host check, before any GPU call (there is no GPU here)."""
+    assert moe.moe_layer_static_max_bytes() == 16 << 20
+    d = D()
+    assert moe.moe_workspace_size(d, 4, moe.MOE_CALL_LAYER) <= moe.moe_layer_static_max_bytes()
+    assert moe.moe_workspace_size(d, 8192, moe.MOE_CALL_LAYER) > moe.moe_layer_static_max_bytes()
+    fake = 0x10000
+    w = moe._Weights(fake, None, moe._QMat(fake, fake), moe._QMat(fake, fake), moe._QMat(fake, fake),
+                     moe._QMat(fake, fake), moe._QMat(fake, fake), moe._QMat(fake, fake))
+    assert _raw("moe_layer_static", ctypes.byref(d.c), ctypes.byref(w), fake, 8192, fake, None, None, None,
+                None) == moe.MOE_ERR_UNSUPPORTED
+    assert _raw("moe_layer_static", ctypes.byref(d.c), ctypes.byref(w), fake, 0, fake, None, None, None,
+                None) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_kv_validation_rejects_before_launch():
     fake = 0x10000
     assert _raw("moe_kv_encode", fake, 4, 48, fake, fake, None) == moe.MOE_ERR_INVALID_ARG        # D % 32
