@@ -286,36 +286,34 @@ def kv_workload(reps: int = 20):
             "encode": roof(enc_bytes, enc_ms, "k_kv_encode"), "gather": roof(gat_bytes, gat_ms, "k_kv_gather")}
 
 
-def sweep_tokens(reps: int = 10):
+def sweep_tokens(reps: int = 20):
     """Mid-size batches: moe_layer time per call for T = 1 .. 8192 tokens on the prefill8k layer
-    (hidden 2048, 256 experts top-8 + shared, 4-bit), with the path moe_layer takes at each T
-    (decode kernels for T <= 4, the grouped-GEMM path above), and the grouped-GEMM path forced
-    through the separate entry points at T <= 4 for the crossover."""
+    (hidden 2048, 256 experts top-8 + shared, 4-bit), each T captured as a HIP graph of 10 calls and
+    replayed. moe_layer's default regime switch is timed at every T; for T <= 8 also both regimes
+    forced through the descriptor's decode_max_tokens (8: decode kernels, 1: grouped GEMMs)."""
     spec = synth.CONFIGS["prefill8k"]
     d = synth.make_layer(spec)
     L = upload(spec, d)
+
+    def with_desc(dmt):
+        m = L.mats
+        return moe.DeviceLayer(moe.LayerDesc.from_spec(spec, dmt), L.w_router, L.router_bias, m["gate"], m["up"],
+                               m["down"], m["sh_gate"], m["sh_up"], m["sh_down"])
+    Ld, Lg = with_desc(8), with_desc(1)
     xs_all = dev_x(d["x"])
     rows = []
-    for T in [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192]:
+    for T in [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192]:
         x = xs_all[:T].contiguous()
-        ws = moe.Workspace()
         out = torch.empty((T, spec.H), dtype=torch.float32, device="cuda")
-        ms = time_calls([lambda: moe.moe_layer(L, x, out=out, ws=ws)], 2, reps)
-        row = {"T": T, "path": "decode" if T <= 4 else "grouped_gemm", "us_per_call": round(ms * 1e3, 2),
-               "tokens_per_s": round(T / (ms / 1e3), 1)}
-        if T <= 4:
-            lg = torch.empty((T, spec.E), dtype=torch.float32, device="cuda")
-            w1, w2, w3, w4 = moe.Workspace(), moe.Workspace(), moe.Workspace(), moe.Workspace()
-            ys = torch.empty((T * spec.k, spec.H), dtype=torch.float32, device="cuda")
-            ysh = torch.empty((T, spec.H), dtype=torch.float32, device="cuda")
 
-            def forced():
-                _, ids, p = moe.moe_route(L, x, logits=lg, ws=w1)
-                off, perm, inv = moe.moe_permute(L, ids, ws=w2)
-                moe.moe_experts_prefill(L, x, off, perm, y_sorted=ys, y_shared=ysh, ws=w3)
-                moe.moe_combine(L, p, ys, inv, ysh, out=out)
-            ms2 = time_calls([forced], 2, reps)
-            row["grouped_gemm_us_per_call"] = round(ms2 * 1e3, 2)
+        def timed(layer):
+            ws = moe.Workspace()
+            return time_calls([lambda: moe.moe_layer(layer, x, out=out, ws=ws)] * 10, 2, reps, graph=True)
+        row = {"T": T, "us_per_call": round(timed(L) * 1e3, 2)}
+        row["tokens_per_s"] = round(T / (row["us_per_call"] / 1e6), 1)
+        if T <= 8:
+            row["decode_kernels_us"] = round(timed(Ld) * 1e3, 2)
+            row["grouped_gemm_us"] = round(timed(Lg) * 1e3, 2)
         rows.append(row)
         log("T=%d: %s" % (T, row))
     return rows
@@ -391,8 +389,8 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
     if args.sweep_tokens:
-        print(json.dumps({"sweep": "moe_layer time per call vs tokens per call", "layer": "prefill8k shape",
-                          "rows": sweep_tokens()}), flush=True)
+        print(json.dumps({"sweep": "moe_layer time per call vs tokens per call (HIP graph replays)",
+                          "layer": "prefill8k shape", "rows": sweep_tokens()}), flush=True)
         return
 
     others = {}

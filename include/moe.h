@@ -69,6 +69,7 @@
  *   Outputs Y, y_pairs, y_sorted, y_shared are fp32 with rows of H.
  *
  * Shape limits (MOE_ERR_INVALID_ARG otherwise): T >= 1; 1 <= k <= min(E, 16); E <= 1024;
+ * 0 <= decode_max_tokens <= 8;
  * H, I multiples of 32 and Is = 0 or a multiple of 32; H <= 16384; I, Is <= 4096;
  * pointers to codes, scales, x, outputs and workspace 16-byte aligned.
  */
@@ -82,13 +83,13 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef int32_t moe_status;
 enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1,  /* null pointer, bad shape, misalignment */
-    MOE_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (e.g. T > 4 to decode) */
+    MOE_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement (e.g. T > 8 to decode) */
     MOE_ERR_WORKSPACE = 3,    /* ws_bytes smaller than moe_workspace_size() */
     MOE_ERR_HIP = 4           /* a HIP launch failed */
 };
@@ -120,6 +121,9 @@ typedef struct {
     int32_t top_k;         /* k */
     int32_t shared_inter;  /* Is, 0 = no shared expert */
     moe_qformat fmt;       /* code format of every expert matrix */
+    int32_t decode_max_tokens;  /* moe_layer's regime switch: the decode kernels for T <= this (when
+                                   they fit), the grouped GEMMs above; 0 = the default, 6 (measured
+                                   crossover at H 2048, 256 experts top-8, 4-bit); at most 8 */
 } moe_layer_desc;
 
 typedef struct {
@@ -139,7 +143,7 @@ typedef struct {
  *                  -0.0 and +0.0 being equal
  *   p[t][j]      = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0) over the chosen k (fp32)
  * logits may be NULL (then they live in the workspace). T >= 1. Workspace: MOE_CALL_ROUTE (the logits
- * when logits is NULL and, for T > 4 with few row tiles, the partial sums of the K-split router GEMM,
+ * when logits is NULL and, for T > 8 with few row tiles, the partial sums of the K-split router GEMM,
  * added in a fixed order so that results are deterministic).
  */
 moe_status moe_route(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x, int32_t T,
@@ -160,7 +164,8 @@ moe_status moe_permute(const moe_layer_desc* desc, const int32_t* ids, int32_t T
                        int32_t* inv, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Expert FFNs for a decode step of 1 <= T <= 4 tokens: the selected experts run on the GPU and a
+ * Expert FFNs for a decode step of 1 <= T <= 8 tokens with T k <= 64 pairs (e.g. one token, or a
+ * verify pass of a token and its drafts): the selected experts run on the GPU and a
  * token costs the bytes of the experts it reads (648news 07-nano-cuda-moe-qwen38-release, section
  * "asynchronous CPU/GPU compute"; 648news 10-cyber-on-strata-moe-local-inference, section "bitwise
  * validation and speed bottleneck"). Each distinct chosen expert's weights are read once for all
@@ -172,7 +177,7 @@ moe_status moe_permute(const moe_layer_desc* desc, const int32_t* ids, int32_t T
  * hi + lo pair (about 22 bits). Workspace: MOE_CALL_EXPERTS_DECODE.
  * The kernels keep every chosen pair's SwiGLU activations in LDS (160 KB per workgroup):
  * 4 (T k + T) max(I, Is) bytes plus the routing plan and about 4 E bytes must fit; a shape beyond
- * that (or T > 4) returns MOE_ERR_UNSUPPORTED before anything is enqueued, and so does
+ * that (or T > 8, or T k > 64) returns MOE_ERR_UNSUPPORTED before anything is enqueued, and so does
  * moe_workspace_size(MOE_CALL_EXPERTS_DECODE).
  */
 moe_status moe_experts_decode(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x,
@@ -220,8 +225,8 @@ moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const float* p, co
                        const int32_t* row_of_pair, const float* y_shared, float* out, void* stream);
 
 /*
- * The whole layer: route, permute, experts, combine (the five steps above in one call). T <= 4
- * takes the decode path (three launches: router GEMV; top-k + gate/up; down with the combine
+ * The whole layer: route, permute, experts, combine (the five steps above in one call).
+ * T <= decode_max_tokens (default 6; T k <= 64) takes the decode path (three launches: router GEMV; top-k + gate/up; down with the combine
  * fused) when its LDS fits the shape (see moe_experts_decode), else, like larger T, the prefill
  * path (router GEMM, top-k, permutation, grouped GEMMs, combine); moe_workspace_size sizes the
  * path that is taken. out [T][H] fp32. logits/ids/p are optional outputs (NULL = kept in the

@@ -46,7 +46,8 @@ class _QMat(ctypes.Structure):
 
 class _Desc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("num_experts", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("shared_inter", ctypes.c_int32), ("fmt", ctypes.c_int32)]
+                ("top_k", ctypes.c_int32), ("shared_inter", ctypes.c_int32), ("fmt", ctypes.c_int32),
+                ("decode_max_tokens", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -144,14 +145,16 @@ def _keep(stream, *tensors):
 
 
 class LayerDesc:
-    def __init__(self, hidden: int, inter: int, num_experts: int, top_k: int, shared_inter: int, fmt: int):
+    def __init__(self, hidden: int, inter: int, num_experts: int, top_k: int, shared_inter: int, fmt: int,
+                 decode_max_tokens: int = 0):
         self.hidden, self.inter, self.num_experts = hidden, inter, num_experts
         self.top_k, self.shared_inter, self.fmt = top_k, shared_inter, fmt
-        self.c = _Desc(hidden, inter, num_experts, top_k, shared_inter, fmt)
+        self.decode_max_tokens = decode_max_tokens
+        self.c = _Desc(hidden, inter, num_experts, top_k, shared_inter, fmt, decode_max_tokens)
 
     @classmethod
-    def from_spec(cls, spec) -> "LayerDesc":
-        return cls(spec.H, spec.I, spec.E, spec.k, spec.Is, spec.fmt)
+    def from_spec(cls, spec, decode_max_tokens: int = 0) -> "LayerDesc":
+        return cls(spec.H, spec.I, spec.E, spec.k, spec.Is, spec.fmt, decode_max_tokens)
 
 
 class DeviceLayer:

@@ -10,6 +10,13 @@ using namespace moe;
 namespace {
 
 constexpr int kMaxE = 1024, kMaxK = 16, kMaxH = 16384, kMaxI = 4096, kMaxT = 1 << 20;
+// Router GEMV (weights read once for all tokens) up to this many tokens, the bf16x3 MFMA GEMM above.
+constexpr int kGemvMaxT = 8;
+// moe_layer takes the decode kernels up to this many tokens by default (when they fit the shape):
+// the crossover measured on the 8K-prefill layer shape (H 2048, 256 experts top-8 + shared, 4-bit);
+// moe_layer_desc.decode_max_tokens overrides it (up to 8).
+constexpr int kLayerDecodeMaxT = 6;
+constexpr int kDecodeMaxT = 8;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -21,6 +28,7 @@ moe_status check_desc(const moe_layer_desc* d) {
     if (d->shared_inter < 0 || d->shared_inter > kMaxI || d->shared_inter % 32) return MOE_ERR_INVALID_ARG;
     if (d->num_experts < 1 || d->num_experts > kMaxE) return MOE_ERR_INVALID_ARG;
     if (d->top_k < 1 || d->top_k > kMaxK || d->top_k > d->num_experts) return MOE_ERR_INVALID_ARG;
+    if (d->decode_max_tokens < 0 || d->decode_max_tokens > kDecodeMaxT) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -69,7 +77,7 @@ RouteWs carve_route(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
     Carve c(base);
     RouteWs r;
     r.logits = c.take<float>((size_t)T * d->num_experts);
-    const size_t pb = T > 4 ? router_scratch_bytes(T, d->hidden, d->num_experts) : 0;
+    const size_t pb = T > kGemvMaxT ? router_scratch_bytes(T, d->hidden, d->num_experts) : 0;
     r.part = pb ? c.take<float>(pb / sizeof(float)) : nullptr;
     if (bytes) *bytes = c.bytes();
     return r;
@@ -102,9 +110,13 @@ PrefillWs carve_prefill_ws(const moe_layer_desc* d, int T, void* base, size_t* b
     return r;
 }
 
-// moe_layer's regime: the decode kernels for 1 <= T <= 4 when they fit the shape (their LDS holds
-// every chosen pair's activations), the grouped-GEMM path otherwise.
-bool layer_uses_decode(const moe_layer_desc* d, int T) { return T <= 4 && decode_fits(shape_view(d), T, true); }
+// moe_layer's regime: the decode kernels for 1 <= T <= kLayerDecodeMaxT when they fit the shape (T k
+// <= 64 pairs, and their LDS holds x and every chosen pair's activations), the grouped-GEMM path
+// otherwise.
+bool layer_uses_decode(const moe_layer_desc* d, int T) {
+    const int tmax = d->decode_max_tokens > 0 ? d->decode_max_tokens : kLayerDecodeMaxT;
+    return T <= tmax && decode_fits(shape_view(d), T, true);
+}
 
 struct LayerWs {
     float* logits;
@@ -211,7 +223,7 @@ moe_status moe_workspace_size(const moe_layer_desc* d, int32_t T, moe_call call,
         case MOE_CALL_ROUTE: carve_route(d, T, nullptr, &b); break;
         case MOE_CALL_PERMUTE: carve_perm(d, T, nullptr, &b); break;
         case MOE_CALL_EXPERTS_DECODE:
-            if (T > 4 || !decode_fits(shape_view(d), T, false)) return MOE_ERR_UNSUPPORTED;
+            if (!decode_fits(shape_view(d), T, false)) return MOE_ERR_UNSUPPORTED;
             carve_decode(d, T, nullptr, &b);
             break;
         case MOE_CALL_EXPERTS_PREFILL:
@@ -236,12 +248,12 @@ moe_status moe_route(const moe_layer_desc* d, const moe_layer_weights* w, const 
     if (logits && ((uintptr_t)logits & 3u)) return MOE_ERR_INVALID_ARG;
     size_t need = 0;
     carve_route(d, T, nullptr, &need);
-    const bool split = T > 4 && router_scratch_bytes(T, d->hidden, d->num_experts) > 0;
+    const bool split = T > kGemvMaxT && router_scratch_bytes(T, d->hidden, d->num_experts) > 0;
     if (!logits || split) MOE_TRY(check_ws(ws, ws_bytes, need));
     const RouteWs rw = (!logits || split) ? carve_route(d, T, ws, nullptr) : RouteWs{nullptr, nullptr};
     float* lg = logits ? logits : rw.logits;
     hipStream_t s = (hipStream_t)stream;
-    if (T > 4)
+    if (T > kGemvMaxT)
         return launch_route_topk(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, d->top_k, lg, ids, p,
                                  rw.part, s);
     MOE_TRY(launch_route_gemv(w->w_router, w->router_bias, x, T, d->hidden, d->num_experts, lg, s));
@@ -265,7 +277,7 @@ moe_status moe_experts_decode(const moe_layer_desc* d, const moe_layer_weights* 
                               void* stream) {
     MOE_TRY(check_desc(d));
     MOE_TRY(check_T(T));
-    if (T > 4 || !decode_fits(shape_view(d), T, false)) return MOE_ERR_UNSUPPORTED;
+    if (!decode_fits(shape_view(d), T, false)) return MOE_ERR_UNSUPPORTED;
     MOE_TRY(check_expert_weights(d, w));
     if (!x || !aligned16(x) || !ids || !y_pairs || !aligned16(y_pairs)) return MOE_ERR_INVALID_ARG;
     if (d->shared_inter > 0 && (!y_shared || !aligned16(y_shared))) return MOE_ERR_INVALID_ARG;

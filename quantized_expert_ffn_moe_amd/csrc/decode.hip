@@ -1,4 +1,5 @@
-// Decode regime (1 <= T <= 4 tokens): router + top-k, then the chosen experts' FFNs streamed from HBM.
+// Decode regime (1 <= T <= 8 tokens, T k <= 64 pairs): router + top-k, then the chosen experts' FFNs streamed
+// from HBM.
 //
 // Decode on the pages runs the selected experts' weights on the GPU and prices each token by the
 // expert bytes it reads (648news 07-nano-cuda-moe-qwen38-release, section "asynchronous CPU/GPU
@@ -35,14 +36,15 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 // ----------------------------------------------------------------------------------- routing plan
 
-// Union of the chosen experts of T <= 4 tokens (T*k <= 64 pairs), built in LDS by a whole block.
+// Union of the chosen experts of T <= 8 tokens (T*k <= 64 pairs), built in LDS by a whole block.
+constexpr int kMaxDecodeT = 8;
 struct DecodePlan {
-    int nU;                  // distinct routed experts
-    int expert[64];          // slot -> expert id, slots in order of first appearance
-    uint32_t tokmask[64];    // slot -> bitmask of the tokens that chose it
-    int pair_of[64][4];      // slot, token -> pair q = t*k + j, or -1
-    float pw[64][4];         // slot, token -> routing probability of that pair (0 if none)
-    int xexp[4];             // token -> e_t of its activation scale 2^e_t (token_exp_from_bits)
+    int nU;                            // distinct routed experts
+    int expert[64];                    // slot -> expert id, slots in order of first appearance
+    uint32_t tokmask[64];              // slot -> bitmask of the tokens that chose it
+    int pair_of[64][kMaxDecodeT];      // slot, token -> pair q = t*k + j, or -1
+    float pw[64][kMaxDecodeT];         // slot, token -> routing probability of that pair (0 if none)
+    int xexp[kMaxDecodeT];             // token -> e_t of its activation scale 2^e_t (token_exp_from_bits)
 };
 
 // Built by one wave (lane q = pair q = t*k + j; T*k <= 64), LDS only, no block barrier: the caller
@@ -64,7 +66,7 @@ __device__ void build_plan_wave(const int32_t* __restrict__ ids, const float* __
     for (int i = lane; i < E; i += kWave) first[i] = 64;
     P.tokmask[lane] = 0u;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) { P.pair_of[lane][t] = -1; P.pw[lane][t] = 0.f; }
+    for (int t = 0; t < kMaxDecodeT; ++t) { P.pair_of[lane][t] = -1; P.pw[lane][t] = 0.f; }
     wave_lds_sync();
     const bool valid = q < npairs && e >= 0 && e < E;
     if (valid) atomicMin(&first[e], q);
@@ -323,9 +325,10 @@ __device__ __forceinline__ void bf16x32_to_f32(const uint4 (&raw)[4], float (&v)
 // Gate/up rows per K2 wave and waves per K2 block: 2 rows and up to 16 waves (128 VGPRs); for three
 // or four tokens 3 rows and up to 12 waves (168 VGPRs, so that the 8-bit codes of 3 rows and 4
 // tokens' sums stay in registers), i.e. 9216 rows per pass over 256 CUs: the union of the chosen
-// experts (about 16 + the shared one, 8704 rows) then takes one pass instead of two.
-__host__ __device__ constexpr int gateup_rows(int T) { return T >= 3 ? 3 : 2; }
-__host__ __device__ constexpr int gateup_max_waves(int T) { return T >= 3 ? 12 : 16; }
+// experts (about 16 + the shared one, 8704 rows) then takes one pass instead of two; for five to
+// eight tokens 2 rows and up to 8 waves (256 VGPRs: the sums of 8 tokens stay in registers).
+__host__ __device__ constexpr int gateup_rows(int T) { return T >= 5 ? 2 : T >= 3 ? 3 : 2; }
+__host__ __device__ constexpr int gateup_max_waves(int T) { return T >= 5 ? 8 : T >= 3 ? 12 : 16; }
 constexpr int kDownRows = 1;      // output rows per K3 wave
 constexpr int kDownWaves = 8;     // waves per K3 block (two per SIMD hide each other's latency)
 constexpr int kDownThreads = kDownWaves * kWave;
@@ -789,6 +792,10 @@ moe_status launch_route_gemv(const float* w_r, const float* bias, const uint16_t
         case 2: hipLaunchKernelGGL(k_route_gemv<2>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
         case 3: hipLaunchKernelGGL(k_route_gemv<3>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
         case 4: hipLaunchKernelGGL(k_route_gemv<4>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 5: hipLaunchKernelGGL(k_route_gemv<5>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 6: hipLaunchKernelGGL(k_route_gemv<6>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 7: hipLaunchKernelGGL(k_route_gemv<7>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 8: hipLaunchKernelGGL(k_route_gemv<8>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
         default: return MOE_ERR_UNSUPPORTED;
     }
     MOE_LAUNCH_CHECK();
@@ -839,7 +846,8 @@ static DownFit down_fit(const LayerView& L, int T, bool combine) {
 }
 
 bool decode_fits(const LayerView& L, int T, bool combine) {
-    return T >= 1 && T <= 4 && gateup_smem_bytes(T, L.H, L.E) <= kMaxLds && down_fit(L, T, combine).ok;
+    return T >= 1 && T <= kMaxDecodeT && T * L.k <= 64 && gateup_smem_bytes(T, L.H, L.E) <= kMaxLds &&
+           down_fit(L, T, combine).ok;
 }
 
 // Kernels asking for more than 64 KB of dynamic LDS must say so (gfx950 has 160 KB per workgroup).
@@ -876,7 +884,9 @@ static moe_status launch_gateup(const LayerView& L, const uint16_t* x, const flo
     // waves per block chosen so that the blocks spread evenly over the CUs (4..16 waves), and at
     // most one block per CU: the waves stride over the rows of the experts actually chosen
     const int cus = cu_count();
-    const int64_t wpb = std::min<int64_t>(gateup_max_waves(T), std::max<int64_t>(4, (waves1 + cus - 1) / cus));
+    // (with routing, every token's top-k needs a wave of its own: at least T waves)
+    const int64_t wpb = std::max<int64_t>(ROUTE ? T : 1, std::min<int64_t>(gateup_max_waves(T),
+                                                                          std::max<int64_t>(4, (waves1 + cus - 1) / cus)));
     const int64_t blocks = std::min<int64_t>((waves1 + wpb - 1) / wpb, cus);
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3((unsigned)(wpb * kWave)), sm, s, L, x, logits, ids, p, h,
                        plan_g);
@@ -921,6 +931,10 @@ static moe_status launch_experts_f(const LayerView& L, const uint16_t* x, int T,
         case 2: return launch_experts_t<FMT, 2>(L, x, logits, ids, p, h, out, y_pairs, y_shared, s);
         case 3: return launch_experts_t<FMT, 3>(L, x, logits, ids, p, h, out, y_pairs, y_shared, s);
         case 4: return launch_experts_t<FMT, 4>(L, x, logits, ids, p, h, out, y_pairs, y_shared, s);
+        case 5: return launch_experts_t<FMT, 5>(L, x, logits, ids, p, h, out, y_pairs, y_shared, s);
+        case 6: return launch_experts_t<FMT, 6>(L, x, logits, ids, p, h, out, y_pairs, y_shared, s);
+        case 7: return launch_experts_t<FMT, 7>(L, x, logits, ids, p, h, out, y_pairs, y_shared, s);
+        case 8: return launch_experts_t<FMT, 8>(L, x, logits, ids, p, h, out, y_pairs, y_shared, s);
         default: return MOE_ERR_UNSUPPORTED;
     }
 }

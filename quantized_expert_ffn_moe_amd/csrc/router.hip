@@ -147,7 +147,15 @@ __global__ __launch_bounds__(256) void k_router_reduce(const float* __restrict__
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)T * E) return;
     float acc = 0.f;
-    for (int sp = 0; sp < splits; ++sp) acc += part[(int64_t)sp * T * E + i];
+    const int64_t stride = (int64_t)T * E;
+    for (int sp0 = 0; sp0 < splits; sp0 += 4) {   // four loads in flight, added in split order
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = part[min(sp0 + j, splits - 1) * stride + i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (sp0 + j < splits) acc += v[j];
+    }
     logits[i] = acc + (bias ? bias[i % E] : 0.f);
 }
 
@@ -183,10 +191,22 @@ __global__ __launch_bounds__(256) void k_router_reduce_topk(const float* __restr
 #pragma unroll
     for (int i = 0; i < KPL; ++i) lv[i] = 0.f;
     const int64_t stride = (int64_t)T * E;
-    for (int sp = 0; sp < splits; ++sp) {
-        const float* ps = part + sp * stride + (int64_t)t * E;
+    // four splits' loads in flight at a time (clamped, so they are unconditional), added in split
+    // order (the same sums as one split at a time)
+    for (int sp0 = 0; sp0 < splits; sp0 += 4) {
+        float v[4][KPL];
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) lv[i] += ps[min(lane + kWave * i, E - 1)];
+        for (int j = 0; j < 4; ++j) {
+            const float* ps = part + min(sp0 + j, splits - 1) * stride + (int64_t)t * E;
+#pragma unroll
+            for (int i = 0; i < KPL; ++i) v[j][i] = ps[min(lane + kWave * i, E - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (sp0 + j < splits) {
+#pragma unroll
+                for (int i = 0; i < KPL; ++i) lv[i] += v[j][i];
+            }
     }
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {

@@ -33,12 +33,12 @@ def test_exports_every_declared_symbol():
     L = ctypes.CDLL(moe.library_path)
     for n in names:
         assert hasattr(L, n), n
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     assert moe.moe_status_string(moe.MOE_ERR_WORKSPACE) == "workspace too small"
 
 
-def D(H=2048, I=512, E=256, k=8, Is=512, fmt=moe.MOE_Q4_B32):
-    return moe.LayerDesc(H, I, E, k, Is, fmt)
+def D(H=2048, I=512, E=256, k=8, Is=512, fmt=moe.MOE_Q4_B32, dmt=0):
+    return moe.LayerDesc(H, I, E, k, Is, fmt, dmt)
 
 
 def test_workspace_sizes():
@@ -48,19 +48,31 @@ def test_workspace_sizes():
         assert n >= 0
     assert moe.moe_workspace_size(d, 8192, moe.MOE_CALL_LAYER) > 8192 * 8 * 2048 * 2   # holds fp16 y_sorted
     assert moe.moe_workspace_size(d, 4, moe.MOE_CALL_COMBINE) == 0
-    with pytest.raises(moe.MoeError) as e:
-        moe.moe_workspace_size(d, 5, moe.MOE_CALL_EXPERTS_DECODE)
-    assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+    assert moe.moe_workspace_size(d, 8, moe.MOE_CALL_EXPERTS_DECODE) > 0      # up to 8 tokens (T k <= 64)
+    for T, dd in ((9, d), (5, D(k=16, E=256))):                                # T > 8, or T k > 64
+        with pytest.raises(moe.MoeError) as e:
+            moe.moe_workspace_size(dd, T, moe.MOE_CALL_EXPERTS_DECODE)
+        assert e.value.status == moe.MOE_ERR_UNSUPPORTED
     # the prefill tiles take any H, I, Is that are multiples of 32
     assert moe.moe_workspace_size(D(H=96, I=32, Is=32), 8, moe.MOE_CALL_EXPERTS_PREFILL) > 0
 
 
 @pytest.mark.parametrize("bad", [dict(k=0), dict(k=17, E=32), dict(k=9, E=8), dict(E=1025), dict(H=100),
-                                 dict(I=0), dict(Is=48 + 1), dict(fmt=3), dict(H=32768)])
+                                 dict(I=0), dict(Is=48 + 1), dict(fmt=3), dict(H=32768), dict(dmt=9),
+                                 dict(dmt=-1)])
 def test_bad_descriptors(bad):
     with pytest.raises(moe.MoeError) as e:
         moe.moe_workspace_size(D(**bad), 1, moe.MOE_CALL_LAYER)
     assert e.value.status == moe.MOE_ERR_INVALID_ARG
+
+
+def test_layer_regime_switch_sizes_the_workspace():
+    """decode_max_tokens moves moe_layer's regime switch; the layer workspace follows the path taken
+    (the grouped-GEMM path holds fp16 expert rows, the decode path does not)."""
+    dec, gemm = D(dmt=8), D(dmt=1)
+    assert moe.moe_workspace_size(dec, 8, moe.MOE_CALL_LAYER) < 8 * 8 * 2048 * 2
+    assert moe.moe_workspace_size(gemm, 8, moe.MOE_CALL_LAYER) > 8 * 8 * 2048 * 2
+    assert moe.moe_workspace_size(D(), 6, moe.MOE_CALL_LAYER) < moe.moe_workspace_size(D(), 7, moe.MOE_CALL_LAYER)
 
 
 def _raw(fn, *args):
@@ -86,8 +98,8 @@ def test_host_validation_rejects_before_launch():
     # missing workspace
     assert _raw("moe_layer", ref(d.c), ref(w), fake, 1, fake, None, None, None, None, 0, None) == \
         moe.MOE_ERR_INVALID_ARG
-    # decode entry with T > 4
-    assert _raw("moe_experts_decode", ref(d.c), ref(w), fake, 5, fake, fake, fake, fake, 1 << 40, None) == \
+    # decode entry with T > 8
+    assert _raw("moe_experts_decode", ref(d.c), ref(w), fake, 9, fake, fake, fake, fake, 1 << 40, None) == \
         moe.MOE_ERR_UNSUPPORTED
     # null router weights for route
     w2 = moe._Weights(None, None, w.gate, w.up, w.down, w.sh_gate, w.sh_up, w.sh_down)

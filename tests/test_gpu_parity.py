@@ -131,6 +131,25 @@ def test_stack48_layer(layer):
     assert_float_match(Y, ref["Y"], "Y")
 
 
+def test_decode_eight_tokens_full_plan():
+    """Eight tokens with top-8 on the decode1 shape: all 64 pairs of the routing plan, through
+    moe_layer (decode kernels) and moe_experts_decode."""
+    _need_gpu()
+    spec = synth.CONFIGS["decode1"].with_(name="dec8", T=8, cfg_id=99)
+    d = synth.make_layer(spec)
+    say("decode T=8 k=8 (64 pairs)")
+    O = orc_layer(spec, d)
+    g_logits, g_ids, g_p, Y = run_layer(spec, d)
+    check_routing(O, d["x"], g_logits, g_ids, g_p)
+    ref = oracle_tokens(O, d["x"], g_logits, range(spec.T))
+    assert_float_match(Y, ref["Y"], "Y")
+    L = dev_layer(spec, d)
+    y_pairs, y_sh = moe.moe_experts_decode(L, dev_x(d["x"]), torch.from_numpy(g_ids).cuda())
+    torch.cuda.synchronize()
+    assert_float_match(y_pairs.cpu().numpy().reshape(8, spec.k, spec.H), ref["y_pairs"], "y_pairs")
+    assert_float_match(y_sh.cpu().numpy(), ref["y_shared"], "y_shared")
+
+
 def test_layer_decode_lds_fallback():
     """T = 4, k = 8, I = 1536: the 36 pairs' activations (221 KB) exceed the decode kernels' LDS, so
     moe_layer takes the grouped-GEMM path; it still meets the rule against the oracle, and
@@ -195,9 +214,9 @@ def test_golden_examples_on_gpu():
 
 # ------------------------------------------------------------------------- router accuracy
 
-@pytest.mark.parametrize("T,E", [(3, 256), (300, 200), (1000, 512)])
+@pytest.mark.parametrize("T,E", [(3, 256), (8, 256), (300, 200), (1000, 512)])
 def test_router_fp32_error_bound(T, E):
-    """Router logits (GEMV for T <= 4, bf16x3 MFMA GEMM above) stay within the worst-case fp32
+    """Router logits (GEMV for T <= 8, bf16x3 MFMA GEMM above) stay within the worst-case fp32
     summation bound of the oracle's fp64 logits: |err| <= 3H * 2^-24 * sum_h |x_h w_h| + 2^-24 |b|
     (3H additions: three bf16 terms per weight on the matrix-core path)."""
     _need_gpu()
@@ -219,7 +238,7 @@ def test_router_fp32_error_bound(T, E):
     assert np.all(err <= bound), "max err/bound %.3f" % float(np.max(err / bound))
 
 
-@pytest.mark.parametrize("T,H,mbits", [(3, 96, 17), (300, 96, 17), (40, 256, 16)])
+@pytest.mark.parametrize("T,H,mbits", [(3, 96, 17), (7, 96, 17), (300, 96, 17), (40, 256, 16)])
 def test_router_exact_on_representable_sums(T, H, mbits):
     """Inputs whose every partial sum is exact in fp32: x in {-1, 0, 1}, w = m * 2^-mbits with m in
     [2^(mbits-1), 2^mbits), H * 2^mbits <= 2^24 (17 bits at H = 96: all three bf16 terms of the
@@ -768,10 +787,10 @@ def test_error_statuses_on_gpu():
     _need_gpu()
     spec, d = host_layer("tiny")
     L = dev_layer(spec, d)
-    x5 = dev_x(np.zeros((5, spec.H), np.uint16))
-    ids = torch.zeros((5, spec.k), dtype=torch.int32, device="cuda")
+    x9 = dev_x(np.zeros((9, spec.H), np.uint16))
+    ids = torch.zeros((9, spec.k), dtype=torch.int32, device="cuda")
     with pytest.raises(moe.MoeError) as e:
-        moe.moe_experts_decode(L, x5, ids)
+        moe.moe_experts_decode(L, x9, ids)
     assert e.value.status == moe.MOE_ERR_UNSUPPORTED
     tiny_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(moe.MoeError) as e:

@@ -7,7 +7,7 @@ rms(oracle)) whatever the size of the activations: tokens of rms 1e-6 ... 1e4, t
 values beyond the fp16 range (|x| >= 65504), and all-zero tokens (output exactly 0). The oracle is
 fp64 throughout, so it needs no such care.
 
-The decode kernels are instantiated per format and token count (T = 1 .. 4); every one of the 12
+The decode kernels are instantiated per format and token count (T = 1 .. 8); every one of the 24
 runs here through moe_layer (top-k inside the gate/up kernel) and moe_experts_decode (ids given),
 with and without a shared expert, and with E in (64, 128] (two router keys per lane in the top-k).
 """
@@ -83,7 +83,7 @@ def check_y(got, want, what):
 
 
 @pytest.mark.parametrize("fmt", [synth.Q8, synth.Q4, synth.Q2])
-@pytest.mark.parametrize("T", [1, 2, 3, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_decode_matrix_and_ranges(fmt, T):
     _need_gpu()
     E = 100 if T % 2 else 16           # E in (64, 128]: two keys per lane in the top-k
