@@ -1,7 +1,8 @@
 """Build ``libmoe.so`` (the C-ABI library of include/moe.h) for gfx950 with hipcc, in-tree.
 
 Every .hip file under csrc/ is compiled to an object (in parallel) and linked into one shared
-library next to this file. Packed fp32 instructions are disabled for device code.
+library next to this file. Packed fp32 instructions are disabled for device code. The measurement
+programs under probes/ (not part of the library) are built next to their sources.
 """
 from __future__ import annotations
 
@@ -16,6 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe.so")
+PROBES = os.path.join(HERE, "probes")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -51,6 +53,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    for src in sorted(glob.glob(os.path.join(PROBES, "*.hip"))):
+        exe = src[:-4]
+        r = subprocess.run([HIPCC, *[f for f in FLAGS if f != "-fPIC"], src, "-o", exe + ".tmp"],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stdout + r.stderr))
+        os.replace(exe + ".tmp", exe)
     if verbose:
         print("built", LIB)
     return LIB
