@@ -373,10 +373,19 @@ moe_status moe_layer(const moe_layer_desc* d, const moe_layer_weights* w, const 
     // of the largest stream), at each token's activation scale; the combine sums and unscales them
     // in fp32
     const _Float16* ysh = d->shared_inter > 0 ? lw.y_shared : nullptr;
-    MOE_TRY(launch_route_topk(w->w_router, w->router_bias, x, T, L.H, L.E, L.k, lg, id, pr, lw.router_part, s));
-    MOE_TRY(launch_permute(id, T, L.k, L.E, lw.offsets, lw.perm, lw.inv, lw.chunks, s));
-    MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, PrefillOut::kF16Scaled,
-                                   lw.prefill, s));
+    if (route_small_fits(L, T)) {
+        // small batches: reduction + top-k, permutation, tile list and x conversion in one kernel
+        MOE_TRY(launch_router_partials(w->w_router, w->router_bias, x, T, L.H, L.E, lg, lw.router_part, s));
+        MOE_TRY(launch_route_small(L, x, T, lw.router_part, router_splits(T, L.H, L.E), lg, id, pr, lw.offsets,
+                                   lw.perm, lw.inv, lw.prefill, s));
+        MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, PrefillOut::kF16Scaled,
+                                       lw.prefill, s, true));
+    } else {
+        MOE_TRY(launch_route_topk(w->w_router, w->router_bias, x, T, L.H, L.E, L.k, lg, id, pr, lw.router_part, s));
+        MOE_TRY(launch_permute(id, T, L.k, L.E, lw.offsets, lw.perm, lw.inv, lw.chunks, s));
+        MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, PrefillOut::kF16Scaled,
+                                       lw.prefill, s));
+    }
     return launch_combine_f16(T, L.k, L.H, pr, lw.y_rows, lw.inv, ysh, prefill_token_exps(L, T, lw.prefill), out, s);
 }
 

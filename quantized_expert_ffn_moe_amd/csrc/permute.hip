@@ -14,10 +14,9 @@
 // A pair whose id lies outside [0, E) is dropped: no slot, inv = -1, and offsets[E] counts only
 // the kept pairs. Small batches run all three steps in one block (k_perm_small).
 #include "kernels.h"
+#include "small_batch.h"
 
 namespace moe {
-
-constexpr int kChunk = 64;
 
 int perm_chunks(int T) { return (T + kChunk - 1) / kChunk; }
 size_t perm_scratch_ints(int T, int E) { return (size_t)(perm_chunks(T) + 1) * E; }
@@ -124,78 +123,12 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
 }
 
 // The same three steps in one block of 1024 threads when the per-(expert, chunk) counts and the
-// per-chunk token masks fit in LDS (small batches: one launch instead of three). Wave w takes the
-// chunks w, w + 16, ...; thread e takes expert e in the scan (E <= 1024).
+// per-chunk token masks fit in LDS (small batches: one launch instead of three).
 __global__ __launch_bounds__(1024) void k_perm_small(const int32_t* __restrict__ ids, int T, int k, int E,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                      int32_t* __restrict__ inv) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int nc = (T + kChunk - 1) / kChunk;
-    unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);        // [nc][E]
-    int32_t* cnt = reinterpret_cast<int32_t*>(mask + (size_t)nc * E);             // [E][nc]
-    int32_t* part = cnt + (size_t)E * nc;                                          // [1024]
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    constexpr int kWaves = 1024 / kWave;
-    for (int i = tid; i < E * nc; i += 1024) {
-        cnt[i] = 0;
-        mask[i] = 0ull;
-    }
-    __syncthreads();
-    for (int c = wave; c < nc; c += kWaves) {
-        const int t = c * kChunk + lane;
-        if (t < T)
-            for (int j = 0; j < k; ++j) {
-                const int e = ids[(size_t)t * k + j];
-                if ((unsigned)e < (unsigned)E) {
-                    atomicAdd(&cnt[e * nc + c], 1);
-                    atomicOr(&mask[(size_t)c * E + e], 1ull << lane);
-                }
-            }
-    }
-    __syncthreads();
-    int tot = 0;
-    if (tid < E)
-        for (int c = 0; c < nc; ++c) tot += cnt[tid * nc + c];
-    part[tid] = tot;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-        const int v = tid >= d ? part[tid - d] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    if (tid < E) {
-        int run = part[tid] - tot;
-        offsets[tid] = run;
-        for (int c = 0; c < nc; ++c) {
-            const int v = cnt[tid * nc + c];
-            cnt[tid * nc + c] = run;
-            run += v;
-        }
-    }
-    if (tid == 1023) offsets[E] = part[1023];   // = kept pairs
-    __syncthreads();
-    const unsigned long long below = (1ull << lane) - 1ull;
-    for (int c = wave; c < nc; c += kWaves) {
-        const int t = c * kChunk + lane;
-        if (t >= T) continue;
-        for (int j = 0; j < k; ++j) {
-            const int q = t * k + j;
-            const int e = ids[q];
-            if ((unsigned)e >= (unsigned)E) {
-                inv[q] = -1;
-                continue;
-            }
-            const int pos = cnt[e * nc + c] + __popcll(mask[(size_t)c * E + e] & below);
-            perm[pos] = q;
-            inv[q] = pos;
-        }
-    }
-}
-
-static size_t perm_small_lds(int T, int E) {
-    const size_t nc = (size_t)perm_chunks(T);
-    return nc * E * 8 + nc * E * 4 + 1024 * 4;
+    perm_small_block(ids, T, k, E, offsets, perm, inv, smem, nullptr);
 }
 
 moe_status launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* perm, int32_t* inv,

@@ -30,6 +30,7 @@
 #include <utility>
 
 #include "kernels.h"
+#include "small_batch.h"
 
 namespace moe {
 
@@ -80,20 +81,23 @@ __host__ __device__ inline int rem_tile_ni(int rem) {
     return n <= 1 ? 1 : n <= 2 ? 2 : 4;
 }
 
-// Built by one block of 256 threads (block 0 of k_x_to_f16): thread i takes experts
-// 4 i .. 4 i + 3 (E <= 1024).
+// Built by one block of NT threads (block 0 of k_x_to_f16, 256 threads, or of k_route_small, 1024):
+// thread i takes experts EPT i .. EPT i + EPT - 1, EPT = 1024 / NT (E <= 1024). offsets may be
+// global or LDS.
 constexpr int kTileThreads = 256;
-__device__ __forceinline__ void build_tiles_block(const int32_t* __restrict__ offsets, int E, int T, int k,
+template <int NT>
+__device__ __forceinline__ void build_tiles_block(const int32_t* offsets, int E, int T, int k,
                                                   int has_shared, int tiles_max, TileDesc* __restrict__ tiles,
                                                   int32_t* __restrict__ ntiles) {
+    constexpr int EPT = 1024 / NT;
     __shared__ int part[1024];   // inclusive prefix of the tile counts of experts 0 .. e
     __shared__ int cnt[1025];    // rows of each group (the shared group last)
-    __shared__ int wsum[kTileThreads / kWave];
+    __shared__ int wsum[NT / kWave];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    int nt4[4], sum = 0;
+    int nt4[EPT], sum = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = 4 * tid + q;
+    for (int q = 0; q < EPT; ++q) {
+        const int e = EPT * tid + q;
         int base = 0, n = 0;
         if (e < E) group_rows(offsets, E, T, T * k, e, base, n);
         cnt[e] = n;
@@ -113,16 +117,16 @@ __device__ __forceinline__ void build_tiles_block(const int32_t* __restrict__ of
     int run = incl - sum;
     for (int w = 0; w < wave; ++w) run += wsum[w];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < EPT; ++q) {
         run += nt4[q];
-        part[4 * tid + q] = run;
+        part[EPT * tid + q] = run;
     }
     __syncthreads();
     const int routed = part[1023];
     const int total = min(routed + (cnt[1024] + kTM - 1) / kTM, tiles_max);
     // every thread writes tiles: slot i of the routed list belongs to the first group whose
     // inclusive prefix exceeds i (binary search), the rest to the shared group
-    for (int i = tid; i < total; i += kTileThreads) {
+    for (int i = tid; i < total; i += NT) {
         int g, first;
         if (i < routed) {
             int lo = 0, hi = 1023;
@@ -167,19 +171,13 @@ __host__ __device__ inline int kperm(int e, int G) {
 // Pieces beyond the first two of a thread (rows longer than 512 VPT) are read again from L2.
 // Block 0 builds the tile list instead (the two do not depend on each other; the first block is
 // dispatched first, so the longer tile build overlaps the conversion).
-template <int G, int VPT>
-__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, int T, int H, _Float16* __restrict__ x16,
-                                                  int32_t* __restrict__ xexp, const int32_t* __restrict__ offsets,
-                                                  int E, int k, int has_shared, int tiles_max,
-                                                  TileDesc* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+// One token's row by a block of NT threads (only the first H / VPT of them hold a piece).
+template <int G, int VPT, int NT>
+__device__ __forceinline__ void x_token_to_f16(const uint16_t* __restrict__ x, int t, int H, _Float16* __restrict__ x16,
+                                               int32_t* __restrict__ xexp) {
     static_assert(VPT % G == 0 && VPT % 8 == 0, "a piece holds whole permutation groups");
     constexpr int NV = VPT / 8;   // 16-byte vectors per piece
-    if (blockIdx.x == 0) {
-        build_tiles_block(offsets, E, T, k, has_shared, tiles_max, tiles, ntiles);
-        return;
-    }
-    __shared__ uint32_t wmax[kTileThreads / kWave];
-    const int t = (int)blockIdx.x - 1;
+    __shared__ uint32_t wmax[NT / kWave];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int np = H / VPT;
     const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
@@ -195,10 +193,10 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
     };
     u32x4 k0[NV], k1[NV];
     load(min(tid, np - 1), k0);
-    load(min(tid + kTileThreads, np - 1), k1);
+    load(min(tid + NT, np - 1), k1);
     uint32_t m = tid < np ? absmax(k0) : 0u;
-    if (tid + kTileThreads < np) m = max(m, absmax(k1));
-    for (int c = tid + 2 * kTileThreads; c < np; c += kTileThreads) {
+    if (tid + NT < np) m = max(m, absmax(k1));
+    for (int c = tid + 2 * NT; c < np; c += NT) {
         u32x4 r[NV];
         load(c, r);
         m = max(m, absmax(r));
@@ -206,7 +204,8 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
     m = wave_max_u32(m);
     if (lane == 0) wmax[wave] = m;
     __syncthreads();
-    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) m = max(m, wmax[w]);
     const int e = token_exp_from_bits(m);
     if (tid == 0) xexp[t] = e;
     const float sc = pow2f(e);
@@ -228,12 +227,76 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
         }
     };
     if (tid < np) convert(k0, tid);
-    if (tid + kTileThreads < np) convert(k1, tid + kTileThreads);
-    for (int c = tid + 2 * kTileThreads; c < np; c += kTileThreads) {
+    if (tid + NT < np) convert(k1, tid + NT);
+    for (int c = tid + 2 * NT; c < np; c += NT) {
         u32x4 r[NV];
         load(c, r);
         convert(r, c);
     }
+}
+
+template <int G, int VPT>
+__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, int T, int H, _Float16* __restrict__ x16,
+                                                  int32_t* __restrict__ xexp, const int32_t* __restrict__ offsets,
+                                                  int E, int k, int has_shared, int tiles_max,
+                                                  TileDesc* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+    if (blockIdx.x == 0) {
+        build_tiles_block<kTileThreads>(offsets, E, T, k, has_shared, tiles_max, tiles, ntiles);
+        return;
+    }
+    x_token_to_f16<G, VPT, kTileThreads>(x, (int)blockIdx.x - 1, H, x16, xexp);
+}
+
+// -------------------------------------------------------------------------------- small batches
+// The routing front end of a small batch as one kernel of 1024-thread blocks, in place of the
+// split-K reduction with the top-k, the permutation, and the x conversion with the tile list (three
+// launches, each a dependent step of a few microseconds at these sizes). Block 0: every token's
+// logits (the router GEMM's split-K partial sums added in split order, plus the bias; or its logits
+// when K was not split), top-k and softmax (wave w takes tokens w, w + 16, ...), the permutation of
+// the pairs (the one-block counting sort) and the tile list; blocks 1 .. T: x of one token to fp16
+// at its activation scale (it does not depend on the routing). Same arithmetic and the same
+// outputs as the separate kernels.
+constexpr int kSmallThreads = 1024;
+template <int KPL, int G, int VPT>
+__global__ __launch_bounds__(kSmallThreads) void k_route_small(const float* __restrict__ part, int splits,
+                                                               const float* __restrict__ bias, float* __restrict__ logits,
+                                                               int T, int E, int k, int32_t* __restrict__ ids,
+                                                               float* __restrict__ p, int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                               const uint16_t* __restrict__ x, int H,
+                                                               _Float16* __restrict__ x16, int32_t* __restrict__ xexp,
+                                                               int has_shared, int tiles_max,
+                                                               TileDesc* __restrict__ tiles, int32_t* __restrict__ ntiles) {
+    if (blockIdx.x > 0) {
+        x_token_to_f16<G, VPT, kSmallThreads>(x, (int)blockIdx.x - 1, H, x16, xexp);
+        return;
+    }
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    int32_t* ids_s = reinterpret_cast<int32_t*>(smem);                                    // [T k]
+    int32_t* offs_s = ids_s + align_up((size_t)T * k, 4);                                 // [E + 1]
+    char* perm_lds = reinterpret_cast<char*>(offs_s + align_up((size_t)E + 1, 4));
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    for (int t = wave; t < T; t += kSmallThreads / kWave) {   // uniform per wave
+        float lv[KPL];
+        if (splits > 1) {
+            router_reduce_token<KPL>(part, splits, T, E, t, bias, logits, lv);
+        } else {
+#pragma unroll
+            for (int i = 0; i < KPL; ++i) lv[i] = logits[(int64_t)t * E + min(lane + kWave * i, E - 1)];
+        }
+        int id;
+        float pr;
+        topk_wave_regs<KPL>(lv, E, k, id, pr);
+        if (lane < k) {
+            ids[(size_t)t * k + lane] = id;
+            p[(size_t)t * k + lane] = pr;
+            ids_s[t * k + lane] = id;
+        }
+    }
+    __syncthreads();
+    perm_small_block(ids_s, T, k, E, offsets, perm, inv, perm_lds, offs_s);
+    __syncthreads();
+    build_tiles_block<kSmallThreads>(offs_s, E, T, k, has_shared, tiles_max, tiles, ntiles);
 }
 
 // -------------------------------------------------------------------------------- dequantisation
@@ -887,12 +950,14 @@ const int32_t* prefill_token_exps(const LayerView& L, int T, void* scratch) {
 template <int FMT>
 static moe_status launch_prefill_f(const LayerView& L, const uint16_t* x, int T, const int32_t* offsets,
                                    const int32_t* perm, void* y_sorted, void* y_shared, PrefillOut mode,
-                                   const PrefillScratch& s, hipStream_t st) {
+                                   const PrefillScratch& s, bool prepared, hipStream_t st) {
     constexpr int G = perm_group<FMT>();
     constexpr int VPT = G <= 8 ? 8 : 16;
-    hipLaunchKernelGGL((k_x_to_f16<G, VPT>), dim3((unsigned)(T + 1)), dim3(kTileThreads), 0, st, x, T, L.H, s.x16,
-                       s.xexp, offsets, L.E, L.k, L.Is > 0 ? 1 : 0, max_tiles(T, L.k, L.E), s.tiles, s.ntiles);
-    MOE_LAUNCH_CHECK();
+    if (!prepared) {
+        hipLaunchKernelGGL((k_x_to_f16<G, VPT>), dim3((unsigned)(T + 1)), dim3(kTileThreads), 0, st, x, T, L.H, s.x16,
+                           s.xexp, offsets, L.E, L.k, L.Is > 0 ? 1 : 0, max_tiles(T, L.k, L.E), s.tiles, s.ntiles);
+        MOE_LAUNCH_CHECK();
+    }
     const int mt = max_tiles(T, L.k, L.E);
     const int nt1 = (L.Imax() + 127) / 128;
     const int g1 = ((mt * nt1 + kXcds - 1) / kXcds) * kXcds;
@@ -924,14 +989,62 @@ static moe_status launch_prefill_f(const LayerView& L, const uint16_t* x, int T,
 
 moe_status launch_prefill_experts(const LayerView& L, const uint16_t* x, int T, const int32_t* offsets,
                                   const int32_t* perm, void* y_sorted, void* y_shared, PrefillOut mode, void* scratch,
-                                  hipStream_t st) {
+                                  hipStream_t st, bool prepared) {
     const PrefillScratch s = carve_prefill(L, T, scratch, nullptr);
     switch (L.fmt) {
-        case MOE_Q8_B32: return launch_prefill_f<MOE_Q8_B32>(L, x, T, offsets, perm, y_sorted, y_shared, mode, s, st);
-        case MOE_Q4_B32: return launch_prefill_f<MOE_Q4_B32>(L, x, T, offsets, perm, y_sorted, y_shared, mode, s, st);
-        case MOE_Q2_B32: return launch_prefill_f<MOE_Q2_B32>(L, x, T, offsets, perm, y_sorted, y_shared, mode, s, st);
+        case MOE_Q8_B32: return launch_prefill_f<MOE_Q8_B32>(L, x, T, offsets, perm, y_sorted, y_shared, mode, s, prepared, st);
+        case MOE_Q4_B32: return launch_prefill_f<MOE_Q4_B32>(L, x, T, offsets, perm, y_sorted, y_shared, mode, s, prepared, st);
+        case MOE_Q2_B32: return launch_prefill_f<MOE_Q2_B32>(L, x, T, offsets, perm, y_sorted, y_shared, mode, s, prepared, st);
         default: return MOE_ERR_INVALID_ARG;
     }
+}
+
+static size_t route_small_lds(const LayerView& L, int T) {
+    return align_up((size_t)T * L.k, 4) * 4 + align_up((size_t)L.E + 1, 4) * 4 + perm_small_lds(T, L.E);
+}
+
+bool route_small_fits(const LayerView& L, int T) {
+    return T >= 2 && T <= kSmallMaxT && L.E <= 1024 && route_small_lds(L, T) <= 65536;
+}
+
+template <int KPL, int FMT>
+static moe_status launch_route_small_f(const LayerView& L, const uint16_t* x, int T, const float* part, int splits,
+                                       float* logits, int32_t* ids, float* p, int32_t* offsets, int32_t* perm,
+                                       int32_t* inv, const PrefillScratch& s, hipStream_t st) {
+    constexpr int G = perm_group<FMT>();
+    constexpr int VPT = G <= 8 ? 8 : 16;
+    auto kern = k_route_small<KPL, G, VPT>;
+    const size_t sm = route_small_lds(L, T);
+    if (sm > 65536) return MOE_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(T + 1)), dim3(kSmallThreads), sm, st, part, splits, L.bias, logits, T, L.E,
+                       L.k, ids, p, offsets, perm, inv, x, L.H, s.x16, s.xexp, L.Is > 0 ? 1 : 0,
+                       max_tiles(T, L.k, L.E), s.tiles, s.ntiles);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
+template <int KPL>
+static moe_status launch_route_small_k(const LayerView& L, const uint16_t* x, int T, const float* part, int splits,
+                                       float* logits, int32_t* ids, float* p, int32_t* offsets, int32_t* perm,
+                                       int32_t* inv, const PrefillScratch& s, hipStream_t st) {
+    switch (L.fmt) {
+        case MOE_Q8_B32: return launch_route_small_f<KPL, MOE_Q8_B32>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
+        case MOE_Q4_B32: return launch_route_small_f<KPL, MOE_Q4_B32>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
+        case MOE_Q2_B32: return launch_route_small_f<KPL, MOE_Q2_B32>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
+        default: return MOE_ERR_INVALID_ARG;
+    }
+}
+
+moe_status launch_route_small(const LayerView& L, const uint16_t* x, int T, const float* part, int splits,
+                              float* logits, int32_t* ids, float* p, int32_t* offsets, int32_t* perm, int32_t* inv,
+                              void* scratch, hipStream_t st) {
+    if (!route_small_fits(L, T)) return MOE_ERR_UNSUPPORTED;
+    const PrefillScratch s = carve_prefill(L, T, scratch, nullptr);
+    if (L.E <= 64) return launch_route_small_k<1>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
+    if (L.E <= 128) return launch_route_small_k<2>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
+    if (L.E <= 256) return launch_route_small_k<4>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
+    if (L.E <= 512) return launch_route_small_k<8>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
+    return launch_route_small_k<16>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
 }
 
 }  // namespace moe

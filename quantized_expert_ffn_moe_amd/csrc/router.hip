@@ -6,6 +6,7 @@
 #include <algorithm>
 
 #include "kernels.h"
+#include "small_batch.h"
 
 namespace moe {
 
@@ -188,32 +189,7 @@ __global__ __launch_bounds__(256) void k_router_reduce_topk(const float* __restr
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
     float lv[KPL];
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) lv[i] = 0.f;
-    const int64_t stride = (int64_t)T * E;
-    // four splits' loads in flight at a time (clamped, so they are unconditional), added in split
-    // order (the same sums as one split at a time)
-    for (int sp0 = 0; sp0 < splits; sp0 += 4) {
-        float v[4][KPL];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float* ps = part + min(sp0 + j, splits - 1) * stride + (int64_t)t * E;
-#pragma unroll
-            for (int i = 0; i < KPL; ++i) v[j][i] = ps[min(lane + kWave * i, E - 1)];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (sp0 + j < splits) {
-#pragma unroll
-                for (int i = 0; i < KPL; ++i) lv[i] += v[j][i];
-            }
-    }
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const int e = lane + kWave * i;
-        lv[i] += bias ? bias[min(e, E - 1)] : 0.f;
-        if (e < E) logits[(int64_t)t * E + e] = lv[i];
-    }
+    router_reduce_token<KPL>(part, splits, T, E, t, bias, logits, lv);
     int id;
     float pr;
     topk_wave_regs<KPL>(lv, E, k, id, pr);
@@ -257,6 +233,17 @@ moe_status launch_router(const float* w_r, const float* bias, const uint16_t* x,
     return MOE_OK;
 }
 
+moe_status launch_router_partials(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
+                                  float* logits, float* scratch, hipStream_t s) {
+    const int sp = router_splits(T, H, E);
+    if (sp > 1 && !scratch) return MOE_ERR_WORKSPACE;
+    const int blocks = ((T + kRtM - 1) / kRtM) * ((E + kRtN - 1) / kRtN);
+    const int grid = ((blocks + kRtXcds - 1) / kRtXcds) * kRtXcds;
+    hipLaunchKernelGGL(k_router_mfma, dim3(grid, sp), dim3(256), 0, s, w_r, bias, x, T, H, E, logits, sp, scratch);
+    MOE_LAUNCH_CHECK();
+    return MOE_OK;
+}
+
 moe_status launch_route_topk(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E, int k,
                              float* logits, int32_t* ids, float* p, float* scratch, hipStream_t s) {
     const int sp = router_splits(T, H, E);
@@ -264,11 +251,8 @@ moe_status launch_route_topk(const float* w_r, const float* bias, const uint16_t
         const moe_status st = launch_router(w_r, bias, x, T, H, E, logits, scratch, s);
         return st != MOE_OK ? st : launch_topk(logits, T, E, k, ids, p, s);
     }
-    if (!scratch) return MOE_ERR_WORKSPACE;
-    const int blocks = ((T + kRtM - 1) / kRtM) * ((E + kRtN - 1) / kRtN);
-    const int grid = ((blocks + kRtXcds - 1) / kRtXcds) * kRtXcds;
-    hipLaunchKernelGGL(k_router_mfma, dim3(grid, sp), dim3(256), 0, s, w_r, bias, x, T, H, E, logits, sp, scratch);
-    MOE_LAUNCH_CHECK();
+    const moe_status st = launch_router_partials(w_r, bias, x, T, H, E, logits, scratch, s);
+    if (st != MOE_OK) return st;
     const dim3 g2((T + 3) / 4), b2(256);
     if (E <= 64) hipLaunchKernelGGL(k_router_reduce_topk<1>, g2, b2, 0, s, scratch, sp, T, E, k, bias, logits, ids, p);
     else if (E <= 128) hipLaunchKernelGGL(k_router_reduce_topk<2>, g2, b2, 0, s, scratch, sp, T, E, k, bias, logits, ids, p);

@@ -32,8 +32,8 @@ def say(*a):
     sys.stdout.flush()
 
 
-def dev_layer(spec, d):
-    return moe.DeviceLayer.from_host(moe.LayerDesc.from_spec(spec), d)
+def dev_layer(spec, d, dmt=0):
+    return moe.DeviceLayer.from_host(moe.LayerDesc.from_spec(spec, decode_max_tokens=dmt), d)
 
 
 def dev_x(x):
@@ -44,11 +44,12 @@ def orc_layer(spec, d):
     return oracle.Layer.from_synth(spec, d)
 
 
-def run_layer(spec, d, x=None):
-    """moe_layer on the GPU; returns numpy logits, ids, p, Y."""
+def run_layer(spec, d, x=None, dmt=0):
+    """moe_layer on the GPU; returns numpy logits, ids, p, Y. dmt: decode_max_tokens of the descriptor
+    (0 = the library's default; 1 sends every batch of two or more tokens to the grouped GEMMs)."""
     x = d["x"] if x is None else x
     T = x.shape[0]
-    L = dev_layer(spec, d)
+    L = dev_layer(spec, d, dmt)
     xd = dev_x(x)
     logits = torch.empty((T, spec.E), dtype=torch.float32, device="cuda")
     ids = torch.empty((T, spec.k), dtype=torch.int32, device="cuda")
@@ -273,13 +274,32 @@ def small_prefill_spec(fmt, T, E=16, k=4, Is=64, H=256, I=128, zipf=True):
 @pytest.mark.parametrize("fmt", [synth.Q8, synth.Q4, synth.Q2])
 @pytest.mark.parametrize("T", [5, 130, 300])
 def test_layer_prefill_small(fmt, T):
-    """Prefill path at sizes the oracle finishes in seconds: several row tiles and ragged tails."""
+    """Prefill path at sizes the oracle finishes in seconds: several row tiles and ragged tails (the
+    grouped GEMMs forced at T = 5, which the default switch would send to the decode kernels)."""
     _need_gpu()
     spec = small_prefill_spec(fmt, T)
     d = synth.make_layer(spec)
     say("prefill small", synth.FMT_NAMES[fmt], "T=%d" % T)
     O = orc_layer(spec, d)
-    g_logits, g_ids, g_p, Y = run_layer(spec, d)
+    g_logits, g_ids, g_p, Y = run_layer(spec, d, dmt=1)
+    check_routing(O, d["x"], g_logits, g_ids, g_p)
+    ref = oracle_tokens(O, d["x"], g_logits, range(T))
+    assert_float_match(Y, ref["Y"], "Y")
+
+
+@pytest.mark.parametrize("fmt,T,E,k", [(synth.Q8, 2, 16, 4), (synth.Q4, 7, 100, 8), (synth.Q2, 16, 256, 8),
+                                       (synth.Q4, 16, 500, 10), (synth.Q8, 13, 1000, 16), (synth.Q4, 17, 256, 8)])
+def test_layer_small_batch_front_end(fmt, T, E, k):
+    """Batches of 2 to 16 tokens on the grouped-GEMM path run the split-K reduction, top-k,
+    permutation, tile list and x conversion as one kernel (one block routes while the others convert
+    x), over every keys-per-lane width of the top-k (E = 16 ... 1000); T = 17 takes the separate
+    kernels. ids bit-exact, logits, p and Y against the oracle."""
+    _need_gpu()
+    spec = small_prefill_spec(fmt, T, E=E, k=k, Is=64 if T % 2 else 0, H=512, I=96)
+    d = synth.make_layer(spec)
+    say("small-batch front end", synth.FMT_NAMES[fmt], "T=%d E=%d k=%d" % (T, E, k))
+    O = orc_layer(spec, d)
+    g_logits, g_ids, g_p, Y = run_layer(spec, d, dmt=1)
     check_routing(O, d["x"], g_logits, g_ids, g_p)
     ref = oracle_tokens(O, d["x"], g_logits, range(T))
     assert_float_match(Y, ref["Y"], "Y")
