@@ -332,8 +332,8 @@ __host__ __device__ constexpr int gateup_max_waves(int T) { return T >= 5 ? 8 : 
 constexpr int kDownRows = 1;      // output rows per K3 wave
 constexpr int kDownWaves = 8;     // waves per K3 block (two per SIMD hide each other's latency)
 constexpr int kDownThreads = kDownWaves * kWave;
-// Down items per row whose loads a K3 lane issues together: 4, and 5 for three or four tokens
-// (16 + 1 experts x 16 blocks = 272 items per row then take one batch of loads, not two).
+// Down items per row whose loads a K3 lane issues together: 4, and 5 from three tokens on (16 + 1
+// experts x 16 blocks = 272 items per row of a 4-token batch then take one batch of loads, not two).
 __host__ __device__ constexpr int down_batch(int T) { return T >= 3 ? 5 : 4; }
 
 // LDS of k_dec_gateup: plan | first[E] | ids_s[64] | p_s[64] | xq[T][4][nb] uint4
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
     uint4* xq = reinterpret_cast<uint4*>(smem + lds_head(L.E));
     float* xc = reinterpret_cast<float*>(xq + (size_t)T * 4 * (L.H / 32));   // [T][nb] pair-offset sums
     // one or two tokens: code pairs keep their offsets and each block's dot product drops the
-    // pair-offset sum xc of its activations (one instruction per pair less); three or four tokens
+    // pair-offset sum xc of its activations (one instruction per pair less); three or more tokens
     // subtract per pair (the extra LDS read per token and block costs them more than it saves)
     constexpr bool kSubPairs = T >= 3;   // code_pairs subtracts the offsets itself
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
