@@ -291,10 +291,8 @@ __device__ __forceinline__ void topk_wave_sorted(const float (&lv)[KPL], int E, 
     for (int j = 0; j < k; ++j) {
         const uint32_t vmax = wave_max_u32(key[0]);
         const uint64_t b = __ballot(key[0] == vmax);
-        int win;
-        if (__popcll(b) == 1) {
-            win = __ffsll((unsigned long long)b) - 1;
-        } else {
+        int win = __ffsll((unsigned long long)b) - 1;
+        if (__builtin_expect(__popcll(b) != 1, 0)) {
             const uint32_t mi = wave_min_u32(key[0] == vmax ? (uint32_t)idx[0] : 0xFFFFFFFFu);
             win = (int)(mi % kWave);
         }
