@@ -143,7 +143,7 @@ typedef struct {
  *                  -0.0 and +0.0 being equal
  *   p[t][j]      = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0) over the chosen k (fp32)
  * logits may be NULL (then they live in the workspace). T >= 1. Workspace: MOE_CALL_ROUTE (the logits
- * when logits is NULL and, for T > 8 with few row tiles, the partial sums of the K-split router GEMM,
+ * when logits is NULL and, for T > 16 with few row tiles, the partial sums of the K-split router GEMM,
  * added in a fixed order so that results are deterministic).
  */
 moe_status moe_route(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x, int32_t T,
@@ -226,10 +226,12 @@ moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const float* p, co
 
 /*
  * The whole layer: route, permute, experts, combine (the five steps above in one call).
- * T <= decode_max_tokens (default 6; T k <= 64) takes the decode path (three launches: router GEMV; top-k + gate/up; down with the combine
- * fused) when its LDS fits the shape (see moe_experts_decode), else, like larger T, the prefill
- * path (router GEMM, top-k, permutation, grouped GEMMs, combine); moe_workspace_size sizes the
- * path that is taken. out [T][H] fp32. logits/ids/p are optional outputs (NULL = kept in the
+ * T <= decode_max_tokens (default 5; T k <= 64) takes the decode path (three launches: router
+ * GEMV; top-k + gate/up; down with the combine fused) when its LDS fits the shape (see
+ * moe_experts_decode), else, like larger T, the prefill path (router GEMV up to 16 tokens, GEMM
+ * above; top-k, permutation, grouped GEMMs, combine; from 2 to 16 tokens the top-k, the
+ * permutation and the x conversion run as one kernel); moe_workspace_size sizes the path that is
+ * taken. out [T][H] fp32. logits/ids/p are optional outputs (NULL = kept in the
  * workspace). Workspace: MOE_CALL_LAYER.
  */
 moe_status moe_layer(const moe_layer_desc* desc, const moe_layer_weights* w, const uint16_t* x, int32_t T,

@@ -10,12 +10,12 @@ using namespace moe;
 namespace {
 
 constexpr int kMaxE = 1024, kMaxK = 16, kMaxH = 16384, kMaxI = 4096, kMaxT = 1 << 20;
-// Router GEMV (weights read once for all tokens) up to this many tokens, the bf16x3 MFMA GEMM above.
-constexpr int kGemvMaxT = 8;
+// The router: the GEMV (weights read once for all tokens) up to kGemvMaxT tokens, the bf16x3 MFMA
+// GEMM above.
 // moe_layer takes the decode kernels up to this many tokens by default (when they fit the shape):
 // the crossover measured on the 8K-prefill layer shape (H 2048, 256 experts top-8 + shared, 4-bit);
 // moe_layer_desc.decode_max_tokens overrides it (up to 8).
-constexpr int kLayerDecodeMaxT = 6;
+constexpr int kLayerDecodeMaxT = 5;
 constexpr int kDecodeMaxT = 8;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -146,7 +146,7 @@ LayerWs carve_layer(const moe_layer_desc* d, int T, void* base, size_t* bytes) {
         r.inv = c.take<int32_t>(P);
         r.chunks = c.take<int32_t>(perm_scratch_ints(T, d->num_experts));
         r.prefill = c.take<char>(prefill_scratch_bytes(shape_view(d), T));
-        const size_t pb = router_scratch_bytes(T, d->hidden, d->num_experts);
+        const size_t pb = T > kGemvMaxT ? router_scratch_bytes(T, d->hidden, d->num_experts) : 0;
         r.router_part = pb ? c.take<float>(pb / sizeof(float)) : nullptr;
     }
     if (bytes) *bytes = c.bytes();
@@ -373,15 +373,15 @@ moe_status moe_layer(const moe_layer_desc* d, const moe_layer_weights* w, const 
     // of the largest stream), at each token's activation scale; the combine sums and unscales them
     // in fp32
     const _Float16* ysh = d->shared_inter > 0 ? lw.y_shared : nullptr;
+    if (T <= kGemvMaxT) MOE_TRY(launch_route_gemv(w->w_router, w->router_bias, x, T, L.H, L.E, lg, s));
     if (route_small_fits(L, T)) {
-        // small batches: reduction + top-k, permutation, tile list and x conversion in one kernel
-        MOE_TRY(launch_router_partials(w->w_router, w->router_bias, x, T, L.H, L.E, lg, lw.router_part, s));
-        MOE_TRY(launch_route_small(L, x, T, lw.router_part, router_splits(T, L.H, L.E), lg, id, pr, lw.offsets,
-                                   lw.perm, lw.inv, lw.prefill, s));
+        // small batches: top-k, permutation, tile list and x conversion in one kernel
+        MOE_TRY(launch_route_small(L, x, T, lg, id, pr, lw.offsets, lw.perm, lw.inv, lw.prefill, s));
         MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, PrefillOut::kF16Scaled,
                                        lw.prefill, s, true));
     } else {
-        MOE_TRY(launch_route_topk(w->w_router, w->router_bias, x, T, L.H, L.E, L.k, lg, id, pr, lw.router_part, s));
+        if (T <= kGemvMaxT) MOE_TRY(launch_topk(lg, T, L.E, L.k, id, pr, s));
+        else MOE_TRY(launch_route_topk(w->w_router, w->router_bias, x, T, L.H, L.E, L.k, lg, id, pr, lw.router_part, s));
         MOE_TRY(launch_permute(id, T, L.k, L.E, lw.offsets, lw.perm, lw.inv, lw.chunks, s));
         MOE_TRY(launch_prefill_experts(L, x, T, lw.offsets, lw.perm, lw.y_rows, lw.y_shared, PrefillOut::kF16Scaled,
                                        lw.prefill, s));

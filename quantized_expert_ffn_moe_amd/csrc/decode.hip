@@ -796,6 +796,14 @@ moe_status launch_route_gemv(const float* w_r, const float* bias, const uint16_t
         case 6: hipLaunchKernelGGL(k_route_gemv<6>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
         case 7: hipLaunchKernelGGL(k_route_gemv<7>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
         case 8: hipLaunchKernelGGL(k_route_gemv<8>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 9: hipLaunchKernelGGL(k_route_gemv<9>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 10: hipLaunchKernelGGL(k_route_gemv<10>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 11: hipLaunchKernelGGL(k_route_gemv<11>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 12: hipLaunchKernelGGL(k_route_gemv<12>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 13: hipLaunchKernelGGL(k_route_gemv<13>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 14: hipLaunchKernelGGL(k_route_gemv<14>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 15: hipLaunchKernelGGL(k_route_gemv<15>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
+        case 16: hipLaunchKernelGGL(k_route_gemv<16>, grid, block, 0, s, w_r, bias, x, H, E, logits); break;
         default: return MOE_ERR_UNSUPPORTED;
     }
     MOE_LAUNCH_CHECK();

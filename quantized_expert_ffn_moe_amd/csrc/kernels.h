@@ -17,18 +17,13 @@ struct LayerView {
     __host__ __device__ int Imax() const { return I > Is ? I : Is; }
 };
 
-// router GEMM (any T) and the top-k + softmax kernel (one wave per token)
-// Router GEMM (the layer uses it above the decode regime); scratch of router_scratch_bytes() (split-K
-// partial sums; none when 0).
+// Router GEMM (above kGemvMaxT tokens) and the top-k + softmax kernel (one wave per token); the GEMM's
+// scratch: router_scratch_bytes() (split-K partial sums; none when 0).
 int router_splits(int T, int H, int E);
 size_t router_scratch_bytes(int T, int H, int E);
 moe_status launch_router(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
                          float* logits, float* scratch, hipStream_t s);
 moe_status launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* p, hipStream_t s);
-// The router GEMM alone: with router_splits() > 1 it writes the split-K partial sums to scratch (to
-// be reduced by k_router_reduce_topk or k_route_small), else logits + bias.
-moe_status launch_router_partials(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
-                                  float* logits, float* scratch, hipStream_t s);
 // Router GEMM + top-k; with a split K the reduction and the top-k run as one kernel.
 moe_status launch_route_topk(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E, int k,
                              float* logits, int32_t* ids, float* p, float* scratch, hipStream_t s);
@@ -39,10 +34,12 @@ size_t perm_scratch_ints(int T, int E);
 moe_status launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets, int32_t* perm, int32_t* inv,
                           int32_t* chunk_scratch, hipStream_t s);
 
-// decode (T <= 8): router GEMV; gate/up (given logits, every block runs the top-k and block 0
-// publishes ids/p); down(+combine). h scratch: decode_scratch_floats() floats.
+// Router GEMV, 1 <= T <= kGemvMaxT (W_r read once for every token; fp32 dot products).
+constexpr int kGemvMaxT = 16;
 moe_status launch_route_gemv(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
                              float* logits, hipStream_t s);
+// decode (T <= 8): gate/up (given logits, every block runs the top-k and block 0 publishes ids/p);
+// down(+combine). h scratch: decode_scratch_floats() floats.
 size_t decode_scratch_floats(const LayerView& L, int T);
 // Whether the decode kernels fit this shape (their LDS holds x, the routing plan and the SwiGLU
 // activations of every chosen pair): with the combine fused (combine) or with per-pair outputs.
@@ -61,14 +58,14 @@ enum class PrefillOut { kF32, kF16, kF16Scaled };
 moe_status launch_prefill_experts(const LayerView& L, const uint16_t* x, int T, const int32_t* offsets,
                                   const int32_t* perm, void* y_sorted, void* y_shared, PrefillOut mode,
                                   void* scratch, hipStream_t s, bool prepared = false);
-// Small batches (2 <= T <= kSmallMaxT): after launch_router_partials, one kernel adds the partial
-// sums, runs the top-k, the permutation, the tile list and the x conversion (the prefill scratch
-// then holds what launch_prefill_experts(..., prepared = true) needs).
+// Small batches (2 <= T <= kSmallMaxT): from the router GEMV's logits, one kernel runs the top-k, the
+// permutation, the tile list and the x conversion (the prefill scratch then holds what
+// launch_prefill_experts(..., prepared = true) needs).
 constexpr int kSmallMaxT = 16;
+static_assert(kSmallMaxT <= kGemvMaxT, "small batches take their logits from the router GEMV");
 bool route_small_fits(const LayerView& L, int T);
-moe_status launch_route_small(const LayerView& L, const uint16_t* x, int T, const float* part, int splits,
-                              float* logits, int32_t* ids, float* p, int32_t* offsets, int32_t* perm, int32_t* inv,
-                              void* scratch, hipStream_t s);
+moe_status launch_route_small(const LayerView& L, const uint16_t* x, int T, const float* logits, int32_t* ids,
+                              float* p, int32_t* offsets, int32_t* perm, int32_t* inv, void* scratch, hipStream_t s);
 // e_t of every token, in the scratch of the last launch_prefill_experts on it
 const int32_t* prefill_token_exps(const LayerView& L, int T, void* scratch);
 

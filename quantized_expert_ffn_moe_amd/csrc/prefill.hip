@@ -248,18 +248,15 @@ __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x
 }
 
 // -------------------------------------------------------------------------------- small batches
-// The routing front end of a small batch as one kernel of 1024-thread blocks, in place of the
-// split-K reduction with the top-k, the permutation, and the x conversion with the tile list (three
-// launches, each a dependent step of a few microseconds at these sizes). Block 0: every token's
-// logits (the router GEMM's split-K partial sums added in split order, plus the bias; or its logits
-// when K was not split), top-k and softmax (wave w takes tokens w, w + 16, ...), the permutation of
-// the pairs (the one-block counting sort) and the tile list; blocks 1 .. T: x of one token to fp16
-// at its activation scale (it does not depend on the routing). Same arithmetic and the same
-// outputs as the separate kernels.
+// The routing front end of a small batch as one kernel of 1024-thread blocks, in place of the top-k,
+// the permutation, and the x conversion with the tile list (three launches, each a dependent step of
+// a few microseconds at these sizes). Block 0: every token's top-k and softmax from the router
+// GEMV's logits (wave w takes tokens w, w + 16, ...), the permutation of the pairs (the one-block
+// counting sort) and the tile list; blocks 1 .. T: x of one token to fp16 at its activation scale
+// (it does not depend on the routing). Same arithmetic and the same outputs as the separate kernels.
 constexpr int kSmallThreads = 1024;
 template <int KPL, int G, int VPT>
-__global__ __launch_bounds__(kSmallThreads) void k_route_small(const float* __restrict__ part, int splits,
-                                                               const float* __restrict__ bias, float* __restrict__ logits,
+__global__ __launch_bounds__(kSmallThreads) void k_route_small(const float* __restrict__ logits,
                                                                int T, int E, int k, int32_t* __restrict__ ids,
                                                                float* __restrict__ p, int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ perm, int32_t* __restrict__ inv,
@@ -278,12 +275,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(const float* __re
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     for (int t = wave; t < T; t += kSmallThreads / kWave) {   // uniform per wave
         float lv[KPL];
-        if (splits > 1) {
-            router_reduce_token<KPL>(part, splits, T, E, t, bias, logits, lv);
-        } else {
 #pragma unroll
-            for (int i = 0; i < KPL; ++i) lv[i] = logits[(int64_t)t * E + min(lane + kWave * i, E - 1)];
-        }
+        for (int i = 0; i < KPL; ++i) lv[i] = logits[(int64_t)t * E + min(lane + kWave * i, E - 1)];
         int id;
         float pr;
         topk_wave_regs<KPL>(lv, E, k, id, pr);
@@ -1008,15 +1001,15 @@ bool route_small_fits(const LayerView& L, int T) {
 }
 
 template <int KPL, int FMT>
-static moe_status launch_route_small_f(const LayerView& L, const uint16_t* x, int T, const float* part, int splits,
-                                       float* logits, int32_t* ids, float* p, int32_t* offsets, int32_t* perm,
+static moe_status launch_route_small_f(const LayerView& L, const uint16_t* x, int T, const float* logits,
+                                       int32_t* ids, float* p, int32_t* offsets, int32_t* perm,
                                        int32_t* inv, const PrefillScratch& s, hipStream_t st) {
     constexpr int G = perm_group<FMT>();
     constexpr int VPT = G <= 8 ? 8 : 16;
     auto kern = k_route_small<KPL, G, VPT>;
     const size_t sm = route_small_lds(L, T);
     if (sm > 65536) return MOE_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(T + 1)), dim3(kSmallThreads), sm, st, part, splits, L.bias, logits, T, L.E,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(T + 1)), dim3(kSmallThreads), sm, st, logits, T, L.E,
                        L.k, ids, p, offsets, perm, inv, x, L.H, s.x16, s.xexp, L.Is > 0 ? 1 : 0,
                        max_tiles(T, L.k, L.E), s.tiles, s.ntiles);
     MOE_LAUNCH_CHECK();
@@ -1024,27 +1017,26 @@ static moe_status launch_route_small_f(const LayerView& L, const uint16_t* x, in
 }
 
 template <int KPL>
-static moe_status launch_route_small_k(const LayerView& L, const uint16_t* x, int T, const float* part, int splits,
-                                       float* logits, int32_t* ids, float* p, int32_t* offsets, int32_t* perm,
+static moe_status launch_route_small_k(const LayerView& L, const uint16_t* x, int T, const float* logits,
+                                       int32_t* ids, float* p, int32_t* offsets, int32_t* perm,
                                        int32_t* inv, const PrefillScratch& s, hipStream_t st) {
     switch (L.fmt) {
-        case MOE_Q8_B32: return launch_route_small_f<KPL, MOE_Q8_B32>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
-        case MOE_Q4_B32: return launch_route_small_f<KPL, MOE_Q4_B32>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
-        case MOE_Q2_B32: return launch_route_small_f<KPL, MOE_Q2_B32>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
+        case MOE_Q8_B32: return launch_route_small_f<KPL, MOE_Q8_B32>(L, x, T, logits, ids, p, offsets, perm, inv, s, st);
+        case MOE_Q4_B32: return launch_route_small_f<KPL, MOE_Q4_B32>(L, x, T, logits, ids, p, offsets, perm, inv, s, st);
+        case MOE_Q2_B32: return launch_route_small_f<KPL, MOE_Q2_B32>(L, x, T, logits, ids, p, offsets, perm, inv, s, st);
         default: return MOE_ERR_INVALID_ARG;
     }
 }
 
-moe_status launch_route_small(const LayerView& L, const uint16_t* x, int T, const float* part, int splits,
-                              float* logits, int32_t* ids, float* p, int32_t* offsets, int32_t* perm, int32_t* inv,
-                              void* scratch, hipStream_t st) {
+moe_status launch_route_small(const LayerView& L, const uint16_t* x, int T, const float* logits, int32_t* ids,
+                              float* p, int32_t* offsets, int32_t* perm, int32_t* inv, void* scratch, hipStream_t st) {
     if (!route_small_fits(L, T)) return MOE_ERR_UNSUPPORTED;
     const PrefillScratch s = carve_prefill(L, T, scratch, nullptr);
-    if (L.E <= 64) return launch_route_small_k<1>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
-    if (L.E <= 128) return launch_route_small_k<2>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
-    if (L.E <= 256) return launch_route_small_k<4>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
-    if (L.E <= 512) return launch_route_small_k<8>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
-    return launch_route_small_k<16>(L, x, T, part, splits, logits, ids, p, offsets, perm, inv, s, st);
+    if (L.E <= 64) return launch_route_small_k<1>(L, x, T, logits, ids, p, offsets, perm, inv, s, st);
+    if (L.E <= 128) return launch_route_small_k<2>(L, x, T, logits, ids, p, offsets, perm, inv, s, st);
+    if (L.E <= 256) return launch_route_small_k<4>(L, x, T, logits, ids, p, offsets, perm, inv, s, st);
+    if (L.E <= 512) return launch_route_small_k<8>(L, x, T, logits, ids, p, offsets, perm, inv, s, st);
+    return launch_route_small_k<16>(L, x, T, logits, ids, p, offsets, perm, inv, s, st);
 }
 
 }  // namespace moe

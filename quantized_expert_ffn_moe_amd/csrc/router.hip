@@ -233,8 +233,10 @@ moe_status launch_router(const float* w_r, const float* bias, const uint16_t* x,
     return MOE_OK;
 }
 
-moe_status launch_router_partials(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
-                                  float* logits, float* scratch, hipStream_t s) {
+// The router GEMM alone: with router_splits() > 1 it writes the split-K partial sums to scratch (to
+// be reduced by k_router_reduce_topk), else logits + bias.
+static moe_status launch_router_partials(const float* w_r, const float* bias, const uint16_t* x, int T, int H, int E,
+                                         float* logits, float* scratch, hipStream_t s) {
     const int sp = router_splits(T, H, E);
     if (sp > 1 && !scratch) return MOE_ERR_WORKSPACE;
     const int blocks = ((T + kRtM - 1) / kRtM) * ((E + kRtN - 1) / kRtN);

@@ -140,7 +140,7 @@ def test_decode_eight_tokens_full_plan():
     d = synth.make_layer(spec)
     say("decode T=8 k=8 (64 pairs)")
     O = orc_layer(spec, d)
-    g_logits, g_ids, g_p, Y = run_layer(spec, d)
+    g_logits, g_ids, g_p, Y = run_layer(spec, d, dmt=8)
     check_routing(O, d["x"], g_logits, g_ids, g_p)
     ref = oracle_tokens(O, d["x"], g_logits, range(spec.T))
     assert_float_match(Y, ref["Y"], "Y")
@@ -215,9 +215,9 @@ def test_golden_examples_on_gpu():
 
 # ------------------------------------------------------------------------- router accuracy
 
-@pytest.mark.parametrize("T,E", [(3, 256), (8, 256), (300, 200), (1000, 512)])
+@pytest.mark.parametrize("T,E", [(3, 256), (8, 256), (16, 256), (17, 256), (300, 200), (1000, 512)])
 def test_router_fp32_error_bound(T, E):
-    """Router logits (GEMV for T <= 8, bf16x3 MFMA GEMM above) stay within the worst-case fp32
+    """Router logits (GEMV for T <= 16, bf16x3 MFMA GEMM above) stay within the worst-case fp32
     summation bound of the oracle's fp64 logits: |err| <= 3H * 2^-24 * sum_h |x_h w_h| + 2^-24 |b|
     (3H additions: three bf16 terms per weight on the matrix-core path)."""
     _need_gpu()
@@ -290,10 +290,10 @@ def test_layer_prefill_small(fmt, T):
 @pytest.mark.parametrize("fmt,T,E,k", [(synth.Q8, 2, 16, 4), (synth.Q4, 7, 100, 8), (synth.Q2, 16, 256, 8),
                                        (synth.Q4, 16, 500, 10), (synth.Q8, 13, 1000, 16), (synth.Q4, 17, 256, 8)])
 def test_layer_small_batch_front_end(fmt, T, E, k):
-    """Batches of 2 to 16 tokens on the grouped-GEMM path run the split-K reduction, top-k,
-    permutation, tile list and x conversion as one kernel (one block routes while the others convert
-    x), over every keys-per-lane width of the top-k (E = 16 ... 1000); T = 17 takes the separate
-    kernels. ids bit-exact, logits, p and Y against the oracle."""
+    """Batches of 2 to 16 tokens on the grouped-GEMM path take their logits from the router GEMV and
+    run the top-k, permutation, tile list and x conversion as one kernel (one block routes while the
+    others convert x), over every keys-per-lane width of the top-k (E = 16 ... 1000); T = 17 takes
+    the router GEMM and the separate kernels. ids bit-exact, logits, p and Y against the oracle."""
     _need_gpu()
     spec = small_prefill_spec(fmt, T, E=E, k=k, Is=64 if T % 2 else 0, H=512, I=96)
     d = synth.make_layer(spec)
@@ -331,7 +331,7 @@ def test_layer_max_shapes(T, k, Is):
     d = synth.make_layer(spec)
     say("max shapes", "T=%d k=%d Is=%d" % (T, k, Is))
     O = orc_layer(spec, d)
-    g_logits, g_ids, g_p, Y = run_layer(spec, d)
+    g_logits, g_ids, g_p, Y = run_layer(spec, d, dmt=1)
     check_routing(O, d["x"], g_logits, g_ids, g_p)
     ref = oracle_tokens(O, d["x"], g_logits, range(T))
     assert_float_match(Y, ref["Y"], "Y")
