@@ -29,8 +29,10 @@ __device__ __forceinline__ void load8<_Float16>(const _Float16* row, int c, int 
     }
 }
 
-// The k rows of a token are read four at a time with every load of a group in flight before any
-// is used (a dropped pair reads row 0 and adds nothing); the sum stays in slot order. With texp,
+// The shared row and the token's exponent do not depend on the routing and are loaded first; the
+// pair rows and weights of a token are the same for the whole block (scalar loads, no LDS), and its
+// k rows are read eight at a time with every load of a group in flight before any is used (a dropped
+// pair reads row 0 and adds nothing). The sum stays in slot order, then the shared row. With texp,
 // the rows of token t are at the scale 2^(2 texp[t]) of its activations and the sum is multiplied
 // by 2^(-2 texp[t]) (exact in fp32).
 template <typename RT>
@@ -39,49 +41,46 @@ __global__ __launch_bounds__(256) void k_combine(int T, int k, int H, const floa
                                                  const int32_t* __restrict__ row_of_pair,
                                                  const RT* __restrict__ y_shared, const int32_t* __restrict__ texp,
                                                  float* __restrict__ out) {
+    constexpr int kB = 8;   // rows in flight
     const int t = blockIdx.y;
+    const int nc = H / 8;
     const int c8 = blockIdx.x * blockDim.x + threadIdx.x;  // columns 4 c8 .. and H/2 + 4 c8 ..
+    const int cc = min(c8, nc - 1);                        // loads stay in the row; only c8 < nc stores
     const int half = H / 2;
-    __shared__ float ps[16];
-    __shared__ int rows[16];
-    if ((int)threadIdx.x < k) {
-        const int q = t * k + (int)threadIdx.x;
-        ps[threadIdx.x] = p[q];
-        rows[threadIdx.x] = row_of_pair ? row_of_pair[q] : q;
-    }
-    __syncthreads();
-    if (c8 >= H / 8) return;
+    float sh[8];
+    if (y_shared) load8<RT>(y_shared + (size_t)t * H, cc, half, sh);
+    const int e = texp ? texp[t] : 0;
     float acc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int j0 = 0; j0 < k; j0 += 4) {
-        float v[4][8];
-        bool ok[4];
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += kB) {
+        float v[kB][8], pj[kB];
+        bool ok[kB];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int r = j0 + jj < k ? rows[j0 + jj] : -1;
-            ok[jj] = (unsigned)r < (unsigned)(T * k);
-            load8<RT>(y_rows + (size_t)(ok[jj] ? r : 0) * H, c8, half, v[jj]);
+        for (int jj = 0; jj < kB; ++jj) {
+            const int q = t * k + min(j0 + jj, k - 1);
+            const int r = row_of_pair ? row_of_pair[q] : q;
+            pj[jj] = p[q];
+            ok[jj] = j0 + jj < k && (unsigned)r < (unsigned)(T * k);
+            load8<RT>(y_rows + (size_t)(ok[jj] ? r : 0) * H, cc, half, v[jj]);
         }
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < kB; ++jj) {
             if (!ok[jj]) continue;
-            const float pj = ps[j0 + jj];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += pj * v[jj][e];
+            for (int i = 0; i < 8; ++i) acc[i] += pj[jj] * v[jj][i];
         }
     }
     if (y_shared) {
-        float v[8];
-        load8<RT>(y_shared + (size_t)t * H, c8, half, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += v[e];
+        for (int i = 0; i < 8; ++i) acc[i] += sh[i];
     }
     if (texp) {
-        const float sc = pow2f(-2 * texp[t]);
+        const float sc = pow2f(-2 * e);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] *= sc;
+        for (int i = 0; i < 8; ++i) acc[i] *= sc;
     }
+    if (c8 >= nc) return;
     reinterpret_cast<float4*>(out + (size_t)t * H)[c8] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     reinterpret_cast<float4*>(out + (size_t)t * H + half)[c8] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }

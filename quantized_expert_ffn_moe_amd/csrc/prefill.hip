@@ -66,9 +66,9 @@ struct TileDesc {
 // remainder, one tile of 32 * ni rows (ni the power of two at or above ceil(rem / 32)). The list is
 // expert-major (each expert's tiles side by side, so that they run on one XCD and share its L2;
 // experts of every size end up mixed along the list, which balances the XCDs), the shared group
-// last; a block scan places the experts and all threads write the list. Offsets are clamped to
-// [0, T*k] and the list to tiles_max entries, so that inconsistent offsets cannot move any access
-// out of bounds.
+// last; a block scan places the experts and each thread writes its experts' tiles. Offsets are
+// clamped to [0, T*k] and the list to tiles_max entries, so that inconsistent offsets cannot move
+// any access out of bounds.
 __device__ __forceinline__ void group_rows(const int32_t* offsets, int E, int T, int Tk, int g, int& base,
                                            int& count) {
     if (g == E) { base = 0; count = T; return; }
@@ -82,29 +82,35 @@ __host__ __device__ inline int rem_tile_ni(int rem) {
 }
 
 // Built by one block of NT threads (block 0 of k_x_to_f16, 256 threads, or of k_route_small, 1024):
-// thread i takes experts EPT i .. EPT i + EPT - 1, EPT = 1024 / NT (E <= 1024). offsets may be
-// global or LDS.
+// thread i takes experts EPT i .. EPT i + EPT - 1, EPT = 1024 / NT (E <= 1024), and writes their
+// first kDirectTiles tiles at its place in the block's exclusive scan of the tile counts (one
+// barrier); the shared group's tiles follow all routed ones, spread over the block. Only when some
+// expert has more tiles (large batches; block-uniform) do all threads then write the rest, list
+// slot i by list slot i, each finding its group by a binary search over the scan in LDS, so that
+// no thread writes a hot expert's tiles alone. offsets may be global or LDS.
 constexpr int kTileThreads = 256;
+constexpr int kDirectTiles = 4;
 template <int NT>
 __device__ __forceinline__ void build_tiles_block(const int32_t* offsets, int E, int T, int k,
                                                   int has_shared, int tiles_max, TileDesc* __restrict__ tiles,
                                                   int32_t* __restrict__ ntiles) {
     constexpr int EPT = 1024 / NT;
-    __shared__ int part[1024];   // inclusive prefix of the tile counts of experts 0 .. e
-    __shared__ int cnt[1025];    // rows of each group (the shared group last)
     __shared__ int wsum[NT / kWave];
+    __shared__ int wbig[NT / kWave];
+    __shared__ int part[1024];   // inclusive prefix of the tile counts (large batches only)
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    int nt4[EPT], sum = 0;
+    int rows[EPT], sum = 0;
+    bool big = false;
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
         const int e = EPT * tid + q;
-        int base = 0, n = 0;
-        if (e < E) group_rows(offsets, E, T, T * k, e, base, n);
-        cnt[e] = n;
-        nt4[q] = (n + kTM - 1) / kTM;
-        sum += nt4[q];
+        int base = 0;
+        rows[q] = 0;
+        if (e < E) group_rows(offsets, E, T, T * k, e, base, rows[q]);
+        const int nt = (rows[q] + kTM - 1) / kTM;
+        sum += nt;
+        big |= nt > kDirectTiles;
     }
-    if (tid == 0) cnt[1024] = has_shared ? T : 0;
     // block exclusive scan of the per-thread tile counts: wave scans, then the wave totals
     int incl = sum;
 #pragma unroll
@@ -112,40 +118,51 @@ __device__ __forceinline__ void build_tiles_block(const int32_t* offsets, int E,
         const int u = __shfl_up(incl, d, kWave);
         if (lane >= d) incl += u;
     }
-    if (lane == kWave - 1) wsum[wave] = incl;
+    const bool wave_big = __ballot(big) != 0ull;
+    if (lane == kWave - 1) {
+        wsum[wave] = incl;
+        wbig[wave] = wave_big ? 1 : 0;
+    }
     __syncthreads();
-    int run = incl - sum;
-    for (int w = 0; w < wave; ++w) run += wsum[w];
+    int run = incl - sum, routed = 0, any_big = 0;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+        run += w < wave ? wsum[w] : 0;
+        routed += wsum[w];
+        any_big |= wbig[w];
+    }
+    // tiles j0, j0 + js, ... below jmax of group g (n rows) at list position first + j
+    auto put = [&](int g, int n, int first, int j0, int js, int jmax) __attribute__((always_inline)) {
+        const int nf = n / kTM, nt = min((n + kTM - 1) / kTM, jmax);
+        for (int j = j0; j < nt; j += js)
+            if (first + j < tiles_max) tiles[first + j] = TileDesc{g, j * kTM, j < nf ? kTM / 32 : rem_tile_ni(n % kTM), 0};
+    };
 #pragma unroll
     for (int q = 0; q < EPT; ++q) {
-        run += nt4[q];
-        part[EPT * tid + q] = run;
+        put(EPT * tid + q, rows[q], run, 0, 1, kDirectTiles);
+        run += (rows[q] + kTM - 1) / kTM;
+        if (any_big) part[EPT * tid + q] = run;
     }
+    const int nsh = has_shared ? T : 0;
+    put(E, nsh, routed, tid, NT, 1 << 30);   // the shared group's tiles (T / 128 of them)
+    if (tid == 0) *ntiles = min(routed + (nsh + kTM - 1) / kTM, tiles_max);
+    if (!any_big) return;
     __syncthreads();
-    const int routed = part[1023];
-    const int total = min(routed + (cnt[1024] + kTM - 1) / kTM, tiles_max);
-    // every thread writes tiles: slot i of the routed list belongs to the first group whose
-    // inclusive prefix exceeds i (binary search), the rest to the shared group
-    for (int i = tid; i < total; i += NT) {
-        int g, first;
-        if (i < routed) {
-            int lo = 0, hi = 1023;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (part[mid] > i) hi = mid;
-                else lo = mid + 1;
-            }
-            g = lo;
-            first = lo > 0 ? part[lo - 1] : 0;
-        } else {
-            g = 1024;
-            first = routed;
+    // slot i of the routed list belongs to the first expert whose inclusive prefix exceeds it
+    for (int i = tid; i < min(routed, tiles_max); i += NT) {
+        int lo = 0, hi = 1023;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (part[mid] > i) hi = mid;
+            else lo = mid + 1;
         }
-        const int j = i - first, rows = cnt[g];
-        const int nf = rows / kTM;
-        tiles[i] = TileDesc{g == 1024 ? E : g, j * kTM, j < nf ? kTM / 32 : rem_tile_ni(rows % kTM), 0};
+        const int first = lo > 0 ? part[lo - 1] : 0;
+        const int j = i - first;
+        if (j < kDirectTiles) continue;
+        int base = 0, n = 0;
+        group_rows(offsets, E, T, T * k, lo, base, n);
+        tiles[i] = TileDesc{lo, j * kTM, j < n / kTM ? kTM / 32 : rem_tile_ni(n % kTM), 0};
     }
-    if (tid == 0) *ntiles = total;
 }
 
 int max_tiles(int T, int k, int E) { return (T * k) / kTM + T / kTM + E + 2; }

@@ -51,8 +51,10 @@ __host__ __device__ inline size_t perm_small_lds(int T, int E) {
 }
 
 // The stable counting sort of the pairs q = t k + j by expert, all three steps in one block of 1024
-// threads (per-chunk counts and token masks in LDS, smem of perm_small_lds bytes): wave w takes the
-// chunks w, w + 16, ...; thread e takes expert e in the scan (E <= 1024). ids may be global or LDS.
+// threads (per-chunk counts and token masks in LDS, smem of perm_small_lds bytes): thread i takes
+// the pairs i, i + 1024, ... in the counting and placing steps (a token's experts are distinct, so
+// its bit in an expert's chunk mask ranks its pair there); thread e takes expert e in the scan
+// (E <= 1024). ids may be global or LDS.
 // offsets[E + 1] (global) and, when offs_lds is given, a copy of them in LDS for the same block.
 // A pair whose id lies outside [0, E) is dropped: inv = -1, offsets[E] counts the kept pairs.
 __device__ inline void perm_small_block(const int32_t* ids, int T, int k, int E, int32_t* __restrict__ offsets,
@@ -69,16 +71,13 @@ __device__ inline void perm_small_block(const int32_t* ids, int T, int k, int E,
         mask[i] = 0ull;
     }
     __syncthreads();
-    for (int c = wave; c < nc; c += kWaves) {
-        const int t = c * kChunk + lane;
-        if (t < T)
-            for (int j = 0; j < k; ++j) {
-                const int e = ids[(size_t)t * k + j];
-                if ((unsigned)e < (unsigned)E) {
-                    atomicAdd(&cnt[e * nc + c], 1);
-                    atomicOr(&mask[(size_t)c * E + e], 1ull << lane);
-                }
-            }
+    for (int q = tid; q < T * k; q += 1024) {
+        const int t = q / k, c = t / kChunk;
+        const int e = ids[q];
+        if ((unsigned)e < (unsigned)E) {
+            atomicAdd(&cnt[e * nc + c], 1);
+            atomicOr(&mask[(size_t)c * E + e], 1ull << (t % kChunk));
+        }
     }
     __syncthreads();
     // exclusive prefix over the experts' totals: a scan inside each wave, then the wave totals
@@ -114,21 +113,17 @@ __device__ inline void perm_small_block(const int32_t* ids, int T, int k, int E,
         if (offs_lds) offs_lds[E] = all;
     }
     __syncthreads();
-    const unsigned long long below = (1ull << lane) - 1ull;
-    for (int c = wave; c < nc; c += kWaves) {
-        const int t = c * kChunk + lane;
-        if (t >= T) continue;
-        for (int j = 0; j < k; ++j) {
-            const int q = t * k + j;
-            const int e = ids[q];
-            if ((unsigned)e >= (unsigned)E) {
-                inv[q] = -1;
-                continue;
-            }
-            const int pos = cnt[e * nc + c] + __popcll(mask[(size_t)c * E + e] & below);
-            perm[pos] = q;
-            inv[q] = pos;
+    for (int q = tid; q < T * k; q += 1024) {
+        const int t = q / k, c = t / kChunk;
+        const int e = ids[q];
+        if ((unsigned)e >= (unsigned)E) {
+            inv[q] = -1;
+            continue;
         }
+        const unsigned long long below = (1ull << (t % kChunk)) - 1ull;
+        const int pos = cnt[e * nc + c] + __popcll(mask[(size_t)c * E + e] & below);
+        perm[pos] = q;
+        inv[q] = pos;
     }
 }
 
