@@ -17,11 +17,13 @@ namespace moe {
 // value). Every product x * wi is exact in fp32, so the three MFMAs per fragment pair give the
 // fp32 dot product up to the order of the fp32 additions.
 //
-// Tiles of 64 tokens x 64 experts, four waves of 32 x 32, K steps of 32 through double-buffered
-// LDS (rows padded to 80 bytes), loads kept two steps ahead in registers. Blocks that share token
-// rows are placed on one XCD so that x is read once into that XCD's L2.
+// Tiles of 64 tokens x 64 experts, four waves of 32 x 32 (v_mfma_f32_32x32x16_bf16: two per K step
+// and weight term; the 16 x 16 x 32 form runs at a far lower rate on this chip), K steps of 32
+// through double-buffered LDS (rows padded to 80 bytes), loads kept two steps ahead in registers.
+// Blocks that share token rows are placed on one XCD so that x is read once into that XCD's L2.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRtM = 64, kRtN = 64, kRtK = 32, kRtLds = kRtK + 8, kRtXcds = 8;
@@ -83,31 +85,27 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const float* __restrict_
         *reinterpret_cast<bf16x8*>(&Bs[st][2][lr * kRtLds + lc]) = p3;
     };
 
-    floatx4 acc[2][2];
+    floatx16 acc;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int kofs = 8 * (lane / 16);
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const int kofs = 8 * (lane / 32);
     auto kstep = [&](int ks, const RouterSlot& next_sl, RouterSlot& refill) __attribute__((always_inline)) {
         const int cur = ks & 1;
         bf16x8 a[2], b[3][2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            a[i] = *reinterpret_cast<const bf16x8*>(&As[cur][(wm * 32 + 16 * i + lane % 16) * kRtLds + kofs]);
+        for (int h = 0; h < 2; ++h)
+            a[h] = *reinterpret_cast<const bf16x8*>(&As[cur][(wm * 32 + lane % 32) * kRtLds + 16 * h + kofs]);
 #pragma unroll
         for (int p = 0; p < 3; ++p)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                b[p][j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][p][(wn * 32 + 16 * j + lane % 16) * kRtLds + kofs]);
-        // smallest terms first
+            for (int h = 0; h < 2; ++h)
+                b[p][h] = *reinterpret_cast<const bf16x8*>(&Bs[cur][p][(wn * 32 + lane % 32) * kRtLds + 16 * h + kofs]);
+        // each half of the step: smallest terms first
 #pragma unroll
-        for (int p = 2; p >= 0; --p)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[p][j], acc[i][j], 0, 0, 0);
+            for (int p = 2; p >= 0; --p)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h], b[p][h], acc, 0, 0, 0);
         lstore(next_sl, cur ^ 1);
         gload(refill, ks + 3);
         __syncthreads();
@@ -126,21 +124,19 @@ __global__ __launch_bounds__(256, 2) void k_router_mfma(const float* __restrict_
     }
     if (ks < nk) kstep(ks, s1, s1);
 
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int e = e0 + wn * 32 + 16 * j + lane % 16;
-            if (e >= E) continue;
+    {
+        const int e = e0 + wn * 32 + lane % 32;
+        if (e < E) {
             const float b = splits == 1 && bias ? bias[e] : 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = t0 + wm * 32 + 16 * i + 4 * (lane / 16) + r;
+            for (int r = 0; r < 16; ++r) {
+                const int t = t0 + wm * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
                 if (t >= T) continue;
-                if (splits == 1) logits[(size_t)t * E + e] = acc[i][j][r] + b;
-                else part[((size_t)blockIdx.y * T + t) * E + e] = acc[i][j][r];
+                if (splits == 1) logits[(size_t)t * E + e] = acc[r] + b;
+                else part[((size_t)blockIdx.y * T + t) * E + e] = acc[r];
             }
         }
+    }
 }
 
 __global__ __launch_bounds__(256) void k_router_reduce(const float* __restrict__ part, int splits, int T, int E,
