@@ -700,6 +700,8 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
                 const int i = (int)threadIdx.x + kDownThreads * b;
                 if (i < n4) hq4[i] = hv0[b];
             }
+            // the rest (unrolled: each group of loads in flight together, not one round trip each)
+#pragma unroll 8
             for (int i = (int)threadIdx.x + kDownThreads * kHBatch; i < n4; i += kDownThreads) hq[i] = hs[i];
             __syncthreads();
             h_in = true;
@@ -744,7 +746,8 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // lane -> (row, slot of the chunk, token): the slot's block partials summed in order
+            // lane -> (row, slot of the chunk, token): the slot's block partials summed in order (the
+            // loops unrolled so that eight LDS reads are in flight before their in-order adds)
             const int nr = s1 - s0, ns = nr + (has_sh ? 1 : 0);
             for (int st = lane; st < RPW * ns * T; st += kWave) {
                 const int r = st / (ns * T), rem = st % (ns * T);
@@ -757,10 +760,12 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
                     const int q = P.pair_of[s0 + sl][t];
                     if (q < 0) continue;
                     float sum = 0.f;
+#pragma unroll 8
                     for (int b = 0; b < nbI; ++b) sum += pr[sl * nbI + b];
                     y_pairs[(size_t)q * H + m] = sum * sc;
                 } else {
                     float sum = 0.f;
+#pragma unroll 8
                     for (int b = 0; b < nbS; ++b) sum += pr[nr * nbI + b];
                     y_shared[(size_t)t * H + m] = sum * sc;
                 }
