@@ -367,6 +367,36 @@ def test_experts_prefill_entry(T):
     assert_float_match(Y.cpu().numpy(), ref["Y"], "Y")
 
 
+def test_experts_prefill_hot_experts():
+    """Every token routed to experts 0 and 1 (ids given): each of the two groups holds 700 rows,
+    five full 128-row tiles and a 60-row remainder, more than the four tiles per expert that the
+    tile list's first pass writes, so its second pass places the rest. Every y_sorted row against
+    the oracle's expert outputs for that routing."""
+    _need_gpu()
+    T = 700
+    spec = small_prefill_spec(synth.Q4, T, E=8, k=2, Is=64, I=64)
+    d = synth.make_layer(spec)
+    say("prefill hot experts T=%d" % T)
+    O = orc_layer(spec, d)
+    L = dev_layer(spec, d)
+    xd = dev_x(d["x"])
+    g_ids = np.tile(np.array([[0, 1]], dtype=np.int32), (T, 1))
+    offsets, perm, inv = moe.moe_permute(L, torch.from_numpy(g_ids).cuda())
+    y_sorted, y_shared = moe.moe_experts_prefill(L, xd, offsets, perm)
+    torch.cuda.synchronize()
+    o_off, o_perm, o_inv = oracle.permute(g_ids, spec.E)
+    assert np.array_equal(offsets.cpu().numpy(), o_off)
+    assert np.array_equal(perm.cpu().numpy(), o_perm)
+    # logits that make the oracle choose experts 0 then 1 for every token
+    lg = np.full((T, spec.E), -10.0)
+    lg[:, 0], lg[:, 1] = 10.0, 9.0
+    ref = oracle_tokens(O, d["x"], lg, range(T))
+    assert np.array_equal(ref["ids"], g_ids)
+    want_sorted = ref["y_pairs"].reshape(T * spec.k, spec.H)[o_perm]
+    assert_float_match(y_sorted.cpu().numpy(), want_sorted, "y_sorted")
+    assert_float_match(y_shared.cpu().numpy(), ref["y_shared"], "y_shared")
+
+
 @pytest.mark.parametrize("fmt,T,H,I,Is", [(synth.Q4, 300, 256, 128, 64), (synth.Q8, 200, 800, 160, 96),
                                            (synth.Q2, 130, 800, 160, 0)])
 def test_experts_prefill_f16_entry(fmt, T, H, I, Is):
