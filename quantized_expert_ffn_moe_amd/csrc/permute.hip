@@ -21,18 +21,32 @@ namespace moe {
 int perm_chunks(int T) { return (T + kChunk - 1) / kChunk; }
 size_t perm_scratch_ints(int T, int E) { return (size_t)(perm_chunks(T) + 1) * E; }
 
+// A token's k <= 16 expert ids, loaded together (unconditional, clamped loads: one round trip, not
+// k); ids past k read as -1.
+constexpr int kMaxTopK = 16;
+__device__ __forceinline__ void token_ids(const int32_t* __restrict__ ids, int T, int k, int t, int (&ev)[kMaxTopK]) {
+    const size_t row = (size_t)min(t, T - 1) * k;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) ev[j] = ids[row + min(j, k - 1)];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+        if (j >= k) ev[j] = -1;
+}
+
 __global__ __launch_bounds__(64) void k_perm_hist(const int32_t* __restrict__ ids, int T, int k, int E,
                                                   int32_t* __restrict__ counts) {
     extern __shared__ int32_t cnt[];
     const int c = blockIdx.x, lane = threadIdx.x;
+    const int t = c * kChunk + lane;
+    int ev[kMaxTopK];
+    token_ids(ids, T, k, t, ev);
     for (int e = lane; e < E; e += kWave) cnt[e] = 0;
     __syncthreads();
-    const int t = c * kChunk + lane;
-    if (t < T)
-        for (int j = 0; j < k; ++j) {
-            const int e = ids[(size_t)t * k + j];
-            if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
-        }
+    if (t < T) {
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+            if ((unsigned)ev[j] < (unsigned)E) atomicAdd(&cnt[ev[j]], 1);
+    }
     __syncthreads();
     const int nc = gridDim.x;
     for (int e = lane; e < E; e += kWave) counts[(size_t)e * nc + c] = cnt[e];
@@ -82,40 +96,57 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t* __restrict__
     extern __shared__ unsigned long long tokmask[];
     int32_t* offs = reinterpret_cast<int32_t*>(tokmask + E);   // [E + 1]
     const int c = blockIdx.x, lane = threadIdx.x;
+    const int t = c * kChunk + lane;
+    // the token's ids and this lane's E / 64 <= 16 expert totals, each group loaded together
+    int ev[kMaxTopK];
+    token_ids(ids, T, k, t, ev);
+    const int per = (E + kWave - 1) / kWave;
+    const int lo = min(lane * per, E), hi = min(lo + per, E);
+    int tv[kMaxTopK];
+#pragma unroll
+    for (int i = 0; i < kMaxTopK; ++i) tv[i] = totals[min(lo + i, E - 1)];
     for (int e = lane; e < E; e += kWave) tokmask[e] = 0ull;
     {
-        const int per = (E + kWave - 1) / kWave;
-        const int lo = min(lane * per, E), hi = min(lo + per, E);
         int sum = 0;
-        for (int i = lo; i < hi; ++i) sum += totals[i];
+#pragma unroll
+        for (int i = 0; i < kMaxTopK; ++i)
+            if (lo + i < hi) sum += tv[i];
         int total;
         int run = wave_excl_scan(sum, total);
-        for (int i = lo; i < hi; ++i) {
-            offs[i] = run;
-            run += totals[i];
-        }
+#pragma unroll
+        for (int i = 0; i < kMaxTopK; ++i)
+            if (lo + i < hi) {
+                offs[lo + i] = run;
+                run += tv[i];
+            }
         if (lane == 0) offs[E] = total;   // = kept pairs
     }
     __syncthreads();
     if (c == 0)
         for (int e = lane; e <= E; e += kWave) offsets[e] = offs[e];
-    const int t = c * kChunk + lane;
-    if (t < T)
-        for (int j = 0; j < k; ++j) {
-            const int e = ids[(size_t)t * k + j];
-            if ((unsigned)e < (unsigned)E) atomicOr(&tokmask[e], 1ull << lane);
-        }
+    if (t < T) {
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+            if ((unsigned)ev[j] < (unsigned)E) atomicOr(&tokmask[ev[j]], 1ull << lane);
+    }
     __syncthreads();
     if (t < T) {
         const unsigned long long below = (1ull << lane) - 1ull;
-        for (int j = 0; j < k; ++j) {
+        // the chunk's base inside each chosen expert, all k loaded together
+        int bv[kMaxTopK];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+            bv[j] = base[(size_t)min(max(ev[j], 0), E - 1) * gridDim.x + c];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            if (j >= k) break;
             const int q = t * k + j;
-            const int e = ids[q];
+            const int e = ev[j];
             if ((unsigned)e >= (unsigned)E) {
                 inv[q] = -1;
                 continue;
             }
-            const int pos = offs[e] + base[(size_t)e * gridDim.x + c] + __popcll(tokmask[e] & below);
+            const int pos = offs[e] + bv[j] + __popcll(tokmask[e] & below);
             perm[pos] = q;
             inv[q] = pos;
         }
