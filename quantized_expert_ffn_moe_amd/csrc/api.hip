@@ -9,7 +9,7 @@ using namespace moe;
 
 namespace {
 
-constexpr int kMaxE = 1024, kMaxK = 16, kMaxH = 16384, kMaxI = 4096, kMaxT = 1 << 20;
+constexpr int kMaxE = 1024, kMaxK = kMaxTopK, kMaxH = 16384, kMaxI = 4096, kMaxT = 1 << 20;
 // The router: the GEMV (weights read once for all tokens) up to kGemvMaxT tokens, the bf16x3 MFMA
 // GEMM above.
 // moe_layer takes the decode kernels up to this many tokens by default (when they fit the shape):

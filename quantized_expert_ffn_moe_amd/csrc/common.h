@@ -10,6 +10,7 @@
 namespace moe {
 
 constexpr int kWave = 64;
+constexpr int kMaxTopK = 16;   // the largest top_k the library accepts
 
 // ------------------------------------------------------------------------------------- numbers
 

@@ -21,9 +21,8 @@ namespace moe {
 int perm_chunks(int T) { return (T + kChunk - 1) / kChunk; }
 size_t perm_scratch_ints(int T, int E) { return (size_t)(perm_chunks(T) + 1) * E; }
 
-// A token's k <= 16 expert ids, loaded together (unconditional, clamped loads: one round trip, not
-// k); ids past k read as -1.
-constexpr int kMaxTopK = 16;
+// A token's k <= kMaxTopK expert ids, loaded together (unconditional, clamped loads: one round trip,
+// not k); ids past k read as -1.
 __device__ __forceinline__ void token_ids(const int32_t* __restrict__ ids, int T, int k, int t, int (&ev)[kMaxTopK]) {
     const size_t row = (size_t)min(t, T - 1) * k;
 #pragma unroll
