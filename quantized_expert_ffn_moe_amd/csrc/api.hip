@@ -10,8 +10,9 @@ using namespace moe;
 namespace {
 
 constexpr int kMaxE = 1024, kMaxK = kMaxTopK, kMaxH = 16384, kMaxI = 4096, kMaxT = 1 << 20;
-// The router: the GEMV (weights read once for all tokens) up to kGemvMaxT tokens, the bf16x3 MFMA
-// GEMM above.
+// (The router is the GEMV, weights read once for all tokens, up to kGemvMaxT tokens of kernels.h,
+// and the bf16x3 MFMA GEMM above.)
+
 // moe_layer takes the decode kernels up to this many tokens by default (when they fit the shape):
 // the crossover measured on the 8K-prefill layer shape (H 2048, 256 experts top-8 + shared, 4-bit);
 // moe_layer_desc.decode_max_tokens overrides it (up to 8).

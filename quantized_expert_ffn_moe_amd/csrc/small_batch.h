@@ -1,5 +1,6 @@
-// Device steps that the small-batch kernels share: the per-token reduction of the router's split-K
-// partial sums, and the token-to-expert permutation of a small batch done by one block.
+// Device steps shared between kernels of the small and mid-size batch paths: the per-token reduction
+// of the router GEMM's split-K partial sums (k_router_reduce_topk), and the token-to-expert
+// permutation of a batch done by one block (k_perm_small, k_route_small).
 #pragma once
 
 #include "common.h"
