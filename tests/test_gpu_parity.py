@@ -546,11 +546,12 @@ def test_permute_edges(T, E, k):
 
 # ------------------------------------------------------------------------- special cases
 
-def test_permute_drops_out_of_range_ids():
+@pytest.mark.parametrize("T,E,k", [(300, 64, 4), (3000, 1024, 8)])
+def test_permute_drops_out_of_range_ids(T, E, k):
     """Ids outside [0, E) are dropped: no slot, inv = -1, offsets count the kept pairs, and the
-    kept pairs keep the stable expert order."""
+    kept pairs keep the stable expert order (the one-block permutation at T = 300, the three-kernel
+    one at T = 3000 with 1024 experts)."""
     _need_gpu()
-    T, E, k = 300, 64, 4
     spec = synth.LayerSpec("permbad", T=T, H=64, E=E, k=k, I=64, Is=0, fmt=synth.Q8, zipf=False)
     rng = np.random.default_rng(11)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
