@@ -215,7 +215,7 @@ def test_golden_examples_on_gpu():
 
 # ------------------------------------------------------------------------- router accuracy
 
-@pytest.mark.parametrize("T,E", [(3, 256), (8, 256), (16, 256), (17, 256), (300, 200), (1000, 512)])
+@pytest.mark.parametrize("T,E", [(3, 256), (8, 256), (16, 256), (17, 256), (300, 200), (1000, 512), (1500, 256)])
 def test_router_fp32_error_bound(T, E):
     """Router logits (GEMV for T <= 16, bf16x3 MFMA GEMM above) stay within the worst-case fp32
     summation bound of the oracle's fp64 logits: |err| <= 3H * 2^-24 * sum_h |x_h w_h| + 2^-24 |b|
@@ -239,12 +239,13 @@ def test_router_fp32_error_bound(T, E):
     assert np.all(err <= bound), "max err/bound %.3f" % float(np.max(err / bound))
 
 
-@pytest.mark.parametrize("T,H,mbits", [(3, 96, 17), (7, 96, 17), (300, 96, 17), (40, 256, 16), (600, 96, 17)])
+@pytest.mark.parametrize("T,H,mbits", [(3, 96, 17), (7, 96, 17), (300, 96, 17), (40, 256, 16), (600, 96, 17),
+                                       (1100, 96, 17)])
 def test_router_exact_on_representable_sums(T, H, mbits):
     """Inputs whose every partial sum is exact in fp32: x in {-1, 0, 1}, w = m * 2^-mbits with m in
     [2^(mbits-1), 2^mbits), H * 2^mbits <= 2^24 (17 bits at H = 96: all three bf16 terms of the
     split are needed; H = 256 with 16 bits runs the K-split GEMM with its partial-sum reduction;
-    T = 600 spans ten token tiles).
+    T = 600 spans ten token tiles, T = 1100 nine of the 128-token tiles large batches use).
     Any fp32 evaluation order gives the exact value, so the logits must equal the oracle's bit for
     bit."""
     _need_gpu()
