@@ -223,7 +223,9 @@ def prefill_workload(steps: int, warmup: int):
     t0 = time.time()
     d = synth.make_layer(spec)
     L = upload(spec, d)
+    L.pack_prefill_codes()   # the grouped GEMMs' copy of the codes, made once like the weights (not timed)
     x = dev_x(d["x"])
+    torch.cuda.synchronize()
     log("prefill8k ready in %.1f s" % (time.time() - t0))
     T = spec.T
     ws = moe.Workspace()
@@ -258,7 +260,8 @@ def prefill_workload(steps: int, warmup: int):
             "roofline": roof,
             "config": {"workload": "prefill8k", "tokens_per_call": T, "hidden": spec.H, "experts": spec.E,
                        "top_k": spec.k, "inter": spec.I, "shared_inter": spec.Is,
-                       "format": synth.FMT_NAMES[spec.fmt]}}
+                       "format": synth.FMT_NAMES[spec.fmt],
+                       "codes": "packed copy for the grouped GEMMs (moe_pack_prefill_codes, made at setup)"}}
 
 
 def kv_workload(reps: int = 20):
@@ -294,11 +297,14 @@ def sweep_tokens(reps: int = 20):
     spec = synth.CONFIGS["prefill8k"]
     d = synth.make_layer(spec)
     L = upload(spec, d)
+    L.pack_prefill_codes()   # as in the prefill8k measurement
 
     def with_desc(dmt):
         m = L.mats
-        return moe.DeviceLayer(moe.LayerDesc.from_spec(spec, dmt), L.w_router, L.router_bias, m["gate"], m["up"],
-                               m["down"], m["sh_gate"], m["sh_up"], m["sh_down"])
+        Lx = moe.DeviceLayer(moe.LayerDesc.from_spec(spec, dmt), L.w_router, L.router_bias, m["gate"], m["up"],
+                             m["down"], m["sh_gate"], m["sh_up"], m["sh_down"])
+        Lx.prefill_codes, Lx.c.prefill_codes = L.prefill_codes, L.c.prefill_codes
+        return Lx
     Ld, Lg = with_desc(8), with_desc(1)
     xs_all = dev_x(d["x"])
     rows = []

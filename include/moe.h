@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef int32_t moe_status;
 enum {
@@ -122,7 +122,7 @@ typedef struct {
     int32_t shared_inter;  /* Is, 0 = no shared expert */
     moe_qformat fmt;       /* code format of every expert matrix */
     int32_t decode_max_tokens;  /* moe_layer's regime switch: the decode kernels for T <= this (when
-                                   they fit), the grouped GEMMs above; 0 = the default, 6 (measured
+                                   they fit), the grouped GEMMs above; 0 = the default, 5 (measured
                                    crossover at H 2048, 256 experts top-8, 4-bit); at most 8 */
 } moe_layer_desc;
 
@@ -131,6 +131,10 @@ typedef struct {
     const float* router_bias;  /* [E] or NULL */
     moe_qmat gate, up, down;   /* routed experts, stacked expert-major */
     moe_qmat sh_gate, sh_up, sh_down;  /* shared expert; ignored when shared_inter == 0 */
+    const void* prefill_codes; /* NULL, or the codes of every matrix above repacked by
+                                  moe_pack_prefill_codes (16-byte aligned): the grouped GEMMs then
+                                  read their weight codes from there (same results, fewer memory
+                                  transactions); everything else reads the codes above */
 } moe_layer_weights;
 
 /*
@@ -279,6 +283,25 @@ moe_status moe_kv_encode(const uint16_t* src, int32_t rows, int32_t D, int8_t* c
  */
 moe_status moe_kv_gather(const int8_t* codes, const uint16_t* scales, int32_t n_rows, int32_t D,
                          const int32_t* idx, int32_t n_idx, float* out, void* stream);
+
+/*
+ * A copy of the expert codes laid out for the grouped GEMMs' weight loads, made once per set of
+ * weights (for example when a model is loaded) and passed as moe_layer_weights.prefill_codes. Each
+ * matrix of N rows and K columns (BB = 32, 16 or 8 code bytes per 32-value block for Q8, Q4, Q2) is
+ * cut into groups of 32 rows (the last one padded with zero rows) and steps of 64 columns; group r,
+ * step s is one piece of 64 BB bytes: block 2s of rows 32r .. 32r + 31 (BB bytes each, in row
+ * order), then block 2s + 1 of the same rows (zero bytes past the row's last block). A matrix takes
+ * ceil(N / 32) ceil(K / 64) 64 BB bytes, its pieces group-major; the matrices follow one another:
+ * the E routed gate matrices (N = I, K = H), the E up matrices, the E down matrices (N = H, K = I),
+ * then the shared gate, up and down (N = Is or H, K = H or Is) when shared_inter > 0. Scales are
+ * not copied (they stay in the moe_qmat arrays). The copy must be made again if the codes change.
+ */
+/* Bytes of the packed copy of the expert codes (host only; 0 for an invalid descriptor). */
+size_t moe_prefill_codes_bytes(const moe_layer_desc* desc);
+/* Writes the packed copy of w's expert codes to dst (device, moe_prefill_codes_bytes bytes, 16-byte
+ * aligned), stream-ordered. Invalid descriptor or weights, or a NULL or misaligned dst: an error
+ * status before anything is enqueued. */
+moe_status moe_pack_prefill_codes(const moe_layer_desc* desc, const moe_layer_weights* w, void* dst, void* stream);
 
 /* Bytes of workspace an entry point needs for this shape (host only; no GPU work). */
 moe_status moe_workspace_size(const moe_layer_desc* desc, int32_t T, moe_call call, size_t* bytes);

@@ -53,7 +53,8 @@ class _Desc(ctypes.Structure):
 class _Weights(ctypes.Structure):
     _fields_ = [("w_router", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
                 ("gate", _QMat), ("up", _QMat), ("down", _QMat),
-                ("sh_gate", _QMat), ("sh_up", _QMat), ("sh_down", _QMat)]
+                ("sh_gate", _QMat), ("sh_up", _QMat), ("sh_down", _QMat),
+                ("prefill_codes", ctypes.c_void_p)]
 
 
 _lib = None
@@ -99,6 +100,10 @@ def lib():
         L.moe_status_string.argtypes = [st]
         L.moe_abi_version.restype = i32
         L.moe_abi_version.argtypes = []
+        L.moe_prefill_codes_bytes.restype = sz
+        L.moe_prefill_codes_bytes.argtypes = [D]
+        L.moe_pack_prefill_codes.restype = st
+        L.moe_pack_prefill_codes.argtypes = [D, W, vp, vp]
         _lib = L
     return _lib
 
@@ -169,7 +174,28 @@ class DeviceLayer:
             return _QMat(None, None) if pair is None else _QMat(_ptr(pair[0]), _ptr(pair[1]))
 
         self.c = _Weights(_ptr(w_router), _ptr(router_bias), qm(gate), qm(up), qm(down), qm(sh_gate), qm(sh_up),
-                          qm(sh_down))
+                          qm(sh_down), None)
+        self.prefill_codes = None
+
+    def pack_prefill_codes(self, stream=None) -> "DeviceLayer":
+        """Make the packed copy of the expert codes (moe_pack_prefill_codes) and hand it to every
+        later call through the weights (the grouped GEMMs then read it); a one-time cost."""
+        n = int(lib().moe_prefill_codes_bytes(ctypes.byref(self.desc.c)))
+        if n == 0:
+            raise MoeError(MOE_ERR_INVALID_ARG, "moe_prefill_codes_bytes")
+        buf = torch.empty(n, dtype=torch.uint8, device=self.mats["gate"][0].device)
+        self.c.prefill_codes = None
+        _check(lib().moe_pack_prefill_codes(ctypes.byref(self.desc.c), ctypes.byref(self.c), _ptr(buf),
+                                            _stream(stream)), "moe_pack_prefill_codes")
+        self.prefill_codes = buf
+        self.c.prefill_codes = _ptr(buf)
+        return self
+
+    def drop_prefill_codes(self) -> "DeviceLayer":
+        """Back to the row-major codes only."""
+        self.c.prefill_codes = None
+        self.prefill_codes = None
+        return self
 
     @classmethod
     def from_host(cls, desc: LayerDesc, d: dict, device="cuda") -> "DeviceLayer":

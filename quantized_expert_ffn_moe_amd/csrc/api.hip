@@ -42,6 +42,7 @@ moe_status check_expert_weights(const moe_layer_desc* d, const moe_layer_weights
     if (!qmat_ok(w->gate) || !qmat_ok(w->up) || !qmat_ok(w->down)) return MOE_ERR_INVALID_ARG;
     if (d->shared_inter > 0 && (!qmat_ok(w->sh_gate) || !qmat_ok(w->sh_up) || !qmat_ok(w->sh_down)))
         return MOE_ERR_INVALID_ARG;
+    if (w->prefill_codes && !aligned16(w->prefill_codes)) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 
@@ -62,6 +63,7 @@ LayerView view(const moe_layer_desc* d, const moe_layer_weights* w) {
     L.sg_codes = sh ? (const uint8_t*)w->sh_gate.codes : nullptr; L.sg_scales = sh ? w->sh_gate.scales : nullptr;
     L.su_codes = sh ? (const uint8_t*)w->sh_up.codes : nullptr; L.su_scales = sh ? w->sh_up.scales : nullptr;
     L.sd_codes = sh ? (const uint8_t*)w->sh_down.codes : nullptr; L.sd_scales = sh ? w->sh_down.scales : nullptr;
+    L.pk = (const uint8_t*)w->prefill_codes;
     return L;
 }
 
@@ -203,6 +205,20 @@ void* static_scratch(moe_status* st) {
 extern "C" {
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+size_t moe_prefill_codes_bytes(const moe_layer_desc* d) {
+    if (check_desc(d) != MOE_OK) return 0;
+    return (size_t)packed_offsets(shape_view(d)).total;
+}
+
+moe_status moe_pack_prefill_codes(const moe_layer_desc* d, const moe_layer_weights* w, void* dst, void* stream) {
+    MOE_TRY(check_desc(d));
+    MOE_TRY(check_expert_weights(d, w));
+    if (!dst || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+    LayerView L = view(d, w);
+    L.pk = nullptr;
+    return launch_pack_codes(L, static_cast<uint8_t*>(dst), (hipStream_t)stream);
+}
 
 const char* moe_status_string(moe_status s) {
     switch (s) {

@@ -14,8 +14,38 @@ struct LayerView {
     const uint16_t *g_scales, *u_scales, *d_scales;
     const uint8_t *sg_codes, *su_codes, *sd_codes;
     const uint16_t *sg_scales, *su_scales, *sd_scales;
+    const uint8_t* pk;   // the packed copy of the codes for the grouped GEMMs, or NULL
     __host__ __device__ int Imax() const { return I > Is ? I : Is; }
 };
+
+// The packed codes (moe_pack_prefill_codes): a matrix of N rows and K columns in pieces of 32 rows x
+// 64 columns (64 BB bytes: block 2s of the 32 rows, then block 2s + 1), group-major; the matrices in
+// the order E gates, E ups, E downs, then the shared gate, up and down.
+__host__ __device__ inline int64_t packed_mat_bytes(int N, int K, int fmt) {
+    return (int64_t)((N + 31) / 32) * ((K + 63) / 64) * 64 * block_bytes(fmt);
+}
+struct PackedOffsets {
+    int64_t pg, pd, psg, psd;                         // bytes of one gate/up, down, shared gate/up, shared down
+    int64_t gate, up, down, sh_gate, sh_up, sh_down;  // where each stack starts
+    int64_t total;
+};
+__host__ __device__ inline PackedOffsets packed_offsets(const LayerView& L) {
+    PackedOffsets o;
+    o.pg = packed_mat_bytes(L.I, L.H, L.fmt);
+    o.pd = packed_mat_bytes(L.H, L.I, L.fmt);
+    o.psg = L.Is > 0 ? packed_mat_bytes(L.Is, L.H, L.fmt) : 0;
+    o.psd = L.Is > 0 ? packed_mat_bytes(L.H, L.Is, L.fmt) : 0;
+    o.gate = 0;
+    o.up = o.gate + (int64_t)L.E * o.pg;
+    o.down = o.up + (int64_t)L.E * o.pg;
+    o.sh_gate = o.down + (int64_t)L.E * o.pd;
+    o.sh_up = o.sh_gate + o.psg;
+    o.sh_down = o.sh_up + o.psg;
+    o.total = o.sh_down + o.psd;
+    return o;
+}
+// Writes the packed copy of L's codes to dst (16-byte aligned, packed_offsets(L).total bytes).
+moe_status launch_pack_codes(const LayerView& L, uint8_t* dst, hipStream_t s);
 
 // Router GEMM (above kGemvMaxT tokens) and the top-k + softmax kernel (one wave per token); the GEMM's
 // scratch: router_scratch_bytes() (split-K partial sums; none when 0).

@@ -559,10 +559,35 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
             smat[0] = smat[1] = reinterpret_cast<const uint8_t*>(L.d_scales + e * H * nb);
         }
     }
-    const int64_t bbytes = mrows * rb, sbytes = mrows * nb * 2;
-    // lane offsets of block g of row wrow (tile 0; tile 1 adds its row difference)
-    const int bvo0 = (int)(wrow[0] * rb) + g * BB, svo0 = (wrow[0] * nb + g) * 2;
-    const int bdv = (int)((wrow[1] - wrow[0]) * rb), sdv = (wrow[1] - wrow[0]) * nb * 2;
+    int64_t bbytes = mrows * rb;
+    const int64_t sbytes = mrows * nb * 2;
+    // lane offsets of block g of row wrow (tile 0; tile 1 adds its row difference), and the code
+    // bytes the buffer base advances per K step
+    int bvo0 = (int)(wrow[0] * rb) + g * BB, bdv = (int)((wrow[1] - wrow[0]) * rb), cstep = 2 * BB;
+    const int svo0 = (wrow[0] * nb + g) * 2, sdv = (wrow[1] - wrow[0]) * nb * 2;
+    if (L.pk) {
+        // the packed copy: the piece of (32-row group, step) is 64 BB bytes and lane (frow, g) reads
+        // BB bytes at BB (frow + 32 g) of it, so that each load is one contiguous run; a group past
+        // the matrix reads its last group (those rows are never stored)
+        const PackedOffsets po = packed_offsets(L);
+        const int ngrp = (int)((mrows + 31) / 32);
+        int grp[2];
+        if constexpr (GATEUP) {
+            grp[0] = grp[1] = min((n0 + 32 * wave) / 32, ngrp - 1);
+            const int64_t e = td.group;
+            bmat[0] = L.pk + (shared ? po.sh_gate : po.gate + e * po.pg);
+            bmat[1] = L.pk + (shared ? po.sh_up : po.up + e * po.pg);
+            bbytes = shared ? po.psg : po.pg;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) grp[j] = min((n0 + 64 * wave + 32 * j) / 32, ngrp - 1);
+            bmat[0] = bmat[1] = L.pk + (shared ? po.sh_down : po.down + (int64_t)td.group * po.pd);
+            bbytes = shared ? po.psd : po.pd;
+        }
+        cstep = 64 * BB;
+        bvo0 = grp[0] * nsteps * cstep + BB * (frow + 32 * g);
+        bdv = (grp[1] - grp[0]) * nsteps * cstep;
+    }
     // SD: lane l of wave w loads 16 bytes (the 8 scales of 4 K steps) of row wrow[l / 32] of tile
     // l / 32 for rows 32 w + l % 32; they land at byte 16 l of the wave's 1 KB of the group's buffer
     const char* sgsrc = nullptr;
@@ -612,7 +637,7 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int cofs = 2 * t * BB, sofs = 4 * t;
+            const int cofs = cstep * t, sofs = 4 * t;
             const int bvo = bvo0 + j * bdv, svo = svo0 + j * sdv;
             const __amdgpu_buffer_rsrc_t rc =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(bmat[j] + cofs), (short)0, (int)(bbytes - cofs), kRawBufferWord3);
@@ -921,6 +946,52 @@ __global__ __launch_bounds__(kGT, 2) void k_grouped_gemm(LayerView L, int T, con
         default: if (sd) MOE_GEMM_TILE(1, true); else MOE_GEMM_TILE(1, false); break;
     }
 #undef MOE_GEMM_TILE
+}
+
+// -------------------------------------------------------------------------------- packed codes
+
+// One thread per 4 bytes of the packed copy of `count` matrices of N x K whose row-major codes
+// start at src (one after another): byte o of a matrix's copy lies in piece o / (64 BB) = (group r,
+// step s); its slot l = (o % (64 BB)) / BB holds block 2s + l / 32 of row 32 r + l % 32, zero past
+// the matrix's rows or the row's blocks.
+__global__ __launch_bounds__(256) void k_pack_codes(const uint8_t* __restrict__ src, int N, int K, int fmt,
+                                                    int64_t pmat, int count, uint8_t* __restrict__ dst) {
+    const int64_t units = pmat / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= units * count) return;
+    const int64_t m = i / units, o = (i % units) * 4;
+    const int BB = block_bytes(fmt);
+    const int nsteps = (K + 63) / 64, nb = K / 32;
+    const int64_t rb = row_bytes(fmt, K);
+    const int64_t c = o / (64 * BB);
+    const int ob = (int)(o % (64 * BB));
+    const int r = (int)(c / nsteps), st = (int)(c % nsteps);
+    const int l = ob / BB, bo = ob % BB;
+    const int row = 32 * r + l % 32, blk = 2 * st + l / 32;
+    uint32_t v = 0u;
+    if (row < N && blk < nb)
+        v = *reinterpret_cast<const uint32_t*>(src + (m * N + row) * rb + (int64_t)blk * BB + bo);
+    *reinterpret_cast<uint32_t*>(dst + m * pmat + o) = v;
+}
+
+moe_status launch_pack_codes(const LayerView& L, uint8_t* dst, hipStream_t s) {
+    const PackedOffsets po = packed_offsets(L);
+    auto pack = [&](const uint8_t* src, int N, int K, int64_t pmat, int count, int64_t at) -> moe_status {
+        const int64_t n = pmat / 4 * count;
+        hipLaunchKernelGGL(k_pack_codes, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, N, K, L.fmt, pmat,
+                           count, dst + at);
+        MOE_LAUNCH_CHECK();
+        return MOE_OK;
+    };
+    moe_status st = pack(L.g_codes, L.I, L.H, po.pg, L.E, po.gate);
+    if (st == MOE_OK) st = pack(L.u_codes, L.I, L.H, po.pg, L.E, po.up);
+    if (st == MOE_OK) st = pack(L.d_codes, L.H, L.I, po.pd, L.E, po.down);
+    if (st == MOE_OK && L.Is > 0) {
+        st = pack(L.sg_codes, L.Is, L.H, po.psg, 1, po.sh_gate);
+        if (st == MOE_OK) st = pack(L.su_codes, L.Is, L.H, po.psg, 1, po.sh_up);
+        if (st == MOE_OK) st = pack(L.sd_codes, L.H, L.Is, po.psd, 1, po.sh_down);
+    }
+    return st;
 }
 
 // -------------------------------------------------------------------------------- launch

@@ -29,11 +29,11 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert {"moe_route", "moe_permute", "moe_experts_decode", "moe_experts_prefill", "moe_combine", "moe_layer",
             "moe_workspace_size", "moe_status_string", "moe_abi_version", "moe_kv_encode", "moe_kv_gather",
-            "moe_experts_prefill_f16"} <= set(names)
+            "moe_experts_prefill_f16", "moe_prefill_codes_bytes", "moe_pack_prefill_codes"} <= set(names)
     L = ctypes.CDLL(moe.library_path)
     for n in names:
         assert hasattr(L, n), n
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == 3
     assert moe.moe_status_string(moe.MOE_ERR_WORKSPACE) == "workspace too small"
 
 
@@ -122,6 +122,33 @@ def test_host_validation_rejects_before_launch():
     # fp16 rows must be 16-byte aligned
     assert _raw("moe_experts_prefill_f16", ref(d.c), ref(w), fake, 8, fake, fake, fake + 2, fake, fake, 1 << 40,
                 None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_prefill_codes_size_and_checks():
+    """The packed copy's size from its definition in moe.h (every matrix ceil(N / 32) ceil(K / 64)
+    pieces of 64 BB bytes; E gates and ups of I x H, E downs of H x I, the shared three), 0 for an
+    invalid descriptor; moe_pack_prefill_codes refuses a missing or misaligned destination or a
+    misaligned prefill_codes in the weights before launching anything (fake aligned device
+    addresses, no GPU here)."""
+    ref = ctypes.byref
+    for fmt, BB in ((moe.MOE_Q8_B32, 32), (moe.MOE_Q4_B32, 16), (moe.MOE_Q2_B32, 8)):
+        for E, H, I, Is in ((5, 800, 160, 96), (256, 2048, 512, 512), (3, 64, 32, 0)):
+            d = D(H=H, I=I, E=E, k=2, Is=Is, fmt=fmt)
+
+            def P(N, K):
+                return -(-N // 32) * -(-K // 64) * 64 * BB
+            want = E * (2 * P(I, H) + P(H, I)) + ((2 * P(Is, H) + P(H, Is)) if Is else 0)
+            assert _raw("moe_prefill_codes_bytes", ref(d.c)) == want
+    assert _raw("moe_prefill_codes_bytes", ref(D(H=33).c)) == 0
+    d, fake = D(), 0x10000
+    q = moe._QMat(fake, fake)
+    w = moe._Weights(fake, None, q, q, q, q, q, q, None)
+    assert _raw("moe_pack_prefill_codes", ref(d.c), ref(w), None, None) == moe.MOE_ERR_INVALID_ARG
+    assert _raw("moe_pack_prefill_codes", ref(d.c), ref(w), fake + 8, None) == moe.MOE_ERR_INVALID_ARG
+    w_bad = moe._Weights(fake, None, q, q, q, q, q, q, fake + 4)
+    assert _raw("moe_pack_prefill_codes", ref(d.c), ref(w_bad), fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert _raw("moe_layer", ref(d.c), ref(w_bad), fake, 100, fake, None, None, None, fake, 1 << 40, None) == \
+        moe.MOE_ERR_INVALID_ARG
 
 
 def test_decode_lds_limit_settled_before_launch():

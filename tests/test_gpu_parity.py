@@ -398,6 +398,56 @@ def test_experts_prefill_hot_experts():
     assert_float_match(y_shared.cpu().numpy(), ref["y_shared"], "y_shared")
 
 
+@pytest.mark.parametrize("fmt,T,H,I,Is,E,k", [(synth.Q8, 200, 800, 160, 96, 16, 4),
+                                              (synth.Q4, 300, 256, 128, 64, 16, 4),
+                                              (synth.Q2, 130, 800, 160, 0, 16, 4),
+                                              (synth.Q4, 700, 512, 96, 64, 8, 2)])
+def test_packed_prefill_codes_bitwise(fmt, T, H, I, Is, E, k):
+    """The grouped GEMMs reading the packed copy of the codes (moe_pack_prefill_codes) give the same
+    bits as reading the row-major codes (same operands, same MFMA order): y_sorted / y_shared of
+    moe_experts_prefill and the output of moe_layer. H = 800 and I = 160 leave a half-empty last K
+    step in every matrix. The row-major path is checked against the oracle elsewhere; Y of the
+    packed path is also checked against it here."""
+    _need_gpu()
+    spec = synth.LayerSpec("pk", T=T, H=H, E=E, k=k, I=I, Is=Is, fmt=fmt, zipf=True, cfg_id=130 + fmt)
+    d = synth.make_layer(spec)
+    say("packed codes", synth.FMT_NAMES[fmt], "T=%d H=%d I=%d Is=%d" % (T, H, I, Is))
+    L = dev_layer(spec, d, dmt=1)
+    xd = dev_x(d["x"])
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    _, ids, p = moe.moe_route(L, xd, logits=logits)
+    offsets, perm, inv = moe.moe_permute(L, ids)
+    ys0, ysh0 = moe.moe_experts_prefill(L, xd, offsets, perm)
+    Y0 = moe.moe_layer(L, xd)
+    L.pack_prefill_codes()
+    ys1, ysh1 = moe.moe_experts_prefill(L, xd, offsets, perm)
+    Y1 = moe.moe_layer(L, xd)
+    torch.cuda.synchronize()
+    assert torch.equal(ys0, ys1)
+    if Is:
+        assert torch.equal(ysh0, ysh1)
+    assert torch.equal(Y0, Y1)
+    O = orc_layer(spec, d)
+    rows = list(range(0, T, max(1, T // 16)))
+    ref = oracle_tokens(O, d["x"], logits.cpu().numpy(), rows)
+    assert_float_match(Y1.cpu().numpy()[rows], ref["Y"], "Y (packed)")
+
+
+def test_packed_prefill_codes_prefill8k_bitwise():
+    """The 8192-token chunk the benchmark times: moe_layer with the packed codes gives the same
+    bits as with the row-major codes."""
+    _need_gpu()
+    spec, d = host_layer("prefill8k")
+    say("packed codes: prefill8k")
+    L = dev_layer(spec, d)
+    xd = dev_x(d["x"])
+    Y0 = moe.moe_layer(L, xd)
+    L.pack_prefill_codes()
+    Y1 = moe.moe_layer(L, xd)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0, Y1)
+
+
 @pytest.mark.parametrize("fmt,T,H,I,Is", [(synth.Q4, 300, 256, 128, 64), (synth.Q8, 200, 800, 160, 96),
                                            (synth.Q2, 130, 800, 160, 0)])
 def test_experts_prefill_f16_entry(fmt, T, H, I, Is):
