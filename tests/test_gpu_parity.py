@@ -277,7 +277,7 @@ def small_prefill_spec(fmt, T, E=16, k=4, Is=64, H=256, I=128, zipf=True):
 @pytest.mark.parametrize("T", [5, 130, 300])
 def test_layer_prefill_small(fmt, T):
     """Prefill path at sizes the oracle finishes in seconds: several row tiles and ragged tails (the
-    grouped GEMMs forced at T = 5, which the default switch would send to the decode kernels)."""
+    grouped GEMMs forced at every T through decode_max_tokens = 1)."""
     _need_gpu()
     spec = small_prefill_spec(fmt, T)
     d = synth.make_layer(spec)

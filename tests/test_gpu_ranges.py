@@ -90,7 +90,8 @@ def test_decode_matrix_and_ranges(fmt, T):
     Is = 64 if T % 2 == 0 else 0
     spec = synth.LayerSpec("dm", T=T, H=512, E=E, k=4, I=160, Is=Is, fmt=fmt, zipf=True, cfg_id=200 + fmt)
     d = synth.make_layer(spec)
-    L = moe.DeviceLayer.from_host(moe.LayerDesc.from_spec(spec), d)
+    # moe_layer on the decode kernels at every T here (its default switch is lower)
+    L = moe.DeviceLayer.from_host(moe.LayerDesc.from_spec(spec, decode_max_tokens=8), d)
     O = oracle.Layer.from_synth(spec, d)
     for label, x in activation_cases(spec, T, 3 + T):
         say(synth.FMT_NAMES[fmt], "T=%d E=%d Is=%d" % (T, E, Is), label)
