@@ -293,8 +293,11 @@ moe_status moe_kv_gather(const int8_t* codes, const uint16_t* scales, int32_t n_
  * order), then block 2s + 1 of the same rows (zero bytes past the row's last block). A matrix takes
  * ceil(N / 32) ceil(K / 64) 64 BB bytes, its pieces group-major; the matrices follow one another:
  * the E routed gate matrices (N = I, K = H), the E up matrices, the E down matrices (N = H, K = I),
- * then the shared gate, up and down (N = Is or H, K = H or Is) when shared_inter > 0. Scales are
- * not copied (they stay in the moe_qmat arrays). The copy must be made again if the codes change.
+ * then the shared gate, up and down (N = Is or H, K = H or Is) when shared_inter > 0. The scales of
+ * the same matrices follow, in the same order: a matrix's scales in pieces of 32 rows x 8 blocks
+ * (512 bytes, row by row, 8 fp16 scales each, zero past the rows or the row's last block), group-
+ * major, ceil(N / 32) ceil(K / 256) 512 bytes per matrix. The copy must be made again if the codes
+ * or scales change.
  */
 /* Bytes of the packed copy of the expert codes (host only; 0 for an invalid descriptor). */
 size_t moe_prefill_codes_bytes(const moe_layer_desc* desc);

@@ -18,15 +18,22 @@ struct LayerView {
     __host__ __device__ int Imax() const { return I > Is ? I : Is; }
 };
 
-// The packed codes (moe_pack_prefill_codes): a matrix of N rows and K columns in pieces of 32 rows x
-// 64 columns (64 BB bytes: block 2s of the 32 rows, then block 2s + 1), group-major; the matrices in
-// the order E gates, E ups, E downs, then the shared gate, up and down.
+// The packed copy (moe_pack_prefill_codes): the codes of a matrix of N rows and K columns in pieces
+// of 32 rows x 64 columns (64 BB bytes: block 2s of the 32 rows, then block 2s + 1), group-major;
+// its scales in pieces of 32 rows x 8 blocks (512 bytes: row by row, 8 scales each), group-major;
+// the code matrices in the order E gates, E ups, E downs, shared gate, up, down, then the scale
+// matrices in the same order.
 __host__ __device__ inline int64_t packed_mat_bytes(int N, int K, int fmt) {
     return (int64_t)((N + 31) / 32) * ((K + 63) / 64) * 64 * block_bytes(fmt);
 }
+__host__ __device__ inline int64_t packed_scale_bytes(int N, int K) {
+    return (int64_t)((N + 31) / 32) * ((K / 32 + 7) / 8) * 512;
+}
 struct PackedOffsets {
-    int64_t pg, pd, psg, psd;                         // bytes of one gate/up, down, shared gate/up, shared down
-    int64_t gate, up, down, sh_gate, sh_up, sh_down;  // where each stack starts
+    int64_t pg, pd, psg, psd;                         // code bytes of one gate/up, down, shared gate/up, shared down
+    int64_t gate, up, down, sh_gate, sh_up, sh_down;  // where each code stack starts
+    int64_t qg, qd, qsg, qsd;                         // scale bytes of the same matrices
+    int64_t s_gate, s_up, s_down, s_sh_gate, s_sh_up, s_sh_down;   // where each scale stack starts
     int64_t total;
 };
 __host__ __device__ inline PackedOffsets packed_offsets(const LayerView& L) {
@@ -41,7 +48,17 @@ __host__ __device__ inline PackedOffsets packed_offsets(const LayerView& L) {
     o.sh_gate = o.down + (int64_t)L.E * o.pd;
     o.sh_up = o.sh_gate + o.psg;
     o.sh_down = o.sh_up + o.psg;
-    o.total = o.sh_down + o.psd;
+    o.qg = packed_scale_bytes(L.I, L.H);
+    o.qd = packed_scale_bytes(L.H, L.I);
+    o.qsg = L.Is > 0 ? packed_scale_bytes(L.Is, L.H) : 0;
+    o.qsd = L.Is > 0 ? packed_scale_bytes(L.H, L.Is) : 0;
+    o.s_gate = o.sh_down + o.psd;
+    o.s_up = o.s_gate + (int64_t)L.E * o.qg;
+    o.s_down = o.s_up + (int64_t)L.E * o.qg;
+    o.s_sh_gate = o.s_down + (int64_t)L.E * o.qd;
+    o.s_sh_up = o.s_sh_gate + o.qsg;
+    o.s_sh_down = o.s_sh_up + o.qsg;
+    o.total = o.s_sh_down + o.qsd;
     return o;
 }
 // Writes the packed copy of L's codes to dst (16-byte aligned, packed_offsets(L).total bytes).

@@ -564,6 +564,9 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
     // lane offsets of block g of row wrow (tile 0; tile 1 adds its row difference), and the code
     // bytes the buffer base advances per K step
     int bvo0 = (int)(wrow[0] * rb) + g * BB, bdv = (int)((wrow[1] - wrow[0]) * rb), cstep = 2 * BB;
+    // SD: where each lane's 16 bytes of scales start, and how far they move per group of 4 steps
+    const char* sgsrc = nullptr;
+    int sgstep = 16;
     const int svo0 = (wrow[0] * nb + g) * 2, sdv = (wrow[1] - wrow[0]) * nb * 2;
     if (L.pk) {
         // the packed copy: the piece of (32-row group, step) is 64 BB bytes and lane (frow, g) reads
@@ -587,13 +590,22 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
         cstep = 64 * BB;
         bvo0 = grp[0] * nsteps * cstep + BB * (frow + 32 * g);
         bdv = (grp[1] - grp[0]) * nsteps * cstep;
+        if constexpr (SD) {
+            // packed scales: the piece of (32-row group, 4 steps) is 512 bytes, row r at 16 r
+            const int j = lane / 32;
+            int64_t sb;
+            if constexpr (GATEUP) sb = shared ? (j ? po.s_sh_up : po.s_sh_gate) : (j ? po.s_up : po.s_gate) + (int64_t)td.group * po.qg;
+            else sb = shared ? po.s_sh_down : po.s_down + (int64_t)td.group * po.qd;
+            sgsrc = reinterpret_cast<const char*>(L.pk) + sb + (int64_t)grp[j] * (nb / 8) * 512 + 16 * (lane % 32);
+            sgstep = 512;
+        }
     }
     // SD: lane l of wave w loads 16 bytes (the 8 scales of 4 K steps) of row wrow[l / 32] of tile
-    // l / 32 for rows 32 w + l % 32; they land at byte 16 l of the wave's 1 KB of the group's buffer
-    const char* sgsrc = nullptr;
+    // l / 32 for rows 32 w + l % 32 (from the packed copy when there is one); they land at byte
+    // 16 l of the wave's 1 KB of the group's buffer
     if constexpr (SD) {
         const int j = lane / 32;
-        sgsrc = reinterpret_cast<const char*>(smat[j]) + (int64_t)wrow[j] * nb * 2;
+        if (!sgsrc) sgsrc = reinterpret_cast<const char*>(smat[j]) + (int64_t)wrow[j] * nb * 2;
     }
     uint8_t* sbuf = smem + kStages * kStageBytes;
 
@@ -631,7 +643,7 @@ __device__ __forceinline__ void gemm_tile(const LayerView& L, int T, const TileD
             // the scales of steps t .. t + 3 (blocks 2 t .. 2 t + 7), issued by the steps that start a
             // group of four (known at compile time)
             if constexpr (SD && decltype(group_start)::value)
-                __builtin_amdgcn_global_load_lds(sgsrc + 4 * (t & ~3),
+                __builtin_amdgcn_global_load_lds(sgsrc + sgstep * (t >> 2),
                                                  (lds_void*)(sbuf + ((t >> 2) & 1) * (kGW * 1024) + wave * 1024), 16,
                                                  0, 0);
         }
@@ -974,6 +986,34 @@ __global__ __launch_bounds__(256) void k_pack_codes(const uint8_t* __restrict__ 
     *reinterpret_cast<uint32_t*>(dst + m * pmat + o) = v;
 }
 
+// One thread per 16 bytes (8 scales) of the packed scales of `count` matrices of N rows and nb
+// blocks (row-major [N][nb] each, one after another): piece (group r, blocks 8q .. 8q + 7) holds
+// row 32 r + i at 16 i; zero past the rows or blocks.
+__global__ __launch_bounds__(256) void k_pack_scales(const uint16_t* __restrict__ src, int N, int nb, int64_t pmat,
+                                                     int count, uint8_t* __restrict__ dst) {
+    const int64_t units = pmat / 16;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= units * count) return;
+    const int64_t m = i / units, u = i % units;
+    const int nq = (nb + 7) / 8;
+    const int64_t piece = u / 32;
+    const int rr = (int)(u % 32);
+    const int r = (int)(piece / nq), q = (int)(piece % nq);
+    const int row = 32 * r + rr;
+    uint16_t v[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const int blk = 8 * q + b;
+        v[b] = (row < N && blk < nb) ? src[(m * N + row) * nb + blk] : (uint16_t)0;
+    }
+    uint4 o;
+    o.x = v[0] | ((uint32_t)v[1] << 16);
+    o.y = v[2] | ((uint32_t)v[3] << 16);
+    o.z = v[4] | ((uint32_t)v[5] << 16);
+    o.w = v[6] | ((uint32_t)v[7] << 16);
+    *reinterpret_cast<uint4*>(dst + m * pmat + 16 * u) = o;
+}
+
 moe_status launch_pack_codes(const LayerView& L, uint8_t* dst, hipStream_t s) {
     const PackedOffsets po = packed_offsets(L);
     auto pack = [&](const uint8_t* src, int N, int K, int64_t pmat, int count, int64_t at) -> moe_status {
@@ -983,13 +1023,26 @@ moe_status launch_pack_codes(const LayerView& L, uint8_t* dst, hipStream_t s) {
         MOE_LAUNCH_CHECK();
         return MOE_OK;
     };
+    auto pack_s = [&](const uint16_t* src, int N, int K, int64_t pmat, int count, int64_t at) -> moe_status {
+        const int64_t n = pmat / 16 * count;
+        hipLaunchKernelGGL(k_pack_scales, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, N, K / 32, pmat,
+                           count, dst + at);
+        MOE_LAUNCH_CHECK();
+        return MOE_OK;
+    };
     moe_status st = pack(L.g_codes, L.I, L.H, po.pg, L.E, po.gate);
     if (st == MOE_OK) st = pack(L.u_codes, L.I, L.H, po.pg, L.E, po.up);
     if (st == MOE_OK) st = pack(L.d_codes, L.H, L.I, po.pd, L.E, po.down);
+    if (st == MOE_OK) st = pack_s(L.g_scales, L.I, L.H, po.qg, L.E, po.s_gate);
+    if (st == MOE_OK) st = pack_s(L.u_scales, L.I, L.H, po.qg, L.E, po.s_up);
+    if (st == MOE_OK) st = pack_s(L.d_scales, L.H, L.I, po.qd, L.E, po.s_down);
     if (st == MOE_OK && L.Is > 0) {
         st = pack(L.sg_codes, L.Is, L.H, po.psg, 1, po.sh_gate);
         if (st == MOE_OK) st = pack(L.su_codes, L.Is, L.H, po.psg, 1, po.sh_up);
         if (st == MOE_OK) st = pack(L.sd_codes, L.H, L.Is, po.psd, 1, po.sh_down);
+        if (st == MOE_OK) st = pack_s(L.sg_scales, L.Is, L.H, po.qsg, 1, po.s_sh_gate);
+        if (st == MOE_OK) st = pack_s(L.su_scales, L.Is, L.H, po.qsg, 1, po.s_sh_up);
+        if (st == MOE_OK) st = pack_s(L.sd_scales, L.H, L.Is, po.qsd, 1, po.s_sh_down);
     }
     return st;
 }

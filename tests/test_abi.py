@@ -126,7 +126,8 @@ def test_host_validation_rejects_before_launch():
 
 def test_prefill_codes_size_and_checks():
     """The packed copy's size from its definition in moe.h (every matrix ceil(N / 32) ceil(K / 64)
-    pieces of 64 BB bytes; E gates and ups of I x H, E downs of H x I, the shared three), 0 for an
+    pieces of 64 BB code bytes and ceil(N / 32) ceil(K / 256) pieces of 512 scale bytes; E gates and
+    ups of I x H, E downs of H x I, the shared three), 0 for an
     invalid descriptor; moe_pack_prefill_codes refuses a missing or misaligned destination or a
     misaligned prefill_codes in the weights before launching anything (fake aligned device
     addresses, no GPU here)."""
@@ -135,8 +136,8 @@ def test_prefill_codes_size_and_checks():
         for E, H, I, Is in ((5, 800, 160, 96), (256, 2048, 512, 512), (3, 64, 32, 0)):
             d = D(H=H, I=I, E=E, k=2, Is=Is, fmt=fmt)
 
-            def P(N, K):
-                return -(-N // 32) * -(-K // 64) * 64 * BB
+            def P(N, K):   # codes and scales of one matrix
+                return -(-N // 32) * -(-K // 64) * 64 * BB + -(-N // 32) * -(-K // 256) * 512
             want = E * (2 * P(I, H) + P(H, I)) + ((2 * P(Is, H) + P(H, Is)) if Is else 0)
             assert _raw("moe_prefill_codes_bytes", ref(d.c)) == want
     assert _raw("moe_prefill_codes_bytes", ref(D(H=33).c)) == 0

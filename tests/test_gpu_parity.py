@@ -401,12 +401,15 @@ def test_experts_prefill_hot_experts():
 @pytest.mark.parametrize("fmt,T,H,I,Is,E,k", [(synth.Q8, 200, 800, 160, 96, 16, 4),
                                               (synth.Q4, 300, 256, 128, 64, 16, 4),
                                               (synth.Q2, 130, 800, 160, 0, 16, 4),
-                                              (synth.Q4, 700, 512, 96, 64, 8, 2)])
+                                              (synth.Q4, 700, 512, 96, 64, 8, 2),
+                                              (synth.Q8, 260, 512, 256, 256, 16, 4),
+                                              (synth.Q2, 200, 256, 256, 0, 8, 2)])
 def test_packed_prefill_codes_bitwise(fmt, T, H, I, Is, E, k):
     """The grouped GEMMs reading the packed copy of the codes (moe_pack_prefill_codes) give the same
     bits as reading the row-major codes (same operands, same MFMA order): y_sorted / y_shared of
     moe_experts_prefill and the output of moe_layer. H = 800 and I = 160 leave a half-empty last K
-    step in every matrix. The row-major path is checked against the oracle elsewhere; Y of the
+    step in every matrix; where K is a multiple of 256 (H = 256 or 512, I or Is = 256) the GEMMs
+    also read the packed scales. The row-major path is checked against the oracle elsewhere; Y of the
     packed path is also checked against it here."""
     _need_gpu()
     spec = synth.LayerSpec("pk", T=T, H=H, E=E, k=k, I=I, Is=Is, fmt=fmt, zipf=True, cfg_id=130 + fmt)
