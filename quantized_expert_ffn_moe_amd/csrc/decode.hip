@@ -189,24 +189,28 @@ __device__ __forceinline__ float pair_offset(int p) {
 // is subtracted (Q4: offset 8, Q8: offset 128, Q2: offset 1.5, the level being c - 1.5). With
 // SUB = false the subtraction is left out: each half is pair_offset(p) + f * level, and the caller
 // removes pair_offset(p) times the pair's activations once per block.
+//
+// The sign flip of the two's-complement codes (XOR with the code's top bit) and the OR with 1024.0
+// touch disjoint bits, so they merge into one constant: ((w & mask) ^ (flip & mask | 1024.0)) is a
+// single three-input bit operation per pair.
 template <int FMT, bool SUB = true>
 __device__ __forceinline__ void code_pairs(const uint32_t* w, uint32_t (&pr)[16]) {
     if constexpr (FMT == MOE_Q4_B32) {
+        constexpr uint32_t kLo = 0x00080008u | kMagic, kHi = 0x00800080u | kMagic;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const uint32_t u = w[d] ^ 0x88888888u;
-            const uint32_t v = u >> 8;
-            pr[4 * d + 0] = sub_k<1032, SUB>((u & 0x000F000Fu) | kMagic);
-            pr[4 * d + 1] = sub_k<1152, SUB>((u & 0x00F000F0u) | kMagic);
-            pr[4 * d + 2] = sub_k<1032, SUB>((v & 0x000F000Fu) | kMagic);
-            pr[4 * d + 3] = sub_k<1152, SUB>((v & 0x00F000F0u) | kMagic);
+            const uint32_t u = w[d], v = w[d] >> 8;
+            pr[4 * d + 0] = sub_k<1032, SUB>((u & 0x000F000Fu) ^ kLo);
+            pr[4 * d + 1] = sub_k<1152, SUB>((u & 0x00F000F0u) ^ kHi);
+            pr[4 * d + 2] = sub_k<1032, SUB>((v & 0x000F000Fu) ^ kLo);
+            pr[4 * d + 3] = sub_k<1152, SUB>((v & 0x00F000F0u) ^ kHi);
         }
     } else if constexpr (FMT == MOE_Q8_B32) {
+        constexpr uint32_t kB = 0x00800080u | kMagic;
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
-            const uint32_t u = w[d] ^ 0x80808080u;
-            pr[2 * d + 0] = sub_k<1152, SUB>((u & 0x00FF00FFu) | kMagic);
-            pr[2 * d + 1] = sub_k<1152, SUB>(((u >> 8) & 0x00FF00FFu) | kMagic);
+            pr[2 * d + 0] = sub_k<1152, SUB>((w[d] & 0x00FF00FFu) ^ kB);
+            pr[2 * d + 1] = sub_k<1152, SUB>(((w[d] >> 8) & 0x00FF00FFu) ^ kB);
         }
     } else {
 #pragma unroll
@@ -322,13 +326,26 @@ __device__ __forceinline__ void bf16x32_to_f32(const uint4 (&raw)[4], float (&v)
 
 // ----------------------------------------------------------------------------------- K2 gate/up
 
-// Gate/up rows per K2 wave and waves per K2 block: 2 rows and up to 16 waves (128 VGPRs); for three
-// or four tokens 3 rows and up to 12 waves (168 VGPRs, so that the 8-bit codes of 3 rows and 4
-// tokens' sums stay in registers), i.e. 9216 rows per pass over 256 CUs: the union of the chosen
-// experts (about 16 + the shared one, 8704 rows) then takes one pass instead of two; for five to
-// eight tokens 2 rows and up to 8 waves (256 VGPRs: the sums of 8 tokens stay in registers).
-__host__ __device__ constexpr int gateup_rows(int T) { return T >= 5 ? 2 : T >= 3 ? 3 : 2; }
-__host__ __device__ constexpr int gateup_max_waves(int T) { return T >= 5 ? 8 : T >= 3 ? 12 : 16; }
+// Sum over each row of 16 lanes (lanes 16r .. 16r + 15); lane 16r holds its row's sum.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __uint_as_float(dpp_u32<0xb1>(__float_as_uint(v)));    // quad_perm [1,0,3,2]
+    v += __uint_as_float(dpp_u32<0x4e>(__float_as_uint(v)));    // quad_perm [2,3,0,1]
+    v += __uint_as_float(dpp_u32<0x141>(__float_as_uint(v)));   // row_half_mirror
+    v += __uint_as_float(dpp_u32<0x140>(__float_as_uint(v)));   // row_mirror
+    return v;
+}
+
+// Gate/up rows per K2 wave and waves per K2 block. One or two tokens: 4 rows, one per 16-lane row
+// of the wave (each lane 4 of the row's 32-blocks per step), so that a row's dot product ends in a
+// 16-lane sum and the four rows share one epilogue; up to 8 waves (256 VGPRs: the 8-bit codes of
+// 4 blocks of gate and up stay in registers), 8192 rows per pass over 256 CUs. Three or four tokens: 3 rows
+// over all 64 lanes and up to 12 waves (168 VGPRs, so that the 8-bit codes of 3 rows and 4 tokens'
+// sums stay in registers), i.e. 9216 rows per pass over 256 CUs: the union of the chosen experts
+// (about 16 + the shared one, 8704 rows) then takes one pass instead of two; for five to eight
+// tokens 2 rows and up to 8 waves (256 VGPRs: the sums of 8 tokens stay in registers).
+__host__ __device__ constexpr int gateup_rows(int T) { return T >= 5 ? 2 : T >= 3 ? 3 : 4; }
+__host__ __device__ constexpr bool gateup_row_lanes(int T) { return T <= 2; }
+__host__ __device__ constexpr int gateup_max_waves(int T) { return T >= 5 ? 8 : T >= 3 ? 12 : 8; }
 constexpr int kDownRows = 1;      // output rows per K3 wave
 constexpr int kDownWaves = 8;     // waves per K3 block (two per SIMD hide each other's latency)
 constexpr int kDownThreads = kDownWaves * kWave;
@@ -458,6 +475,98 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
         for (int i = threadIdx.x; i < (int)(sizeof(DecodePlan) / 4); i += blockDim.x) dst[i] = src[i];
     }
 
+    if constexpr (gateup_row_lanes(T)) {
+        // tasks of 4 consecutive rows of one expert (I and Is are multiples of 32), row n0 + g on
+        // lanes 16g .. 16g + 15, lane li of a row taking the 32-blocks li, li + 16, ...: those of
+        // the distinct chosen experts (slot order) then the shared expert's, one task per wave and
+        // step, the grid striding over them
+        static_assert(R == 4, "one row per 16 lanes");
+        constexpr int JB = 4;                      // 32-blocks per lane whose loads are in flight together
+        const int g = lane >> 4, li = lane & 15;
+        const int gw = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (int)(blockDim.x / kWave) + wave);
+        const int tstride = (int)gridDim.x * (int)(blockDim.x / kWave);
+        const int tpeI = L.I / 4, tpeS = L.Is / 4;
+        const int nrouted = P.nU * tpeI;
+        const int ntasks = nrouted + tpeS;
+        const int64_t rb = row_bytes(FMT, H);
+        for (int tk = gw; tk < ntasks; tk += tstride) {   // uniform per wave
+            int slot, n;
+            const uint8_t *gc, *uc;
+            const uint16_t *gsp, *usp;
+            if (tk < nrouted) {
+                slot = tk / tpeI;
+                n = (tk - slot * tpeI) * 4 + g;
+                const int64_t row = (int64_t)P.expert[slot] * L.I + n;
+                gc = L.g_codes + row * rb; uc = L.u_codes + row * rb;
+                gsp = L.g_scales + row * nb; usp = L.u_scales + row * nb;
+            } else {
+                slot = 64;  // shared
+                n = (tk - nrouted) * 4 + g;
+                gc = L.sg_codes + (int64_t)n * rb; uc = L.su_codes + (int64_t)n * rb;
+                gsp = L.sg_scales + (int64_t)n * nb; usp = L.su_scales + (int64_t)n * nb;
+            }
+            const uint32_t mask = slot < 64 ? P.tokmask[slot] : (1u << T) - 1u;
+            float ga[T], ua[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) ga[t] = ua[t] = 0.f;
+            for (int j0 = 0; j0 * 16 < nb; j0 += JB) {   // uniform
+                uint32_t wg[JB][8], wu[JB][8];
+                uint16_t sgb[JB], sub[JB];
+                int bj[JB];
+                // every load of the step issued before any is used (scales first); blocks past the
+                // row's end read its last block (result unused)
+#pragma unroll
+                for (int jj = 0; jj < JB; ++jj) {
+                    bj[jj] = li + 16 * (j0 + jj);
+                    const int bc = min(bj[jj], nb - 1);
+                    sgb[jj] = gsp[bc];
+                    sub[jj] = usp[bc];
+                }
+#pragma unroll
+                for (int jj = 0; jj < JB; ++jj) {
+                    const int bc = min(bj[jj], nb - 1);
+                    load_codes<FMT>(gc + (int64_t)bc * block_bytes(FMT), wg[jj]);
+                    load_codes<FMT>(uc + (int64_t)bc * block_bytes(FMT), wu[jj]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                auto blockdot = [&](const uint32_t (&w)[8], uint16_t sc, int b, float (&acc)[T]) __attribute__((always_inline)) {
+                    uint32_t pw[16];
+                    code_pairs<FMT, false>(w, pw);
+                    const float sf = f16_to_f32(sc);
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        uint32_t xr[16];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const uint4 v = xq[((size_t)t * 4 + c) * nb + b];
+                            xr[4 * c] = v.x; xr[4 * c + 1] = v.y; xr[4 * c + 2] = v.z; xr[4 * c + 3] = v.w;
+                        }
+                        float d = 0.f;
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) d = dot2(pw[j], xr[j], d);
+                        acc[t] += sf * (d - xc[t * nb + b]);
+                    }
+                };
+#pragma unroll
+                for (int jj = 0; jj < JB; ++jj) {
+                    if (bj[jj] < nb) {
+                        blockdot(wg[jj], sgb[jj], bj[jj], ga);
+                        blockdot(wu[jj], sub[jj], bj[jj], ua);
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const float gs_ = row16_sum(ga[t]);
+                const float us_ = row16_sum(ua[t]);
+                if (li == 0 && ((mask >> t) & 1u)) {
+                    const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
+                    put_staged<FMT>(reinterpret_cast<_Float16*>(h + (size_t)row * Imax), Imax / 32, n,
+                                    silu_mul_scaled(gs_, us_, pow2f(-P.xexp[t])));
+                }
+            }
+        }
+    } else {
     // tasks of R consecutive rows of one expert (the last task of an expert may hold fewer): those
     // of the distinct chosen experts (slot order) then the shared expert's, one task per wave and
     // step, the grid striding over them (a grid of at most one block per CU)
@@ -554,13 +663,15 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
                 }
             }
     }
+    }
 }
 
 // ----------------------------------------------------------------------------------- K3 down
 
-// LDS of k_dec_down: plan | first[E] | ids/p [64] | hq[rows][8][nbm] uint4 (fp16 hi/lo pairs;
-// lanes reading consecutive 32-blocks hit consecutive banks) | partials [waves][RPW][T][items_cap]
-// (per-pair outputs only)
+// LDS of k_dec_down: plan | (unused, E ints) | eoff[64] int64 | hq[rows][8][nbm] uint4 (fp16 hi/lo
+// pairs; lanes reading consecutive 32-blocks hit consecutive banks) | partials
+// [waves][RPW][T][items_cap] (per-pair outputs only). The layout up to hq is the gate/up kernel's
+// (lds_head), whose ids/p arrays (512 bytes) hold eoff here.
 static size_t down_smem_bytes(int T, int k, int E, int Imax, int items_cap, bool combine) {
     size_t b = lds_head(E) + (size_t)(T * k + T) * (Imax / 32) * 128;
     if (!combine) b += (size_t)kDownWaves * kDownRows * T * items_cap * 4;
@@ -583,6 +694,8 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
     constexpr int RPW = kDownRows, MAXJ = down_batch(T);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     DecodePlan& P = *reinterpret_cast<DecodePlan*>(smem);
+    // per slot: element offset of the expert's down scales (its codes sit block_bytes times further)
+    int64_t* eoff = reinterpret_cast<int64_t*>(smem + align_up(sizeof(DecodePlan), 16) + align_up((size_t)L.E * 4, 16));
     uint4* hq = reinterpret_cast<uint4*>(smem + lds_head(L.E));
     const int Imax = L.Imax();
     const int nbm = Imax / 32;
@@ -611,17 +724,33 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
         uint32_t* pd = reinterpret_cast<uint32_t*>(&P);
 #pragma unroll
         for (int i = 0; i < (kPlanWords + kDownThreads - 1) / kDownThreads; ++i) {
+            // unconditional (threads past the end write the last word again, with its own value):
+            // a conditional store would let the compiler sink the load behind the h loads
             const int w = (int)threadIdx.x + kDownThreads * i;
-            if (w < kPlanWords) pd[w] = pw[i];
+            pd[min(w, kPlanWords - 1)] = pw[i];
         }
+        // plan words 1 .. 64 are expert[0 .. 63] (nU comes first): their threads turn them into
+        // the slots' matrix offsets once, instead of every lane per item
+        static_assert(offsetof(DecodePlan, expert) == 4, "expert[] follows nU");
+        const int s = (int)threadIdx.x - 1;
+        if (s >= 0 && s < 64) eoff[s] = (int64_t)(int)pw[0] * L.H * (L.I / 32);
     }
     __syncthreads();
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const int H = L.H;
     const int nbI = L.I / 32, nbS = L.Is / 32;
     const int nU = P.nU;
-    const int64_t rbI = row_bytes(FMT, L.I), rbS = row_bytes(FMT, L.Is);
     const int m0 = (blockIdx.x * kDownWaves + wave) * RPW;
+    // per output row of the wave: element offsets of the row within a routed expert's scales and
+    // within the shared expert's (codes: block_bytes times these)
+    int offR[RPW], offSh[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const int m = min(m0 + r, H - 1);
+        offR[r] = m * nbI;
+        offSh[r] = m * nbS;
+    }
+    const int qd = kWave / nbI, rd = kWave - qd * nbI;   // a lane's next item: 64 items further
     float* mypart = part + (size_t)wave * RPW * T * items_cap;
     // every item in one pass when the partials fit (always with the combine fused), else chunks of
     // spc routed slots and then the shared expert's blocks
@@ -653,34 +782,32 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
         const uint8_t* dcp[RPW][MAXJ];
         const uint16_t* dsp[RPW][MAXJ];
         // addresses first; an item past the end reads expert 0's first row (valid memory, result
-        // unused), so that every load below is unconditional and all of them stay in flight together
+        // unused), so that every load below is unconditional and all of them stay in flight together.
+        // Item it = (slot, block b) of the routed experts for it < nU nbI, then the shared expert's
+        // blocks; one division per batch, then 64 items further per step.
+        const int nUb = nU * nbI;
+        int it = it0 + lane + kWave * j0;
+        int slot = it / nbI, b = it - slot * nbI;
 #pragma unroll
         for (int jj = 0; jj < MAXJ; ++jj) {
-            const int it = it0 + lane + kWave * (j0 + jj);
-            const bool iv = it < it1;
-            int slot = 64, b = 0;
-            if (iv) {
-                if (it < nU * nbI) { slot = it / nbI; b = it - slot * nbI; }
-                else b = it - nU * nbI;
+            if (jj > 0) {
+                it += kWave;
+                slot += qd;
+                b += rd;
+                if (b >= nbI) { b -= nbI; ++slot; }
             }
-            slot_[jj] = slot;
-            b_[jj] = b;
-            const int e = P.expert[slot < 64 ? slot : 0];
+            const bool iv = it < it1;
+            const bool routed = iv && it < nUb;
+            const int bs = it - nUb;   // block of the shared expert
+            slot_[jj] = routed ? slot : 64;
+            b_[jj] = routed ? b : bs;
+            const int64_t eo = eoff[routed ? slot : 0];
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
-                const int m = min(m0 + r, H - 1);
                 ok[r][jj] = iv && m0 + r < H;
-                if (!iv) {
-                    dcp[r][jj] = L.d_codes;
-                    dsp[r][jj] = L.d_scales;
-                } else if (slot < 64) {
-                    const int64_t row = (int64_t)e * H + m;
-                    dcp[r][jj] = L.d_codes + row * rbI + (int64_t)b * block_bytes(FMT);
-                    dsp[r][jj] = L.d_scales + row * nbI + b;
-                } else {
-                    dcp[r][jj] = L.sd_codes + (int64_t)m * rbS + (int64_t)b * block_bytes(FMT);
-                    dsp[r][jj] = L.sd_scales + (int64_t)m * nbS + b;
-                }
+                const int64_t so = routed ? eo + (offR[r] + b) : iv ? (int64_t)(offSh[r] + bs) : (int64_t)0;
+                dcp[r][jj] = (routed || !iv ? L.d_codes : L.sd_codes) + so * block_bytes(FMT);
+                dsp[r][jj] = (routed || !iv ? L.d_scales : L.sd_scales) + so;
             }
         }
 #pragma unroll
