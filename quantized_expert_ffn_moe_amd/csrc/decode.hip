@@ -529,29 +529,47 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
                     load_codes<FMT>(uc + (int64_t)bc * block_bytes(FMT), wu[jj]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                auto blockdot = [&](const uint32_t (&w)[8], uint16_t sc, int b, float (&acc)[T]) __attribute__((always_inline)) {
-                    uint32_t pw[16];
-                    code_pairs<FMT, false>(w, pw);
-                    const float sf = f16_to_f32(sc);
+                // staged x of XB blocks read from LDS together (one round trip), then their dot
+                // products: all four blocks for one token, one block at a time for two
+                constexpr int XB = T == 1 ? JB : 1;
 #pragma unroll
-                    for (int t = 0; t < T; ++t) {
-                        uint32_t xr[16];
+                for (int j1 = 0; j1 < JB; j1 += XB) {
+                    uint4 xv[XB][T][4];
+                    float xcv[XB][T];
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const uint4 v = xq[((size_t)t * 4 + c) * nb + b];
-                            xr[4 * c] = v.x; xr[4 * c + 1] = v.y; xr[4 * c + 2] = v.z; xr[4 * c + 3] = v.w;
+                    for (int jx = 0; jx < XB; ++jx) {
+                        const int bc = min(bj[j1 + jx], nb - 1);
+#pragma unroll
+                        for (int t = 0; t < T; ++t) {
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) xv[jx][t][c] = xq[((size_t)t * 4 + c) * nb + bc];
+                            xcv[jx][t] = xc[t * nb + bc];
                         }
-                        float d = 0.f;
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) d = dot2(pw[j], xr[j], d);
-                        acc[t] += sf * (d - xc[t * nb + b]);
                     }
-                };
+                    __builtin_amdgcn_sched_barrier(0);
+                    auto blockdot = [&](const uint32_t (&w)[8], uint16_t sc, int jx, float (&acc)[T]) __attribute__((always_inline)) {
+                        uint32_t pw[16];
+                        code_pairs<FMT, false>(w, pw);
+                        const float sf = f16_to_f32(sc);
 #pragma unroll
-                for (int jj = 0; jj < JB; ++jj) {
-                    if (bj[jj] < nb) {
-                        blockdot(wg[jj], sgb[jj], bj[jj], ga);
-                        blockdot(wu[jj], sub[jj], bj[jj], ua);
+                        for (int t = 0; t < T; ++t) {
+                            float d = 0.f;
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                d = dot2(pw[4 * c], xv[jx][t][c].x, d);
+                                d = dot2(pw[4 * c + 1], xv[jx][t][c].y, d);
+                                d = dot2(pw[4 * c + 2], xv[jx][t][c].z, d);
+                                d = dot2(pw[4 * c + 3], xv[jx][t][c].w, d);
+                            }
+                            acc[t] += sf * (d - xcv[jx][t]);
+                        }
+                    };
+#pragma unroll
+                    for (int jx = 0; jx < XB; ++jx) {
+                        if (bj[j1 + jx] < nb) {
+                            blockdot(wg[j1 + jx], sgb[j1 + jx], jx, ga);
+                            blockdot(wu[j1 + jx], sub[j1 + jx], jx, ua);
+                        }
                     }
                 }
             }
@@ -778,6 +796,11 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
         uint32_t w[RPW][MAXJ][8];
         uint16_t sdb[RPW][MAXJ];
         int slot_[MAXJ], b_[MAXJ];
+        // up to four tokens: the row of h per item and token is looked up with the addresses (-1:
+        // the token did not choose the slot) and the item's h is read from LDS in groups (the
+        // registers this takes would spill from five tokens on, which keep the lookups in the loop)
+        constexpr bool kBatchH = T <= 4;
+        int hrow[MAXJ][kBatchH ? T : 1];
         bool ok[RPW][MAXJ];
         const uint8_t* dcp[RPW][MAXJ];
         const uint16_t* dsp[RPW][MAXJ];
@@ -801,6 +824,10 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
             const int bs = it - nUb;   // block of the shared expert
             slot_[jj] = routed ? slot : 64;
             b_[jj] = routed ? b : bs;
+            if constexpr (kBatchH) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) hrow[jj][t] = routed ? P.pair_of[routed ? slot : 0][t] : npairs + t;
+            }
             const int64_t eo = eoff[routed ? slot : 0];
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
@@ -841,24 +868,63 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
             for (int r = 0; r < RPW; ++r) {
                 if (!ok[r][jj]) continue;
                 uint32_t pd[16];
-                code_pairs<FMT>(w[r][jj], pd);
+                float dt[T];   // the item's dot product per token
+                if constexpr (kBatchH) {
+                    // h (hi and lo) read from LDS TB tokens at a time, the first group before the
+                    // codes are needed: the reads of a group are in flight together
+                    constexpr int TB = T < 2 ? T : 2;
+                    uint4 hv[TB][8];
+                    auto read_h = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+                        for (int tb = 0; tb < TB; ++tb) {
+                            const int t = min(t0 + tb, T - 1);
+                            const uint4* hp = hq + (size_t)max(hrow[jj][t], 0) * 8 * nbm + b;
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) hv[tb][c] = hp[(size_t)c * nbm];
+                        }
+                        __builtin_amdgcn_sched_barrier(0);   // (the scheduler would pair them with the dot products)
+                    };
+                    read_h(0);
+                    code_pairs<FMT>(w[r][jj], pd);
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        if (t > 0 && t % TB == 0) read_h(t);
+                        float d = 0.f;
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) {
+                            const int j = 4 * (c & 3);
+                            d = dot2(pd[j], hv[t % TB][c].x, d);
+                            d = dot2(pd[j + 1], hv[t % TB][c].y, d);
+                            d = dot2(pd[j + 2], hv[t % TB][c].z, d);
+                            d = dot2(pd[j + 3], hv[t % TB][c].w, d);
+                        }
+                        dt[t] = hrow[jj][t] < 0 ? 0.f : d;
+                    }
+                } else {
+                    code_pairs<FMT>(w[r][jj], pd);
+#pragma unroll
+                    for (int t = 0; t < T; ++t) {
+                        const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
+                        float d = 0.f;
+                        if (row >= 0) {
+                            const uint4* hp = hq + (size_t)row * 8 * nbm + b;
+#pragma unroll
+                            for (int c = 0; c < 8; ++c) {
+                                const uint4 hv = hp[(size_t)c * nbm];
+                                const int j = 4 * (c & 3);
+                                d = dot2(pd[j], hv.x, d);
+                                d = dot2(pd[j + 1], hv.y, d);
+                                d = dot2(pd[j + 2], hv.z, d);
+                                d = dot2(pd[j + 3], hv.w, d);
+                            }
+                        }
+                        dt[t] = d;
+                    }
+                }
                 const float sd = f16_to_f32(sdb[r][jj]);
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
-                    const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
-                    float d = 0.f;
-                    if (row >= 0) {
-                        const uint4* hp = hq + (size_t)row * 8 * nbm + b;
-#pragma unroll
-                        for (int c = 0; c < 8; ++c) {
-                            const uint4 hv = hp[(size_t)c * nbm];
-                            const int j = 4 * (c & 3);
-                            d = dot2(pd[j], hv.x, d);
-                            d = dot2(pd[j + 1], hv.y, d);
-                            d = dot2(pd[j + 2], hv.z, d);
-                            d = dot2(pd[j + 3], hv.w, d);
-                        }
-                    }
+                    const float d = dt[t];
                     if constexpr (COMBINE) {
                         const float wgt = slot < 64 ? P.pw[slot][t] : 1.f;
                         acc[r][t] += wgt * sd * d;
