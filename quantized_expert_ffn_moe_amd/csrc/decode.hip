@@ -939,29 +939,37 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // lane -> (row, slot of the chunk, token): the slot's block partials summed in order (the
-            // loops unrolled so that eight LDS reads are in flight before their in-order adds)
+            // lane -> (row, slot of the chunk or the shared expert, token): the slot's block partials
+            // summed in block order, read four at a time when the block counts allow (16-byte
+            // aligned: the partial arrays then hold multiples of four); one path for routed slots
+            // and the shared expert
             const int nr = s1 - s0, ns = nr + (has_sh ? 1 : 0);
+            const bool vec4 = ((nbI | nbS) & 3) == 0;
             for (int st = lane; st < RPW * ns * T; st += kWave) {
-                const int r = st / (ns * T), rem = st % (ns * T);
-                const int sl = rem / T, t = rem % T;
+                const int r = RPW == 1 ? 0 : st / (ns * T);
+                const int rem = st - r * ns * T;
+                const int sl = rem / T, t = rem - sl * T;
                 const int m = m0 + r;
-                if (m >= H) continue;
-                const float* pr = mypart + ((size_t)r * T + t) * items_cap;
+                const bool sh = sl >= nr;
+                const int q = sh ? t : P.pair_of[s0 + sl][t];   // y_shared row (token) or y_pairs row
                 const float sc = pow2f(-2 * P.xexp[t]);
-                if (sl < nr) {
-                    const int q = P.pair_of[s0 + sl][t];
-                    if (q < 0) continue;
-                    float sum = 0.f;
-#pragma unroll 8
-                    for (int b = 0; b < nbI; ++b) sum += pr[sl * nbI + b];
-                    y_pairs[(size_t)q * H + m] = sum * sc;
+                const int cnt = sh ? nbS : nbI;
+                const float* pr = mypart + ((size_t)r * T + t) * items_cap + (size_t)(sh ? nr : sl) * nbI;
+                float sum = 0.f;
+                if (vec4) {
+#pragma unroll 4
+                    for (int b = 0; b < cnt; b += 4) {
+                        const float4 v = *reinterpret_cast<const float4*>(pr + b);
+                        sum += v.x;
+                        sum += v.y;
+                        sum += v.z;
+                        sum += v.w;
+                    }
                 } else {
-                    float sum = 0.f;
 #pragma unroll 8
-                    for (int b = 0; b < nbS; ++b) sum += pr[nr * nbI + b];
-                    y_shared[(size_t)t * H + m] = sum * sc;
+                    for (int b = 0; b < cnt; ++b) sum += pr[b];
                 }
+                if (m < H && q >= 0) (sh ? y_shared : y_pairs)[(size_t)q * H + m] = sum * sc;
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
