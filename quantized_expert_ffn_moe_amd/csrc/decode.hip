@@ -725,6 +725,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
     constexpr int kHBatch = 3;   // uint4 of h per thread held in registers across the weight loads
     const uint4* hs = reinterpret_cast<const uint4*>(h);
     const int n4 = nrows_h * 8 * nbm;
+    const int hrot = (int)((blockIdx.x / 8) * 320u % (unsigned)n4);
     const uint32_t* ps = reinterpret_cast<const uint32_t*>(plan_g);
     uint32_t pw[(kPlanWords + kDownThreads - 1) / kDownThreads];
 #pragma unroll
@@ -736,7 +737,12 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
     const u32x4_t* hs4 = reinterpret_cast<const u32x4_t*>(h);
     u32x4_t hv0[kHBatch];
 #pragma unroll
-    for (int b = 0; b < kHBatch; ++b) hv0[b] = hs4[min((int)threadIdx.x + kDownThreads * b, n4 - 1)];
+    for (int b = 0; b < kHBatch; ++b) {
+        // every block reads all of h; each starts at its own offset, so that the blocks of an XCD do
+        // not all ask for the same lines at once
+        const int i = min((int)threadIdx.x + kDownThreads * b, n4 - 1) + hrot;
+        hv0[b] = hs4[i < n4 ? i : i - n4];
+    }
     __builtin_amdgcn_sched_barrier(0);   // h loads are issued before the wait on the plan words
     {
         uint32_t* pd = reinterpret_cast<uint32_t*>(&P);
@@ -852,11 +858,14 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
 #pragma unroll
             for (int b = 0; b < kHBatch; ++b) {
                 const int i = (int)threadIdx.x + kDownThreads * b;
-                if (i < n4) hq4[i] = hv0[b];
+                if (i < n4) hq4[i + hrot < n4 ? i + hrot : i + hrot - n4] = hv0[b];
             }
             // the rest (unrolled: each group of loads in flight together, not one round trip each)
 #pragma unroll 8
-            for (int i = (int)threadIdx.x + kDownThreads * kHBatch; i < n4; i += kDownThreads) hq[i] = hs[i];
+            for (int i = (int)threadIdx.x + kDownThreads * kHBatch; i < n4; i += kDownThreads) {
+                const int ir = i + hrot < n4 ? i + hrot : i + hrot - n4;   // the same rotation
+                hq[ir] = hs[ir];
+            }
             __syncthreads();
             h_in = true;
         }
