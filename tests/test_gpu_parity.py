@@ -119,6 +119,35 @@ def test_experts_decode_pairs(name):
     assert_float_match(Y.cpu().numpy(), comb, "combine alone")
 
 
+@pytest.mark.parametrize("fmt", [synth.Q8, synth.Q4, synth.Q2])
+@pytest.mark.parametrize("T", [1, 2])
+def test_decode_ragged_row_groups(fmt, T):
+    """The one- and two-token gate/up kernel (four rows per wave, 16 lanes per row, four 32-blocks
+    per lane and step) at a hidden size of 65 blocks (the second step of every row holds one
+    block), an intermediate size of 3 blocks (the down kernel steps a lane's items with a
+    remainder and sums per-pair partials one at a time) and a shared expert of 2 blocks:
+    moe_layer and moe_experts_decode against the oracle."""
+    _need_gpu()
+    spec = synth.LayerSpec("rg", T=T, H=2080, E=40, k=3, I=96, Is=64, fmt=fmt, zipf=True, cfg_id=240 + 4 * fmt + T)
+    d = synth.make_layer(spec)
+    say("ragged row groups", synth.FMT_NAMES[fmt], "T=%d" % T)
+    O = orc_layer(spec, d)
+    L = dev_layer(spec, d)
+    xd = dev_x(d["x"])
+    logits = torch.empty((T, spec.E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, spec.k), dtype=torch.int32, device="cuda")
+    p = torch.empty((T, spec.k), dtype=torch.float32, device="cuda")
+    Y = moe.moe_layer(L, xd, logits=logits, ids=ids, p=p)
+    y_pairs, y_shared = moe.moe_experts_decode(L, xd, ids)
+    torch.cuda.synchronize()
+    g_logits = logits.cpu().numpy()
+    check_routing(O, d["x"], g_logits, ids.cpu().numpy(), p.cpu().numpy())
+    ref = oracle_tokens(O, d["x"], g_logits, range(T))
+    assert_float_match(Y.cpu().numpy(), ref["Y"], "Y")
+    assert_float_match(y_pairs.cpu().numpy().reshape(T, spec.k, spec.H), ref["y_pairs"], "y_pairs")
+    assert_float_match(y_shared.cpu().numpy(), ref["y_shared"], "y_shared")
+
+
 @pytest.mark.parametrize("layer", [0, 47])
 def test_stack48_layer(layer):
     """One layer of the 48-layer, 512-expert, top-10, 2-bit stack at full size."""
@@ -699,7 +728,7 @@ def test_prefill_repeat_bitwise(T, H, E, k, I, Is):
     spec = synth.LayerSpec("rep", T=T, H=H, E=E, k=k, I=I, Is=Is, fmt=synth.Q4, zipf=True, cfg_id=98)
     d = synth.make_layer(spec)
     say("prefill repeat T=%d H=%d I=%d" % (T, H, I))
-    L = dev_layer(spec, d)
+    L = dev_layer(spec, d, dmt=1)   # the fused layer on the grouped GEMMs too
     xd = dev_x(d["x"])
     _, ids, p = moe.moe_route(L, xd)
     off, perm, inv = moe.moe_permute(L, ids)
