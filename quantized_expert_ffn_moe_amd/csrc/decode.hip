@@ -326,7 +326,7 @@ __device__ __forceinline__ void bf16x32_to_f32(const uint4 (&raw)[4], float (&v)
 
 // ----------------------------------------------------------------------------------- K2 gate/up
 
-// Sum over each row of 16 lanes (lanes 16r .. 16r + 15); lane 16r holds its row's sum.
+// Sum over each row of 16 lanes (lanes 16r .. 16r + 15), returned to every lane of the row.
 __device__ __forceinline__ float row16_sum(float v) {
     v += __uint_as_float(dpp_u32<0xb1>(__float_as_uint(v)));    // quad_perm [1,0,3,2]
     v += __uint_as_float(dpp_u32<0x4e>(__float_as_uint(v)));    // quad_perm [2,3,0,1]
@@ -573,15 +573,21 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
                     }
                 }
             }
+            // every lane of a row holds the row's sums (the same bits: the DPP tree adds the same
+            // pairs in every lane); lane li of the row takes token li, one epilogue for all
+            float gsel = 0.f, usel = 0.f;
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 const float gs_ = row16_sum(ga[t]);
                 const float us_ = row16_sum(ua[t]);
-                if (li == 0 && ((mask >> t) & 1u)) {
-                    const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
-                    put_staged<FMT>(reinterpret_cast<_Float16*>(h + (size_t)row * Imax), Imax / 32, n,
-                                    silu_mul_scaled(gs_, us_, pow2f(-P.xexp[t])));
-                }
+                gsel = li == t ? gs_ : gsel;
+                usel = li == t ? us_ : usel;
+            }
+            if (li < T && ((mask >> li) & 1u)) {
+                const int t = li;
+                const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
+                put_staged<FMT>(reinterpret_cast<_Float16*>(h + (size_t)row * Imax), Imax / 32, n,
+                                silu_mul_scaled(gsel, usel, pow2f(-P.xexp[t])));
             }
         }
     } else {
@@ -668,18 +674,28 @@ __global__ __launch_bounds__(kWave * gateup_max_waves(T)) void k_dec_gateup(Laye
                 rowdot(wu[i], sub[i], u[i]);
             }
         }
+        // the R T sums of gate and up moved into lanes 0 .. R T - 1 (row i, token t at lane i T + t),
+        // so that one epilogue (SiLU, h in its staged layout) serves them all instead of R T
+        // epilogues of a single active lane
+        static_assert(R * T <= kWave, "one lane per output");
+        float gl = 0.f, ul = 0.f;
 #pragma unroll
         for (int i = 0; i < R; ++i)
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const float gs_ = wave_sum(g[i][t]);
-                const float us_ = wave_sum(u[i][t]);
-                if (lane == 0 && i < nv && ((mask >> t) & 1u)) {
-                    const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
-                    put_staged<FMT>(reinterpret_cast<_Float16*>(h + (size_t)row * Imax), Imax / 32, n0 + i,
-                                    silu_mul_scaled(gs_, us_, pow2f(-P.xexp[t])));
-                }
+                const float gs_ = wave_sum(g[i][t]), us_ = wave_sum(u[i][t]);
+                const bool mine = lane == i * T + t;
+                gl = mine ? gs_ : gl;
+                ul = mine ? us_ : ul;
             }
+        {
+            const int i = lane / T, t = lane - i * T;
+            if (lane < R * T && i < nv && ((mask >> t) & 1u)) {
+                const int row = slot < 64 ? P.pair_of[slot][t] : npairs + t;
+                put_staged<FMT>(reinterpret_cast<_Float16*>(h + (size_t)row * Imax), Imax / 32, n0 + i,
+                                silu_mul_scaled(gl, ul, pow2f(-P.xexp[t])));
+            }
+        }
     }
     }
 }
