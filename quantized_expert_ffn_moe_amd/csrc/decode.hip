@@ -740,7 +740,23 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
     constexpr int kPlanWords = (int)(sizeof(DecodePlan) / 4);
     constexpr int kHBatch = 3;   // uint4 of h per thread held in registers across the weight loads
     const uint4* hs = reinterpret_cast<const uint4*>(h);
-    const int n4 = nrows_h * 8 * nbm;
+    // From three tokens on only the fp16 high halves of h are copied and multiplied (h at fp16, as
+    // on the grouped-GEMM path): the staged activations are read from LDS once per output row, and
+    // at four tokens those reads, not the weights, bound the kernel. One and two tokens keep hi +
+    // lo (about 22 bits).
+    constexpr bool kHiOnly = T >= 3;
+    constexpr int NC = kHiOnly ? 4 : 8;          // uint4 per 32-block of an h row that are used
+    const int hstride = NC * nbm;                // uint4 copied per h row
+    const int n4 = nrows_h * hstride;            // uint4 copied
+    // copied element i -> its uint4 in the staged rows (the same index in global memory and LDS)
+    auto hidx = [&](int i) __attribute__((always_inline)) {
+        if constexpr (kHiOnly) {
+            const int row = i / hstride;
+            return row * 8 * nbm + (i - row * hstride);
+        } else {
+            return i;
+        }
+    };
     const int hrot = (int)((blockIdx.x / 8) * 320u % (unsigned)n4);
     const uint32_t* ps = reinterpret_cast<const uint32_t*>(plan_g);
     uint32_t pw[(kPlanWords + kDownThreads - 1) / kDownThreads];
@@ -757,7 +773,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
         // every block reads all of h; each starts at its own offset, so that the blocks of an XCD do
         // not all ask for the same lines at once
         const int i = min((int)threadIdx.x + kDownThreads * b, n4 - 1) + hrot;
-        hv0[b] = hs4[i < n4 ? i : i - n4];
+        hv0[b] = hs4[hidx(i < n4 ? i : i - n4)];
     }
     __builtin_amdgcn_sched_barrier(0);   // h loads are issued before the wait on the plan words
     {
@@ -874,12 +890,12 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
 #pragma unroll
             for (int b = 0; b < kHBatch; ++b) {
                 const int i = (int)threadIdx.x + kDownThreads * b;
-                if (i < n4) hq4[i + hrot < n4 ? i + hrot : i + hrot - n4] = hv0[b];
+                if (i < n4) hq4[hidx(i + hrot < n4 ? i + hrot : i + hrot - n4)] = hv0[b];
             }
             // the rest (unrolled: each group of loads in flight together, not one round trip each)
 #pragma unroll 8
             for (int i = (int)threadIdx.x + kDownThreads * kHBatch; i < n4; i += kDownThreads) {
-                const int ir = i + hrot < n4 ? i + hrot : i + hrot - n4;   // the same rotation
+                const int ir = hidx(i + hrot < n4 ? i + hrot : i + hrot - n4);   // the same rotation
                 hq[ir] = hs[ir];
             }
             __syncthreads();
@@ -898,14 +914,14 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
                     // h (hi and lo) read from LDS TB tokens at a time, the first group before the
                     // codes are needed: the reads of a group are in flight together
                     constexpr int TB = T < 2 ? T : 2;
-                    uint4 hv[TB][8];
+                    uint4 hv[TB][NC];
                     auto read_h = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
                         for (int tb = 0; tb < TB; ++tb) {
                             const int t = min(t0 + tb, T - 1);
                             const uint4* hp = hq + (size_t)max(hrow[jj][t], 0) * 8 * nbm + b;
 #pragma unroll
-                            for (int c = 0; c < 8; ++c) hv[tb][c] = hp[(size_t)c * nbm];
+                            for (int c = 0; c < NC; ++c) hv[tb][c] = hp[(size_t)c * nbm];
                         }
                         __builtin_amdgcn_sched_barrier(0);   // (the scheduler would pair them with the dot products)
                     };
@@ -916,7 +932,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
                         if (t > 0 && t % TB == 0) read_h(t);
                         float d = 0.f;
 #pragma unroll
-                        for (int c = 0; c < 8; ++c) {
+                        for (int c = 0; c < NC; ++c) {
                             const int j = 4 * (c & 3);
                             d = dot2(pd[j], hv[t % TB][c].x, d);
                             d = dot2(pd[j + 1], hv[t % TB][c].y, d);
@@ -934,7 +950,7 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
                         if (row >= 0) {
                             const uint4* hp = hq + (size_t)row * 8 * nbm + b;
 #pragma unroll
-                            for (int c = 0; c < 8; ++c) {
+                            for (int c = 0; c < NC; ++c) {
                                 const uint4 hv = hp[(size_t)c * nbm];
                                 const int j = 4 * (c & 3);
                                 d = dot2(pd[j], hv.x, d);
