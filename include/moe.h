@@ -178,7 +178,8 @@ moe_status moe_permute(const moe_layer_desc* desc, const int32_t* ids, int32_t T
  *   y_shared[t] = the shared expert on x_t (required iff Is > 0, else ignored)
  * Dequantised weights are exact fp16 values; the dot products accumulate in fp32 over fp16
  * operands: x rounded once to fp16 (at its token scale, see "Activation range"), h as an fp16
- * hi + lo pair (about 22 bits). Workspace: MOE_CALL_EXPERTS_DECODE.
+ * hi + lo pair (about 22 bits) for one or two tokens and as one fp16 value from three tokens on.
+ * Workspace: MOE_CALL_EXPERTS_DECODE.
  * The kernels keep every chosen pair's SwiGLU activations in LDS (160 KB per workgroup):
  * 4 (T k + T) max(I, Is) bytes plus the routing plan and about 4 E bytes must fit; a shape beyond
  * that (or T > 8, or T k > 64) returns MOE_ERR_UNSUPPORTED before anything is enqueued, and so does
