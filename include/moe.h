@@ -122,7 +122,7 @@ typedef struct {
     int32_t shared_inter;  /* Is, 0 = no shared expert */
     moe_qformat fmt;       /* code format of every expert matrix */
     int32_t decode_max_tokens;  /* moe_layer's regime switch: the decode kernels for T <= this (when
-                                   they fit), the grouped GEMMs above; 0 = the default, 5 (measured
+                                   they fit), the grouped GEMMs above; 0 = the default, 6 (measured
                                    crossover at H 2048, 256 experts top-8, 4-bit); at most 8 */
 } moe_layer_desc;
 
@@ -231,7 +231,7 @@ moe_status moe_combine(const moe_layer_desc* desc, int32_t T, const float* p, co
 
 /*
  * The whole layer: route, permute, experts, combine (the five steps above in one call).
- * T <= decode_max_tokens (default 5; T k <= 64) takes the decode path (three launches: router
+ * T <= decode_max_tokens (default 6; T k <= 64) takes the decode path (three launches: router
  * GEMV; top-k + gate/up; down with the combine fused) when its LDS fits the shape (see
  * moe_experts_decode), else, like larger T, the prefill path (router GEMV up to 16 tokens, GEMM
  * above; top-k, permutation, grouped GEMMs, combine; from 2 to 16 tokens the top-k, the

@@ -15,9 +15,9 @@ constexpr int kMaxE = 1024, kMaxK = kMaxTopK, kMaxH = 16384, kMaxI = 4096, kMaxT
 
 // moe_layer takes the decode kernels up to this many tokens by default (when they fit the shape):
 // the crossover measured on the 8K-prefill layer shape (H 2048, 256 experts top-8 + shared, 4-bit):
-// the decode kernels win at 5 tokens, the grouped GEMMs (on packed codes) from 6;
+// the decode kernels win up to 6 tokens, the grouped GEMMs (on packed codes) from 7;
 // moe_layer_desc.decode_max_tokens overrides it (up to 8).
-constexpr int kLayerDecodeMaxT = 5;
+constexpr int kLayerDecodeMaxT = 6;
 constexpr int kDecodeMaxT = 8;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }

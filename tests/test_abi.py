@@ -72,9 +72,9 @@ def test_layer_regime_switch_sizes_the_workspace():
     dec, gemm = D(dmt=8), D(dmt=1)
     assert moe.moe_workspace_size(dec, 8, moe.MOE_CALL_LAYER) < 8 * 8 * 2048 * 2
     assert moe.moe_workspace_size(gemm, 8, moe.MOE_CALL_LAYER) > 8 * 8 * 2048 * 2
-    # the default switch on this shape: decode kernels up to 5 tokens, grouped GEMMs from 6
-    assert moe.moe_workspace_size(D(), 5, moe.MOE_CALL_LAYER) < 5 * 8 * 2048 * 2
-    assert moe.moe_workspace_size(D(), 6, moe.MOE_CALL_LAYER) > 6 * 8 * 2048 * 2
+    # the default switch on this shape: decode kernels up to 6 tokens, grouped GEMMs from 7
+    assert moe.moe_workspace_size(D(), 6, moe.MOE_CALL_LAYER) < 6 * 8 * 2048 * 2
+    assert moe.moe_workspace_size(D(), 7, moe.MOE_CALL_LAYER) > 7 * 8 * 2048 * 2
 
 
 def _raw(fn, *args):
