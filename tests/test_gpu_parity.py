@@ -148,6 +148,21 @@ def test_decode_ragged_row_groups(fmt, T):
     assert_float_match(y_shared.cpu().numpy(), ref["y_shared"], "y_shared")
 
 
+@pytest.mark.parametrize("T", [5, 6, 7])
+def test_layer_default_switch(T):
+    """moe_layer with the library's default regime switch on both sides of it (decode kernels up to
+    6 tokens, grouped GEMMs from 7): the same oracle rule either way."""
+    _need_gpu()
+    spec = synth.LayerSpec("sw", T=T, H=512, E=64, k=8, I=128, Is=64, fmt=synth.Q4, zipf=True, cfg_id=260 + T)
+    d = synth.make_layer(spec)
+    say("default switch T=%d" % T)
+    O = orc_layer(spec, d)
+    g_logits, g_ids, g_p, Y = run_layer(spec, d)
+    check_routing(O, d["x"], g_logits, g_ids, g_p)
+    ref = oracle_tokens(O, d["x"], g_logits, range(T))
+    assert_float_match(Y, ref["Y"], "Y")
+
+
 @pytest.mark.parametrize("layer", [0, 47])
 def test_stack48_layer(layer):
     """One layer of the 48-layer, 512-expert, top-10, 2-bit stack at full size."""
