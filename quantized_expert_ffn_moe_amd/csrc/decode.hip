@@ -15,15 +15,18 @@
 //   k_dec_gateup     per block: top-k of every token from the logits (one wave per token, in
 //                    registers), the union of the chosen experts in LDS, x staged as fp16 pairs
 //                    laid out to match the packed codes; then gate/up rows streamed with every
-//                    load of a wave issued up front: codes become fp16 by OR-ing them into the
-//                    mantissa of 1024.0 and multiply into x with v_dot2_f32_f16 (fp32
-//                    accumulation); for one or two tokens the constant 1024 (and the code
-//                    offset) is removed once per block with a sum over the staged x, for three or
-//                    four by a packed subtract per code pair. Block 0 publishes ids and p.
+//                    load of a wave issued up front (one or two tokens: a row per 16 lanes, four
+//                    rows per wave; more: three or two rows over all 64 lanes): codes become fp16
+//                    by OR-ing them into the mantissa of 1024.0 and multiply into x with
+//                    v_dot2_f32_f16 (fp32 accumulation); for one or two tokens the constant 1024
+//                    (and the code offset) is removed once per block with a sum over the staged x,
+//                    from three tokens on by a packed subtract per code pair. Block 0 publishes
+//                    ids and p.
 //   k_dec_down       output rows m: every chosen expert's down row m times its h (LDS as fp16
-//                    hi/lo pairs, laid out so that lanes reading consecutive 32-blocks hit
-//                    consecutive banks), weighted by the routing probability and summed with the
-//                    shared expert (combine fused), or written per pair for moe_experts_decode.
+//                    hi/lo pairs for one or two tokens, the fp16 high halves alone from three on,
+//                    laid out so that lanes reading consecutive 32-blocks hit consecutive banks),
+//                    weighted by the routing probability and summed with the shared expert
+//                    (combine fused), or written per pair for moe_experts_decode.
 #include <algorithm>
 
 #include <atomic>
