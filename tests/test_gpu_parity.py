@@ -236,6 +236,29 @@ def test_experts_decode_stack48_four_tokens():
     assert_float_match(Y.cpu().numpy(), ref["Y"], "Y")
 
 
+def test_experts_decode_chunked_odd_blocks():
+    """moe_experts_decode where the per-pair partial sums do not fit the LDS at once and the block
+    counts are odd (I = 352: 11 blocks per slot, Is = 96: 3 blocks): 64 pairs of 4 tokens reduced
+    in chunks of slots, the partials read one at a time."""
+    _need_gpu()
+    T = 4
+    spec = synth.LayerSpec("chunk", T=T, H=256, E=64, k=16, I=352, Is=96, fmt=synth.Q8, zipf=True, cfg_id=270)
+    d = synth.make_layer(spec)
+    say("chunked odd blocks T=4 k=16 I=352 Is=96")
+    O = orc_layer(spec, d)
+    L = dev_layer(spec, d)
+    xd = dev_x(d["x"])
+    logits = torch.empty((T, spec.E), dtype=torch.float32, device="cuda")
+    _, ids, p = moe.moe_route(L, xd, logits=logits)
+    y_pairs, y_shared = moe.moe_experts_decode(L, xd, ids)
+    torch.cuda.synchronize()
+    g_logits = logits.cpu().numpy()
+    check_routing(O, d["x"], g_logits, ids.cpu().numpy(), p.cpu().numpy())
+    ref = oracle_tokens(O, d["x"], g_logits, range(T))
+    assert_float_match(y_pairs.cpu().numpy().reshape(T, spec.k, spec.H), ref["y_pairs"], "y_pairs")
+    assert_float_match(y_shared.cpu().numpy(), ref["y_shared"], "y_shared")
+
+
 def test_golden_examples_on_gpu():
     """The hand-computed worked examples through moe_layer (T = 1, decode path)."""
     _need_gpu()
