@@ -7,8 +7,10 @@
 // 10-cyber-on-strata-moe-local-inference, section on bitwise validation and the speed bottleneck);
 // this is the ceiling such a stage meets on this GPU at this size, with and without a kernel boundary
 // in the middle. Printed, one JSON object per line:
-//   one_kernel: one read kernel per buffer of B bytes (B = 15,925,248, the one-token expert stage of
-//       the 256-expert top-8 layer with a shared expert, 4-bit codes);
+//   one_kernel: one read kernel per buffer of B bytes, for the expert stages of the decode shapes:
+//       15,925,248 (one token, 256 experts top-8 + a shared expert, 4-bit codes), 56,819,712 (four
+//       tokens of the same layer with 8-bit codes: 16 distinct experts + the shared one) and
+//       14,745,600 (one token, 512 experts top-10, 2-bit codes);
 //   two_kernels: the same bytes as two dependent kernels per buffer (2/3 then 1/3, the split of the
 //       gate/up and down weights);
 //   for grids of 256, 512 and 1024 blocks of 256 threads (every thread keeps 8 16-byte loads in
@@ -34,7 +36,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kInFlight = 8;       // 16-byte loads per thread and step
 constexpr int kBuffers = 48;
-constexpr size_t kBytes = 15925248;
+constexpr size_t kSizes[] = {15925248, 56819712, 14745600};
 constexpr int kReps = 20;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -64,8 +66,9 @@ __global__ __launch_bounds__(kThreads) void k_read(const u32x4* __restrict__ src
     }
 }
 
-float time_graph(hipStream_t s, const std::vector<u32x4*>& bufs, unsigned* out, int blocks, bool split) {
-    const size_t n = kBytes / 16;
+float time_graph(hipStream_t s, const std::vector<u32x4*>& bufs, size_t bytes, unsigned* out, int blocks,
+                 bool split) {
+    const size_t n = bytes / 16;
     const size_t n1 = split ? (n * 2) / 3 : n;
     hipGraph_t g;
     hipGraphExec_t ge;
@@ -99,24 +102,26 @@ float time_graph(hipStream_t s, const std::vector<u32x4*>& bufs, unsigned* out, 
 int main() {
     hipStream_t s;
     CHECK(hipStreamCreate(&s));
-    std::vector<u32x4*> bufs(kBuffers);
-    for (auto& b : bufs) {
-        CHECK(hipMalloc(&b, kBytes));
-        CHECK(hipMemset(b, 0x5a, kBytes));
-    }
     unsigned* out = nullptr;
     CHECK(hipMalloc(&out, 4096 * sizeof(unsigned)));
-    CHECK(hipDeviceSynchronize());
-    for (int blocks : {256, 512, 1024}) {
-        for (bool split : {false, true}) {
-            const float us = time_graph(s, bufs, out, blocks, split);
-            std::printf("{\"probe\": \"%s\", \"blocks\": %d, \"bytes\": %zu, \"us_per_buffer\": %.2f, "
-                        "\"GB_per_s\": %.1f}\n",
-                        split ? "two_kernels" : "one_kernel", blocks, kBytes, us, kBytes / (us * 1e3));
-            std::fflush(stdout);
+    for (size_t bytes : kSizes) {
+        std::vector<u32x4*> bufs(kBuffers);
+        for (auto& b : bufs) {
+            CHECK(hipMalloc(&b, bytes));
+            CHECK(hipMemset(b, 0x5a, bytes));
         }
+        CHECK(hipDeviceSynchronize());
+        for (int blocks : {256, 512, 1024}) {
+            for (bool split : {false, true}) {
+                const float us = time_graph(s, bufs, bytes, out, blocks, split);
+                std::printf("{\"probe\": \"%s\", \"blocks\": %d, \"bytes\": %zu, \"us_per_buffer\": %.2f, "
+                            "\"GB_per_s\": %.1f}\n",
+                            split ? "two_kernels" : "one_kernel", blocks, bytes, us, bytes / (us * 1e3));
+                std::fflush(stdout);
+            }
+        }
+        for (auto& b : bufs) CHECK(hipFree(b));
     }
-    for (auto& b : bufs) CHECK(hipFree(b));
     CHECK(hipFree(out));
     CHECK(hipStreamDestroy(s));
     return 0;
