@@ -741,9 +741,10 @@ __global__ __launch_bounds__(kDownThreads) void k_dec_down(LayerView L, const De
     float* part = reinterpret_cast<float*>(hq + (size_t)(npairs + T) * 8 * nbm);
     // the plan first (the weight addresses depend on it), h (already staged) in flight behind it
     constexpr int kPlanWords = (int)(sizeof(DecodePlan) / 4);
-    // uint4 of h per thread held in registers across the weight loads (1536, or 2560 from three
-    // tokens on: the h loads past the batch go out behind the weights and wait for them)
-    constexpr int kHBatch = T >= 3 ? 5 : 3;
+    // uint4 of h per thread held in registers across the weight loads (2048, or 2560 from three
+    // tokens on: the h loads past the batch go out behind the weights and wait for them; threads
+    // past the end load the last piece again)
+    constexpr int kHBatch = T >= 3 ? 5 : 4;
     const uint4* hs = reinterpret_cast<const uint4*>(h);
     // From three tokens on only the fp16 high halves of h are copied and multiplied (h at fp16, as
     // on the grouped-GEMM path): the staged activations are read from LDS once per output row, and
